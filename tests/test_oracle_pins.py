@@ -1,0 +1,308 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself:
+library conversions (numpy float16, torch bfloat16), exact integer arithmetic in
+float64, closed forms, hand-worked fixtures under tests/golden/, and properties of
+the GELU tanh approximation against the exact erf form."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gemm_epilogues_epilog_amd import inputs
+from tests.helpers import unpack_mask
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def np_of(t: torch.Tensor, dt: str) -> np.ndarray:
+    if dt == "bf16":
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def pack_mask_np(pos: np.ndarray) -> np.ndarray:
+    """Independent numpy packing of a (m, n) bool matrix into (ceil(m/32), n) words."""
+    m, n = pos.shape
+    g = (m + 31) // 32
+    padded = np.zeros((g * 32, n), dtype=np.uint64)
+    padded[:m] = pos
+    weights = (np.uint64(1) << np.arange(32, dtype=np.uint64))[None, :, None]
+    return (padded.reshape(g, 32, n) * weights).sum(axis=1).astype(np.uint32)
+
+
+# ---- conversions ----------------------------------------------------------------
+
+def test_f16_widen_exhaustive():
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ours = oracle.f16_to_f32(h)
+    ref = h.view(np.float16).astype(np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+def test_f16_round_matches_numpy():
+    rng = np.random.default_rng(1)
+    # random values over the whole half range, subnormals, overflow boundary
+    x = np.concatenate([
+        rng.standard_normal(200000).astype(np.float32) * np.float32(2.0) ** rng.integers(-30, 17, 200000).astype(np.float32),
+        np.array([65504, 65519.996, 65520, 65536, 1e9, -65520, 2.0 ** -24, 2.0 ** -25, 3 * 2.0 ** -26,
+                  2.0 ** -26, 6.1e-5, 0.0, -0.0, np.inf, -np.inf], dtype=np.float32),
+    ])
+    ours = oracle.f32_to_f16(x)
+    ref = x.astype(np.float16).view(np.uint16)
+    assert np.array_equal(ours, ref)
+
+
+def test_f16_round_ties_to_even():
+    # exact midpoints between consecutive finite halves round to the even pattern
+    h = np.arange(0, 0x7bff, dtype=np.uint16)
+    lo = h.view(np.float16).astype(np.float64)
+    hi = (h + 1).view(np.float16).astype(np.float64)
+    mid = ((lo + hi) / 2).astype(np.float32)            # exact in fp32
+    ours = oracle.f32_to_f16(mid)
+    expect = np.where(h % 2 == 0, h, h + 1).astype(np.uint16)
+    assert np.array_equal(ours, expect)
+    assert np.array_equal(ours, mid.astype(np.float16).view(np.uint16))
+
+
+def test_bf16_widen_exhaustive():
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ours = oracle.bf16_to_f32(h)
+    ref = torch.from_numpy(h.view(np.int16).copy()).view(torch.bfloat16).float().numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+def test_bf16_round_matches_torch():
+    rng = np.random.default_rng(2)
+    x = (rng.standard_normal(200000).astype(np.float32)
+         * np.float32(2.0) ** rng.integers(-130, 120, 200000).astype(np.float32))
+    # ties: a bf16 value plus half of its ulp
+    base = rng.integers(0, 0x7f00, 5000).astype(np.uint32) << 16
+    ties = (base | 0x8000).view(np.float32)
+    x = np.concatenate([x, ties, np.array([0.0, -0.0, 3.4e38, -3.4e38], np.float32)])
+    ours = oracle.f32_to_bf16(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+
+
+# ---- GELU (tanh form) -----------------------------------------------------------
+
+def test_gelu_identities_and_erf_distance():
+    assert oracle.gelu_tanh(0.0) == 0.0
+    xs = np.linspace(-8, 8, 16001)
+    g = np.array([oracle.gelu_tanh(x) for x in xs])
+    gneg = np.array([oracle.gelu_tanh(-x) for x in xs])
+    # odd part identity of x * Phi-like gates: gelu(x) - gelu(-x) = x
+    assert np.allclose(g - gneg, xs, atol=1e-12, rtol=0)
+    # distance to the exact form x * Phi(x): the tanh approximation's largest error
+    # is 4.73e-4, near |x| = 2.70 (pins both constants of the approximation)
+    exact = np.array([0.5 * x * (1 + math.erf(x / math.sqrt(2))) for x in xs])
+    d = np.abs(g - exact)
+    assert 4.725e-4 < d.max() < 4.740e-4
+    assert 2.6 < abs(xs[d.argmax()]) < 2.8
+    # limits
+    assert abs(oracle.gelu_tanh(10.0) - 10.0) < 1e-12
+    assert abs(oracle.gelu_tanh(-10.0)) < 1e-12
+    # slope 1/2 at the origin
+    assert abs(oracle.gelu_tanh(1e-6) / 1e-6 - 0.5) < 1e-5
+
+
+def test_gelu_tanh_is_not_erf_form_fp32():
+    # fp32 GELU_BIAS at x = 2.7 must follow the tanh form: its gap to the erf form
+    # (4.7e-4) is larger than the fp32 tolerance 1e-4 * |y|.
+    A = np.zeros((1, 4), np.float32)
+    B = np.zeros((4, 4), np.float32)
+    bias = np.array([2.7], np.float32)
+    D = oracle.gemm_epilog(A, B, "GELU_BIAS", bias=bias, ab="f32")["D"]
+    x = float(np.float32(2.7))
+    exact = 0.5 * x * (1 + math.erf(x / math.sqrt(2)))
+    assert abs(D[0, 0] - exact) > 3e-4
+    assert abs(D[0, 0] - exact) < 5e-4
+
+
+# ---- hand-worked fixtures ---------------------------------------------------------
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+def test_worked_example(dt):
+    fx = json.load(open(os.path.join(GOLDEN, "worked_example_3x2x2.json")))
+    cast = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dt]
+    A = np_of(torch.tensor(fx["A"]).to(cast), dt)
+    B = np_of(torch.tensor(fx["B"]).to(cast), dt)
+    bias = np_of(torch.tensor(fx["bias"]).to(cast), dt)
+    w = lambda a: oracle.to_f32(a, dt)
+    o = oracle.gemm_epilog(A, B, "RELU_AUX_BIAS", bias=bias, ab=dt, want_pre=True)
+    assert np.array_equal(w(o["D"]), np.array(fx["relu"], np.float32))
+    assert not np.signbit(w(o["D"])).any()
+    assert np.array_equal(o["pre"], np.array(fx["pre"], np.float32))
+    assert np.array_equal(o["mask"], np.array(fx["mask_words"], np.uint32))
+    o2 = oracle.gemm_epilog(A, B, "BIAS", bias=bias, ab=dt)
+    assert np.array_equal(w(o2["D"]), np.array(fx["pre"], np.float32))
+    o3 = oracle.gemm_epilog(A, B, "NONE", ab=dt)
+    assert np.array_equal(w(o3["D"]), np.array(fx["AB"], np.float32))
+    o4 = oracle.gemm_epilog(A, B, "DRELU_BGRAD", mask=np.array(fx["mask_words"], np.uint32), ab=dt)
+    assert np.array_equal(w(o4["D"]), np.array(fx["dz"], np.float32))
+    assert np.array_equal(w(o4["bgrad"]), np.array(fx["bgrad"], np.float32))
+
+
+def test_mask_layout_fixture():
+    fx = json.load(open(os.path.join(GOLDEN, "mask_layout_40x3.json")))
+    m, n, k = fx["m"], fx["n"], fx["k"]
+    bias = -np.ones(m, np.float16)
+    bias[fx["positive_rows"]] = 1
+    A = np.zeros((m, k), np.float16)
+    B = np.random.default_rng(0).standard_normal((k, n)).astype(np.float16)
+    o = oracle.gemm_epilog(A, B, "RELU_AUX_BIAS", bias=bias)
+    assert np.array_equal(o["mask"], np.array(fx["words"], np.uint32))
+
+
+# ---- exact integer arithmetic vs numpy float64 --------------------------------------
+
+SHAPES = [(1, 8, 8), (40, 24, 16), (67, 16, 9), (96, 40, 3)]
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("shape", SHAPES)
+def test_integer_exact_forward(dt, shape):
+    m, n, k = shape
+    A, B, bias, _, _ = inputs.integer_case(m, n, k, dt)
+    An, Bn, bn = np_of(A, dt), np_of(B, dt), np_of(bias, dt)
+    ab = A.double().numpy() @ B.double().numpy()
+    pre = ab + bias.double().numpy()[:, None]
+    w = lambda a: oracle.to_f32(a, dt).astype(np.float64)
+    for ep, ref in (("NONE", ab), ("BIAS", pre), ("RELU_BIAS", np.maximum(pre, 0)),
+                    ("RELU_BIAS_UNFUSED", np.maximum(pre, 0))):
+        o = oracle.gemm_epilog(An, Bn, ep, bias=bn, ab=dt)
+        assert np.array_equal(w(o["D"]), ref), ep
+    o = oracle.gemm_epilog(An, Bn, "RELU_AUX_BIAS", bias=bn, ab=dt)
+    assert np.array_equal(w(o["D"]), np.maximum(pre, 0))
+    assert np.array_equal(o["mask"], pack_mask_np(pre > 0))
+    assert np.array_equal(unpack_mask(o["mask"], m), pre > 0)
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("shape", SHAPES)
+def test_integer_exact_backward(dt, shape):
+    m, n, k = shape
+    A, B, bias, A2, B2 = inputs.integer_case(m, n, k, dt)
+    pre = A.double().numpy() @ B.double().numpy() + bias.double().numpy()[:, None]
+    mask = pack_mask_np(pre > 0)
+    prod = A2.double().numpy() @ B2.double().numpy()
+    dz = np.where(pre > 0, prod, 0.0)
+    o = oracle.gemm_epilog(np_of(A2, dt), np_of(B2, dt), "DRELU_BGRAD", mask=mask, ab=dt)
+    w = lambda a: oracle.to_f32(a, dt).astype(np.float64)
+    assert np.array_equal(w(o["D"]), dz)
+    assert np.array_equal(w(o["bgrad"]), dz.sum(axis=1))      # sum over n: one value per row
+    assert np.array_equal(o["absum"], np.abs(dz).sum(axis=1))
+
+
+def test_integer_gelu_plumbing():
+    # bias indexing and output rounding of GELU_BIAS on exact pre-activations
+    m, n, k = 40, 24, 16
+    A, B, bias, _, _ = inputs.integer_case(m, n, k, "f32")
+    pre = A.double().numpy() @ B.double().numpy() + bias.double().numpy()[:, None]
+    o = oracle.gemm_epilog(A.numpy(), B.numpy(), "GELU_BIAS", bias=bias.numpy(), ab="f32")
+    ref = 0.5 * pre * (1 + np.vectorize(math.erf)(pre / math.sqrt(2)))
+    assert np.abs(o["D"] - ref).max() < 5e-4
+
+
+# ---- closed forms ----------------------------------------------------------------
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+def test_zero_A(dt):
+    m, n, k = 70, 16, 24
+    _, B, bias, _, _ = inputs.small_case(m, n, k, dt)
+    A = torch.zeros(m, k, dtype=B.dtype)
+    o = oracle.gemm_epilog(np_of(A, dt), np_of(B, dt), "RELU_AUX_BIAS", bias=np_of(bias, dt), ab=dt)
+    b = bias.double().numpy()
+    w = oracle.to_f32(o["D"], dt).astype(np.float64)
+    assert np.array_equal(w, np.repeat(np.maximum(b, 0)[:, None], n, axis=1))
+    assert np.array_equal(unpack_mask(o["mask"], m), np.repeat((b > 0)[:, None], n, axis=1))
+    o2 = oracle.gemm_epilog(np_of(A, dt), np_of(B, dt), "DRELU_BGRAD", mask=o["mask"], ab=dt)
+    assert not oracle.to_f32(o2["D"], dt).any() and not oracle.to_f32(o2["bgrad"], dt).any()
+
+
+def test_identity_operands_f32():
+    rng = np.random.default_rng(5)
+    m = k = 48
+    n = 20
+    B = rng.standard_normal((k, n)).astype(np.float32)
+    bias = rng.standard_normal(m).astype(np.float32)
+    I = np.eye(m, dtype=np.float32)
+    o = oracle.gemm_epilog(I, B, "RELU_BIAS", bias=bias, ab="f32")
+    assert np.array_equal(o["D"], np.maximum(B + bias[:, None], np.float32(0)))
+    A = rng.standard_normal((m, n)).astype(np.float32)
+    o = oracle.gemm_epilog(A, np.eye(n, dtype=np.float32), "BIAS", bias=bias, ab="f32")
+    assert np.array_equal(o["D"], A + bias[:, None])
+
+
+def test_full_mask_bgrad_is_matvec():
+    # all bits set: bgrad = A (B 1), two mat-vecs in float64
+    m, n, k = 96, 64, 128
+    A, B, _, _, _ = inputs.small_case(m, n, k, "f32")
+    mask = np.full(((m + 31) // 32, n), 0xFFFFFFFF, np.uint32)
+    o = oracle.gemm_epilog(A.numpy(), B.numpy(), "DRELU_BGRAD", mask=mask, ab="f32")
+    ref = A.double().numpy() @ (B.double().numpy() @ np.ones(n))
+    assert np.allclose(o["bgrad"], ref, rtol=0, atol=1e-4 * o["absum"].max())
+
+
+def test_ascending_k_order():
+    # fl32 sums in ascending k: (2^24 + 1) rounds back to 2^24, then - 2^24 = 0.
+    A = np.array([[2.0 ** 24, 1.0, -(2.0 ** 24), 0.0]], np.float32)
+    B = np.ones((4, 4), np.float32)
+    o = oracle.gemm_epilog(A, B, "NONE", ab="f32")
+    assert (o["D"] == 0).all()
+
+
+def test_tie_at_zero():
+    # pre exactly 0: ReLU gives +0 and the mask bit is 0
+    A = np.array([[1.0, 1.0]], np.float16)
+    B = np.ones((2, 8), np.float16)
+    bias = np.array([-2.0], np.float16)
+    o = oracle.gemm_epilog(A, B, "RELU_AUX_BIAS", bias=bias)
+    assert (o["D"].view(np.uint16) == 0).all()
+    assert (o["mask"] == 0).all()
+
+
+# ---- properties used by the sampled parity checks ----------------------------------
+
+def test_row_slab_equals_full():
+    m, n, k = 128, 40, 32
+    A, B, bias, A2, B2 = inputs.small_case(m, n, k, "f16")
+    full = oracle.gemm_epilog(A.numpy(), B.numpy(), "RELU_AUX_BIAS", bias=bias.numpy())
+    slab = oracle.gemm_epilog(A.numpy()[32:96], B.numpy(), "RELU_AUX_BIAS", bias=bias.numpy()[32:96])
+    assert np.array_equal(slab["D"].view(np.uint16), full["D"][32:96].view(np.uint16))
+    assert np.array_equal(slab["mask"], full["mask"][1:3])
+    bf = oracle.gemm_epilog(A2.numpy(), B2.numpy(), "DRELU_BGRAD", mask=full["mask"])
+    bs = oracle.gemm_epilog(A2.numpy()[32:96], B2.numpy(), "DRELU_BGRAD", mask=full["mask"][1:3])
+    assert np.array_equal(bs["bgrad"].view(np.uint16), bf["bgrad"][32:96].view(np.uint16))
+
+
+def test_threads_do_not_change_results():
+    m, n, k = 200, 64, 48
+    A, B, bias, _, _ = inputs.small_case(m, n, k, "bf16")
+    a, b, c = np_of(A, "bf16"), np_of(B, "bf16"), np_of(bias, "bf16")
+    o1 = oracle.gemm_epilog(a, b, "RELU_AUX_BIAS", bias=c, ab="bf16", nthreads=1)
+    o7 = oracle.gemm_epilog(a, b, "RELU_AUX_BIAS", bias=c, ab="bf16", nthreads=7)
+    assert np.array_equal(o1["D"], o7["D"]) and np.array_equal(o1["mask"], o7["mask"])
+
+
+def test_unfused_within_one_extra_rounding():
+    m, n, k = 64, 64, 256
+    A, B, bias, _, _ = inputs.small_case(m, n, k, "f16", std=0.1, std_bias=0.5)
+    f = oracle.gemm_epilog(A.numpy(), B.numpy(), "RELU_BIAS", bias=bias.numpy(), want_pre=True)
+    u = oracle.gemm_epilog(A.numpy(), B.numpy(), "RELU_BIAS_UNFUSED", bias=bias.numpy())
+    fd, ud = f["D"].astype(np.float64), u["D"].astype(np.float64)
+    # T1 rounding adds at most half an ulp of |acc| before the bias
+    acc = np.abs(f["pre"].astype(np.float64) - bias.numpy().astype(np.float64)[:, None])
+    assert (np.abs(fd - ud) <= 2.0 ** -11 * (acc + np.abs(fd)) * 2 + 2.0 ** -24).all()
+
+
+def test_oracle_rejects_bad_arguments():
+    with pytest.raises(ValueError):
+        oracle.gemm_epilog(np.zeros((2, 2), np.float16), np.zeros((2, 2), np.float16), "RELU_BIAS", bias=None)
