@@ -1,0 +1,229 @@
+"""Benchmark of the fused GEMM + epilogue path on one MI355X.
+
+A step is one execute of the fused RELU_BIAS kernel on the 7B-FFN workload
+(fp16, m=4096, n=11008, k=4096, fp32 accumulation), inputs resident in HBM. The
+metric is 2mnk / time in TFLOP/s and its fraction of the dense fp16 MFMA peak.
+
+Also measured (reported under "variants", not in "value"): the unfused three-kernel
+chain on the same inputs, bf16 GELU_BIAS, RELU_AUX_BIAS, the bf16 8192^3
+RELU_AUX_BIAS + DRELU_BGRAD pair and the large (65536,16384)x(16384,8192) fp16 shape
+with and without the mask. The CPU oracle is timed on a bounded sample of rows of
+the headline workload on the host cores.
+
+Prints one JSON line (the last line of stdout).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_F16_TFLOPS = 2516.6        # 256 CU x 2.4 GHz x 4096 FLOP/clk/CU, dense fp16/bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def device_inputs(W, device_rng: bool):
+    """Inputs of workload W on the GPU. The headline workload uses the seeded CPU
+    generator shared with the tests; the large variants draw on the device (seeded)."""
+    import torch
+    from gemm_epilogues_epilog_amd import inputs
+    if not device_rng:
+        return W.a().cuda(), W.b().cuda(), W.bias().cuda()
+    g = torch.Generator(device="cuda").manual_seed(W.seed)
+    dt = inputs.TORCH_DT[W.dtype]
+    A = (torch.randn(W.m, W.k, device="cuda", generator=g) * W.std_a).to(dt)
+    B = (torch.randn(W.k, W.n, device="cuda", generator=g) * W.std_b).to(dt)
+    bias = (torch.randn(W.m, device="cuda", generator=g) * W.std_bias).to(inputs.TORCH_DT[W.vec_dtype])
+    return A, B, bias
+
+
+def time_execute(ge, handle, args, steps, warmup):
+    """Warm up, then time `steps` executes: host wall clock bracketed by
+    synchronisations, and one HIP event pair per execute on the launch stream."""
+    import torch
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+    for _ in range(warmup):
+        ge.gemm_epilog_execute(handle, *args, stream=sptr)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in ev:
+        e0.record(stream)
+        ge.gemm_epilog_execute(handle, *args, stream=sptr)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = sorted(e0.elapsed_time(e1) for e0, e1 in ev)   # ms
+    return {"wall_ms_per_step": wall * 1e3 / steps, "event_ms_mean": sum(per) / len(per),
+            "event_ms_median": per[len(per) // 2], "event_ms_p10": per[len(per) // 10],
+            "event_ms_p90": per[min(len(per) - 1, (len(per) * 9) // 10)]}
+
+
+def run_variant(ge, W, epilog, dtype, steps, warmup, device_rng, backward=False):
+    import torch
+    A, B, bias = device_inputs(W, device_rng)
+    m, n, k = W.m, W.n, W.k
+    t0 = time.perf_counter()
+    h = ge.gemm_epilog_plan(m, n, k, (dtype, dtype, dtype), epilog)
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    D = torch.empty(m, n, dtype=A.dtype, device="cuda")
+    aux = bg = None
+    if epilog in ("RELU_AUX_BIAS", "DRELU_BGRAD"):
+        aux = torch.zeros((m + 31) // 32, n, dtype=torch.int32, device="cuda")
+    if epilog == "DRELU_BGRAD":
+        bg = torch.empty(m, dtype=A.dtype, device="cuda")
+        # a realistic mask: the forward pass of the same inputs
+        hf = ge.gemm_epilog_plan(m, n, k, (dtype, dtype, dtype), "RELU_AUX_BIAS")
+        ge.gemm_epilog_execute(hf, A, B, bias, D, aux, None)
+        torch.cuda.synchronize()
+        ge.gemm_epilog_free(hf)
+        bias = None
+    r = time_execute(ge, h, (A, B, bias, D, aux, bg), steps, warmup)
+    desc = ge.gemm_epilog_describe(h)
+    ge.gemm_epilog_free(h)
+    t = r["event_ms_median"] * 1e-3
+    out = {"epilog": epilog, "dtype": dtype, "m": m, "n": n, "k": k, "plan_ms": round(plan_ms, 3),
+           "kernel": desc, "median_ms": round(r["event_ms_median"], 4), "p10_ms": round(r["event_ms_p10"], 4),
+           "p90_ms": round(r["event_ms_p90"], 4), "tflops": round(2 * m * n * k / t / 1e12, 1)}
+    del A, B, D, aux, bg
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(W, budget_s: float):
+    """The CPU oracle on whole 256-row slabs of W until ~budget_s seconds of work."""
+    import numpy as np
+    import torch
+    import oracle
+
+    def to_np(t):
+        return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+
+    B = to_np(W.b())
+    bias = to_np(W.bias())
+    threads = oracle.default_threads()
+    rows = 0
+    flops = 0
+    t0 = time.perf_counter()
+    while rows < W.m and time.perf_counter() - t0 < budget_s:
+        r1 = min(W.m, rows + 256)
+        a = to_np(W.a(rows, r1))
+        oracle.gemm_epilog(a, B, W.epilog, bias=bias[rows:r1], ab=W.dtype)
+        flops += 2 * (r1 - rows) * W.n * W.k
+        rows = r1
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"rows 0..{rows} of {W.m} ({rows * W.n * W.k * 2 / 1e9:.1f} GFLOP of {W.name} "
+                      f"{W.epilog}), {dt:.1f} s, input slabs regenerated per 256 rows inside the timing"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-variants", action="store_true", help="time only the headline kernel")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--traffic", default=None, help="JSON file with measured HBM bytes per launch")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the fused epilogue shards by output tiles; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gemm_epilogues_epilog_amd as ge
+    from gemm_epilogues_epilog_amd import inputs
+
+    ge.load()
+    torch.cuda.set_device(0)
+    prop = torch.cuda.get_device_properties(0)
+    W = inputs.WORKLOADS[inputs.HEADLINE]
+    log(f"[bench] device {prop.name} {getattr(prop, 'gcnArchName', '')} CUs {prop.multi_processor_count}")
+    log(f"[bench] headline {W.name}: generating inputs")
+    A, B, bias = device_inputs(W, device_rng=False)
+    D = torch.empty(W.m, W.n, dtype=A.dtype, device="cuda")
+    t0 = time.perf_counter()
+    h = ge.gemm_epilog_plan(W.m, W.n, W.k, (W.dtype, W.dtype, W.dtype), W.epilog)
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    log(f"[bench] plan {plan_ms:.3f} ms: {ge.gemm_epilog_describe(h)}")
+    r = time_execute(ge, h, (A, B, bias, D, None, None), args.steps, args.warmup)
+    kernel_desc = ge.gemm_epilog_describe(h)
+    ge.gemm_epilog_free(h)
+    flops = W.flops()
+    value = flops / (r["wall_ms_per_step"] * 1e-3) / 1e12
+    achieved = flops / (r["event_ms_mean"] * 1e-3) / 1e12
+    log(f"[bench] headline: {r}")
+
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        tr = json.load(open(args.traffic))
+        if tr.get("kernel") == kernel_desc:
+            traffic = tr.get("bytes_per_launch")
+
+    variants = {}
+    if not args.no_variants:
+        vsteps, vwarm = max(5, args.steps // 2), max(2, args.warmup // 2)
+        plan = [
+            ("ffn_unfused_f16", inputs.HEADLINE, "RELU_BIAS_UNFUSED", "f16", False),
+            ("ffn_aux_f16", inputs.HEADLINE, "RELU_AUX_BIAS", "f16", False),
+            ("ffn_gelu_bf16", "ffn_gelu_bf16_4096x11008x4096", "GELU_BIAS", "bf16", False),
+            ("mlp8192_fwd_aux_bf16", "mlp_bf16_8192", "RELU_AUX_BIAS", "bf16", True),
+            ("mlp8192_bwd_drelu_bgrad_bf16", "mlp_bf16_8192", "DRELU_BGRAD", "bf16", True),
+            ("large_relu_bias_f16", "large_f16_65536x8192x16384", "RELU_BIAS", "f16", True),
+            ("large_aux_f16", "large_f16_65536x8192x16384", "RELU_AUX_BIAS", "f16", True),
+        ]
+        for name, wname, ep, dt, dev_rng in plan:
+            Wv = inputs.WORKLOADS[wname]
+            steps = vsteps if Wv.flops() < 5e12 else max(3, vsteps // 5)
+            log(f"[bench] variant {name}")
+            variants[name] = run_variant(ge, Wv, ep, dt, steps, vwarm, dev_rng)
+            log(f"[bench]   {variants[name]}")
+        fused_ms = r["event_ms_median"]
+        unf = variants["ffn_unfused_f16"]["median_ms"]
+        variants["ffn_fusion_saving"] = {"fused_ms": round(fused_ms, 4), "unfused_ms": unf,
+                                         "saving_frac": round(1 - fused_ms / unf, 4)}
+
+    del A, B, D
+    torch.cuda.empty_cache()
+    log("[bench] cpu baseline (oracle)")
+    cpu = cpu_baseline(W, args.cpu_budget)
+    log(f"[bench] cpu: {cpu}")
+
+    out = {
+        "metric": "fused GEMM+bias+ReLU TFLOP/s & % fp16 MFMA peak (4096x11008x4096)",
+        "value": round(value, 1),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["wall_ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": W.name, "m": W.m, "n": W.n, "k": W.k, "epilog": W.epilog,
+                   "accumulate": "f32", "kernel": kernel_desc, "plan_ms": round(plan_ms, 3),
+                   "cus": prop.multi_processor_count, "frac_of_peak": round(value / PEAK_F16_TFLOPS, 4)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_F16_TFLOPS, 4), "traffic": traffic,
+                     "kernel_ms_mean": round(r["event_ms_mean"], 4), "kernel_ms_median": round(r["event_ms_median"], 4),
+                     "kernel_ms_p10": round(r["event_ms_p10"], 4), "kernel_ms_p90": round(r["event_ms_p90"], 4)},
+        "cpu_baseline": cpu,
+        "variants": variants,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,210 @@
+"""Python binding of the fused GEMM + epilogue library for MI355X (gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP kernels of
+libgemm_epilog.so (built by gemm_epilogues_epilog_amd/build.py). There is no CPU
+fallback; if the library is missing every call raises.
+
+Low-level functions carry the names of the C ABI in include/gemm_epilog.h:
+gemm_epilog_plan, gemm_epilog_execute, gemm_epilog_free, gemm_epilog_aux_bytes,
+gemm_epilog_workspace_bytes, gemm_epilog_describe, gemm_epilog_status_string.
+Pointers may be given as torch tensors (device memory), integers or None.
+
+`Matmul` wraps them in the stateful plan / execute / free object with a context
+manager that the nvmath-python pages describe ("Fusing bias addition via the
+nvmath-python epilog mechanism", paragraph 4, lifecycle item; "Dissecting
+nvmath-python", paragraph on the plan-execute-free lifecycle). Its execute returns
+D, (D, {"relu_aux": mask}) for RELU_AUX_BIAS, or (D, {"drelu_bgrad": bgrad}) for
+DRELU_BGRAD, as the pages' auxiliary outputs ("Fusing epilogs with matrix
+multiplication using nvmath-python", sections on the forward epilogs and on the
+DRELU_BGRAD path).
+"""
+import ctypes
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgemm_epilog.so")
+
+F32, F16, BF16 = 0, 1, 2
+DTYPES = {"f32": F32, "f16": F16, "bf16": BF16}
+EPILOG = {"NONE": 0, "RELU_BIAS": 1, "GELU_BIAS": 2, "RELU_AUX_BIAS": 3, "DRELU_BGRAD": 4, "BIAS": 5,
+          "RELU_BIAS_UNFUSED": 100}
+STATUS = {0: "GE_OK", 1: "GE_ERR_INVALID_VALUE", 2: "GE_ERR_NOT_SUPPORTED", 3: "GE_ERR_NULL_POINTER",
+          4: "GE_ERR_MISALIGNED", 5: "GE_ERR_ALLOC", 6: "GE_ERR_HIP"}
+EXPORTS = ("gemm_epilog_plan", "gemm_epilog_execute", "gemm_epilog_free", "gemm_epilog_aux_bytes",
+           "gemm_epilog_workspace_bytes", "gemm_epilog_describe", "gemm_epilog_status_string")
+
+
+class ge_dtypes_t(ctypes.Structure):
+    _fields_ = [("ab", ctypes.c_int), ("d", ctypes.c_int), ("vec", ctypes.c_int)]
+
+
+class GemmEpilogError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {gemm_epilog_status_string(status)}")
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libgemm_epilog.so; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with gemm_epilogues_epilog_amd/build.py "
+                           "(or __graft_entry__.build()); there is no fallback path")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, c_int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.gemm_epilog_plan.argtypes = [i64, i64, i64, ge_dtypes_t, c_int, ctypes.POINTER(vp)]
+    L.gemm_epilog_plan.restype = c_int
+    L.gemm_epilog_execute.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
+    L.gemm_epilog_execute.restype = c_int
+    L.gemm_epilog_free.argtypes = [vp]
+    L.gemm_epilog_free.restype = c_int
+    L.gemm_epilog_aux_bytes.argtypes = [i64, i64]
+    L.gemm_epilog_aux_bytes.restype = ctypes.c_size_t
+    L.gemm_epilog_workspace_bytes.argtypes = [vp]
+    L.gemm_epilog_workspace_bytes.restype = ctypes.c_size_t
+    L.gemm_epilog_describe.argtypes = [vp]
+    L.gemm_epilog_describe.restype = ctypes.c_char_p
+    L.gemm_epilog_status_string.argtypes = [c_int]
+    L.gemm_epilog_status_string.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _dt(x) -> int:
+    return DTYPES[x] if isinstance(x, str) else int(x)
+
+
+def _ep(x) -> int:
+    return EPILOG[x] if isinstance(x, str) else int(x)
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return int(x.data_ptr())
+
+
+def gemm_epilog_status_string(status: int) -> str:
+    return load().gemm_epilog_status_string(int(status)).decode()
+
+
+def gemm_epilog_aux_bytes(m: int, n: int) -> int:
+    return int(load().gemm_epilog_aux_bytes(m, n))
+
+
+def gemm_epilog_plan(m: int, n: int, k: int, dtypes, epilog, check: bool = True):
+    """dtypes: (ab, d, vec) names or codes. Returns the handle (int), or
+    (status, handle) when check=False."""
+    ab, d, vec = (_dt(x) for x in dtypes)
+    h = ctypes.c_void_p()
+    st = load().gemm_epilog_plan(int(m), int(n), int(k), ge_dtypes_t(ab, d, vec), _ep(epilog), ctypes.byref(h))
+    if not check:
+        return st, h.value
+    if st != 0:
+        raise GemmEpilogError(st, "gemm_epilog_plan")
+    return h.value
+
+
+def gemm_epilog_execute(handle, A, B, bias=None, D=None, aux=None, bgrad=None, stream=None, check: bool = True):
+    """Enqueue one execute. stream: hipStream_t as int, a torch stream, or None for
+    torch's current stream on the current device."""
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream().cuda_stream
+    elif not isinstance(stream, int):
+        stream = stream.cuda_stream
+    st = load().gemm_epilog_execute(handle, _ptr(A), _ptr(B), _ptr(bias), _ptr(D), _ptr(aux), _ptr(bgrad), stream)
+    if check and st != 0:
+        raise GemmEpilogError(st, "gemm_epilog_execute")
+    return st
+
+
+def gemm_epilog_free(handle) -> int:
+    return int(load().gemm_epilog_free(handle))
+
+
+def gemm_epilog_workspace_bytes(handle) -> int:
+    return int(load().gemm_epilog_workspace_bytes(handle))
+
+
+def gemm_epilog_describe(handle) -> str:
+    return load().gemm_epilog_describe(handle).decode()
+
+
+_TORCH_NAME = {"torch.float32": "f32", "torch.float16": "f16", "torch.bfloat16": "bf16"}
+
+
+class Matmul:
+    """Stateful fused matmul over torch device tensors: plan once, execute many times.
+
+    mm = Matmul(m, n, k, "f16", "RELU_BIAS"); mm.plan(); D = mm.execute(A, B, bias); mm.free()
+    or `with Matmul(...) as mm:` which plans on entry and frees on exit.
+    """
+
+    def __init__(self, m: int, n: int, k: int, dtype: str, epilog: str, vec_dtype: Optional[str] = None):
+        self.m, self.n, self.k = int(m), int(n), int(k)
+        self.dtype, self.epilog = dtype, epilog
+        self.vec_dtype = vec_dtype or dtype
+        self.handle = None
+
+    def plan(self):
+        if self.handle is None:
+            self.handle = gemm_epilog_plan(self.m, self.n, self.k, (self.dtype, self.dtype, self.vec_dtype),
+                                           self.epilog)
+        return self
+
+    def describe(self) -> str:
+        return gemm_epilog_describe(self.handle) if self.handle is not None else ""
+
+    def execute(self, A, B, bias=None, relu_aux=None, out=None, bgrad=None, stream=None):
+        import torch
+        if self.handle is None:
+            self.plan()
+        for name, t in (("A", A), ("B", B)):
+            if not (t.is_cuda and t.is_contiguous() and _TORCH_NAME.get(str(t.dtype)) == self.dtype):
+                raise ValueError(f"{name} must be a contiguous {self.dtype} device tensor")
+        if tuple(A.shape) != (self.m, self.k) or tuple(B.shape) != (self.k, self.n):
+            raise ValueError("operand shapes do not match the plan")
+        if out is None:
+            out = torch.empty((self.m, self.n), dtype=A.dtype, device=A.device)
+        aux_words = (self.m + 31) // 32
+        if self.epilog == "RELU_AUX_BIAS" and relu_aux is None:
+            relu_aux = torch.empty((aux_words, self.n), dtype=torch.int32, device=A.device)
+        if self.epilog == "DRELU_BGRAD":
+            if relu_aux is None:
+                raise ValueError("DRELU_BGRAD needs the relu_aux mask of the forward pass")
+            if bgrad is None:
+                vt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[self.vec_dtype]
+                bgrad = torch.empty(self.m, dtype=vt, device=A.device)
+        gemm_epilog_execute(self.handle, A, B, bias, out, relu_aux, bgrad, stream)
+        if self.epilog == "RELU_AUX_BIAS":
+            return out, {"relu_aux": relu_aux}
+        if self.epilog == "DRELU_BGRAD":
+            return out, {"drelu_bgrad": bgrad}
+        return out
+
+    def free(self):
+        if self.handle is not None:
+            gemm_epilog_free(self.handle)
+            self.handle = None
+
+    def __enter__(self):
+        return self.plan()
+
+    def __exit__(self, *exc):
+        self.free()
+        return False
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass

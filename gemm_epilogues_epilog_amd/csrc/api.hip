@@ -1,0 +1,294 @@
+// Host runtime of the fused GEMM + epilogue library: argument validation, plan
+// (kernel configuration + workspace), execute (launches on the caller's stream),
+// free. The C ABI is declared in include/gemm_epilog.h.
+//
+// The plan / execute / free split follows the stateful matmul object of
+// "Dissecting nvmath-python: a seamless bridge between NumPy and cuBLASLt"
+// (blog.hotdry.top), paragraph on the plan-execute-free lifecycle, and
+// "nvmath-python wraps cuBLASLt" (blog.hotdry.top), body: planning is the costly
+// step done once, execution is light and repeated.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "gemm_epilog.h"
+#include "launch.hpp"
+
+struct ge_plan {
+  int64_t m;
+  int n, k;
+  ge_dtypes_t dt;
+  ge_epilog_t ep;
+  int cfg;                 // gek::CfgId
+  int device;
+  int tiles_m, tiles_n, group_m;
+  gek::LaunchFn gemm;      // main kernel (the NONE instance for the unfused chain)
+  void* ws;                // device workspace
+  size_t ws_bytes;
+  float* partial;          // DRELU_BGRAD per-wave row sums
+  int partial_cols;
+  void* t1;                // unfused intermediates
+  void* t2;
+  std::string desc;
+};
+
+namespace {
+
+size_t elem_size(ge_dtype_t d) { return d == GE_F32 ? 4 : 2; }
+
+bool known_dtype(int d) { return d == GE_F32 || d == GE_F16 || d == GE_BF16; }
+
+bool known_epilog(int e) {
+  return e == GE_EPILOG_NONE || e == GE_EPILOG_RELU_BIAS || e == GE_EPILOG_GELU_BIAS ||
+         e == GE_EPILOG_RELU_AUX_BIAS || e == GE_EPILOG_DRELU_BGRAD || e == GE_EPILOG_BIAS ||
+         e == GE_EPILOG_RELU_BIAS_UNFUSED;
+}
+
+bool uses_bias(ge_epilog_t e) {
+  return e == GE_EPILOG_RELU_BIAS || e == GE_EPILOG_GELU_BIAS || e == GE_EPILOG_RELU_AUX_BIAS ||
+         e == GE_EPILOG_BIAS || e == GE_EPILOG_RELU_BIAS_UNFUSED;
+}
+
+const char* dt_name(ge_dtype_t d) { return d == GE_F32 ? "f32" : d == GE_F16 ? "f16" : "bf16"; }
+
+const char* ep_name(ge_epilog_t e) {
+  switch (e) {
+    case GE_EPILOG_NONE: return "NONE";
+    case GE_EPILOG_RELU_BIAS: return "RELU_BIAS";
+    case GE_EPILOG_GELU_BIAS: return "GELU_BIAS";
+    case GE_EPILOG_RELU_AUX_BIAS: return "RELU_AUX_BIAS";
+    case GE_EPILOG_DRELU_BGRAD: return "DRELU_BGRAD";
+    case GE_EPILOG_BIAS: return "BIAS";
+    case GE_EPILOG_RELU_BIAS_UNFUSED: return "RELU_BIAS_UNFUSED";
+  }
+  return "?";
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Pick the largest tile that still gives every compute unit at least one tile;
+// fall back to the small tile for small problems.
+int choose_cfg(int64_t m, int n, ge_dtype_t ab, int cus) {
+  const char* env = std::getenv("GE_TILE");
+  if (env && env[0]) {
+    if (env[0] == 'S') return gek::CFG_S;
+    if (env[0] == 'M') return gek::CFG_M;
+    if (env[0] == 'L' && ab != GE_F32) return gek::CFG_L;
+  }
+  auto tiles = [&](int c) { return cdiv(m, gek::kTiles[c].bm) * cdiv(n, gek::kTiles[c].bn); };
+  if (ab != GE_F32 && tiles(gek::CFG_L) >= cus) return gek::CFG_L;
+  if (tiles(gek::CFG_M) >= cus) return gek::CFG_M;
+  return gek::CFG_S;
+}
+
+gek::LaunchFn lookup(ge_dtype_t ab, int ep, int cfg) {
+  switch (ab) {
+    case GE_F32: return gek::get_launch_f32(ep, cfg);
+    case GE_F16: return gek::get_launch_f16(ep, cfg);
+    case GE_BF16: return gek::get_launch_bf16(ep, cfg);
+  }
+  return nullptr;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gemm_epilog_status_string(ge_status_t s) {
+  switch (s) {
+    case GE_OK: return "GE_OK";
+    case GE_ERR_INVALID_VALUE: return "GE_ERR_INVALID_VALUE: a size or enum value is out of range";
+    case GE_ERR_NOT_SUPPORTED: return "GE_ERR_NOT_SUPPORTED: dtype combination or shape not supported";
+    case GE_ERR_NULL_POINTER: return "GE_ERR_NULL_POINTER: a required pointer is NULL";
+    case GE_ERR_MISALIGNED: return "GE_ERR_MISALIGNED: a pointer violates its alignment rule";
+    case GE_ERR_ALLOC: return "GE_ERR_ALLOC: allocation failed";
+    case GE_ERR_HIP: return "GE_ERR_HIP: a HIP runtime call failed";
+  }
+  return "unknown status";
+}
+
+size_t gemm_epilog_aux_bytes(int64_t m, int64_t n) {
+  if (m < 1 || n < 1) return 0;
+  return (size_t)4 * (size_t)cdiv(m, 32) * (size_t)n;
+}
+
+ge_status_t gemm_epilog_plan(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt, ge_epilog_t ep, ge_handle_t* out) {
+  // ---- host-only validation (no HIP call before this block passes) ----
+  if (!out) return GE_ERR_NULL_POINTER;
+  if (m < 1 || m > 0x7fffffffLL || n < 1 || n > (1LL << 20) || k < 1 || k > (1LL << 20))
+    return GE_ERR_INVALID_VALUE;
+  if (!known_dtype(dt.ab) || !known_dtype(dt.d) || !known_dtype(dt.vec) || !known_epilog(ep))
+    return GE_ERR_INVALID_VALUE;
+  if (dt.d != dt.ab) return GE_ERR_NOT_SUPPORTED;
+  if (dt.vec != dt.d && dt.vec != GE_F32) return GE_ERR_NOT_SUPPORTED;
+  const int64_t mult = dt.ab == GE_F32 ? 4 : 8;   // 16-byte rows
+  if (n % mult != 0 || k % mult != 0) return GE_ERR_NOT_SUPPORTED;
+  const int64_t tiles_bound = cdiv(m, 64) * cdiv(n, 64);
+  if (tiles_bound > 0x7fffffffLL) return GE_ERR_NOT_SUPPORTED;   // grid size
+
+  // ---- device query ----
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return GE_ERR_HIP;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GE_ERR_HIP;
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return GE_ERR_NOT_SUPPORTED;
+  const int cus = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
+
+  ge_plan* h = new (std::nothrow) ge_plan();
+  if (!h) return GE_ERR_ALLOC;
+  h->m = m;
+  h->n = (int)n;
+  h->k = (int)k;
+  h->dt = dt;
+  h->ep = ep;
+  h->device = dev;
+  h->cfg = choose_cfg(m, (int)n, dt.ab, cus);
+  const gek::TileCfg& tc = gek::kTiles[h->cfg];
+  h->tiles_m = (int)cdiv(m, tc.bm);
+  h->tiles_n = (int)cdiv(n, tc.bn);
+  h->group_m = 8;
+  const int kernel_ep = ep == GE_EPILOG_RELU_BIAS_UNFUSED ? (int)gek::NONE : (int)ep;
+  h->gemm = lookup(dt.ab, kernel_ep, h->cfg);
+  if (!h->gemm) {
+    delete h;
+    return GE_ERR_NOT_SUPPORTED;
+  }
+
+  // ---- workspace ----
+  const size_t es = elem_size(dt.d);
+  if (ep == GE_EPILOG_DRELU_BGRAD) {
+    h->partial_cols = (int)cdiv(n, tc.wn);
+    h->ws_bytes = (size_t)h->partial_cols * (size_t)m * sizeof(float);
+  } else if (ep == GE_EPILOG_RELU_BIAS_UNFUSED) {
+    h->ws_bytes = 2 * (size_t)m * (size_t)n * es;
+  }
+  if (h->ws_bytes) {
+    if (hipMalloc(&h->ws, h->ws_bytes) != hipSuccess) {
+      delete h;
+      return GE_ERR_ALLOC;
+    }
+    if (ep == GE_EPILOG_DRELU_BGRAD) {
+      h->partial = static_cast<float*>(h->ws);
+    } else {
+      h->t1 = h->ws;
+      h->t2 = static_cast<char*>(h->ws) + (size_t)m * (size_t)n * es;
+    }
+  }
+  h->desc = std::string(dt_name(dt.ab)) + " " + ep_name(ep) + " tile " + std::to_string(tc.bm) + "x" +
+            std::to_string(tc.bn) + " waves " + std::to_string(tc.bm / tc.wm) + "x" +
+            std::to_string(tc.bn / tc.wn) + " grid " + std::to_string(h->tiles_m * h->tiles_n);
+  *out = h;
+  return GE_OK;
+}
+
+ge_status_t gemm_epilog_execute(ge_handle_t h, const void* A, const void* B, const void* bias, void* D, void* aux,
+                                void* bgrad, void* stream) {
+  // ---- host-only validation ----
+  if (!h) return GE_ERR_NULL_POINTER;
+  if (!A || !B || !D) return GE_ERR_NULL_POINTER;
+  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(D, 16)) return GE_ERR_MISALIGNED;
+  const size_t vs = elem_size(h->dt.vec);
+  if (uses_bias(h->ep)) {
+    if (!bias) return GE_ERR_NULL_POINTER;
+    if (!aligned(bias, vs)) return GE_ERR_MISALIGNED;
+  }
+  if (h->ep == GE_EPILOG_RELU_AUX_BIAS || h->ep == GE_EPILOG_DRELU_BGRAD) {
+    if (!aux) return GE_ERR_NULL_POINTER;
+    if (!aligned(aux, 16)) return GE_ERR_MISALIGNED;
+  }
+  if (h->ep == GE_EPILOG_DRELU_BGRAD) {
+    if (!bgrad) return GE_ERR_NULL_POINTER;
+    if (!aligned(bgrad, vs)) return GE_ERR_MISALIGNED;
+  }
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  gek::Args a;
+  a.A = A;
+  a.B = B;
+  a.bias = bias;
+  a.D = (h->ep == GE_EPILOG_RELU_BIAS_UNFUSED) ? h->t1 : D;
+  a.aux = static_cast<uint32_t*>(aux);
+  a.partial = h->partial;
+  a.m = h->m;
+  a.n = h->n;
+  a.k = h->k;
+  a.vec_dt = (int)h->dt.vec;
+  a.tiles_m = h->tiles_m;
+  a.tiles_n = h->tiles_n;
+  a.group_m = h->group_m;
+  const int grid = h->tiles_m * h->tiles_n;
+
+  if (h->gemm(a, grid, s) != hipSuccess) return GE_ERR_HIP;
+  if (h->ep == GE_EPILOG_DRELU_BGRAD) {
+    if (gek::launch_bgrad_reduce(h->partial, h->partial_cols, h->m, bgrad, (int)h->dt.vec, s) != hipSuccess)
+      return GE_ERR_HIP;
+  } else if (h->ep == GE_EPILOG_RELU_BIAS_UNFUSED) {
+    if (gek::launch_bias_add((int)h->dt.d, h->t1, bias, (int)h->dt.vec, h->t2, h->m, h->n, s) != hipSuccess)
+      return GE_ERR_HIP;
+    if (gek::launch_relu((int)h->dt.d, h->t2, D, h->m, h->n, s) != hipSuccess) return GE_ERR_HIP;
+  }
+  return GE_OK;
+}
+
+ge_status_t gemm_epilog_free(ge_handle_t h) {
+  if (!h) return GE_OK;
+  ge_status_t st = GE_OK;
+  if (h->ws && hipFree(h->ws) != hipSuccess) st = GE_ERR_HIP;
+  delete h;
+  return st;
+}
+
+size_t gemm_epilog_workspace_bytes(ge_handle_t h) { return h ? h->ws_bytes : 0; }
+
+const char* gemm_epilog_describe(ge_handle_t h) { return h ? h->desc.c_str() : ""; }
+
+}  // extern "C"
+
+namespace gek {
+
+// ---- second pass of DRELU_BGRAD: bgrad[i] = sum over t ascending of partial[t][i] ----
+__global__ __launch_bounds__(256) void bgrad_reduce_kernel(const float* __restrict__ partial, int T, int64_t M,
+                                                           void* bgrad, int vec_dt) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= M) return;
+  float s = 0.0f;
+  for (int t = 0; t < T; ++t) s += partial[(int64_t)t * M + i];
+  store_vec(bgrad, vec_dt, i, s);
+}
+
+hipError_t launch_bias_add(int dt, const void* in, const void* bias, int vec_dt, void* out, int64_t m, int n,
+                           hipStream_t s) {
+  const int E = dt == F32 ? 4 : 8;
+  const int64_t chunks = m * (int64_t)n / E;
+  const dim3 grid((unsigned)cdiv(chunks, 256));
+  void* params[] = {&in, &bias, &vec_dt, &out, const_cast<int64_t*>(&chunks), &n};
+  const void* fn = dt == F32 ? reinterpret_cast<const void*>(&bias_add_kernel<F32>)
+                 : dt == F16 ? reinterpret_cast<const void*>(&bias_add_kernel<F16>)
+                             : reinterpret_cast<const void*>(&bias_add_kernel<BF16>);
+  return hipLaunchKernel(fn, grid, dim3(256), params, 0, s);
+}
+
+hipError_t launch_relu(int dt, const void* in, void* out, int64_t m, int n, hipStream_t s) {
+  const int E = dt == F32 ? 4 : 8;
+  const int64_t chunks = m * (int64_t)n / E;
+  const dim3 grid((unsigned)cdiv(chunks, 256));
+  void* params[] = {&in, &out, const_cast<int64_t*>(&chunks)};
+  const void* fn = dt == F32 ? reinterpret_cast<const void*>(&relu_kernel<F32>)
+                 : dt == F16 ? reinterpret_cast<const void*>(&relu_kernel<F16>)
+                             : reinterpret_cast<const void*>(&relu_kernel<BF16>);
+  return hipLaunchKernel(fn, grid, dim3(256), params, 0, s);
+}
+
+hipError_t launch_bgrad_reduce(const float* partial, int t, int64_t m, void* bgrad, int vec_dt, hipStream_t s) {
+  const dim3 grid((unsigned)cdiv(m, 256));
+  void* params[] = {&partial, &t, &m, &bgrad, &vec_dt};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&bgrad_reduce_kernel), grid, dim3(256), params, 0, s);
+}
+
+}  // namespace gek

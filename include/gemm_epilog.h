@@ -1,0 +1,160 @@
+/*
+ * gemm_epilog.h - C ABI of the fused GEMM + epilogue library for AMD Instinct MI355X (gfx950).
+ *
+ * One call computes D = epilogue(A . B) in a single HIP kernel: the bias add, the
+ * activation, the ReLU mask or the masked bias gradient are applied to the fp32
+ * accumulators before the only store of D.
+ *
+ * Sources (web pages describing the method):
+ *  [P1] "Fusing bias addition via the nvmath-python epilog mechanism: parameter
+ *       configuration and engineering practice guide" (blog.hotdry.top).
+ *  [P2] "nvmath-python wraps cuBLASLt: low-overhead matmul and bias-fusion primitives
+ *       for PyTorch" (blog.hotdry.top).
+ *  [P3] "Fusing epilogs with matrix multiplication using nvmath-python" (itzkxy.com).
+ *  [P4] "Dissecting nvmath-python: a seamless bridge between NumPy and cuBLASLt"
+ *       (blog.hotdry.top).
+ *  [P5] "Operator fusion in AI inference compilers: implementation and trade-offs"
+ *       (mqxn.cn).
+ *
+ * Lifecycle ([P4] paragraph on the plan-execute-free lifecycle; [P2] body, plan and
+ * execute steps; [P1] paragraph 4, second item): gemm_epilog_plan validates the
+ * problem, picks a kernel configuration and allocates the plan's workspace once;
+ * gemm_epilog_execute only enqueues work and may be called any number of times;
+ * gemm_epilog_free releases the plan.
+ *
+ * Layouts. Every matrix is dense row-major with no leading-dimension padding:
+ *   A (m, k), B (k, n), D (m, n). bias and bgrad hold m values, one per row of D:
+ *   the bias has shape (m,) or (m, 1) and is added to every column ([P1] paragraph 2;
+ *   [P2] body, initialisation example).
+ *   The ReLU mask (aux) is uint32 words [ceil(m/32)][n], row-major: bit (i % 32) of
+ *   word (i / 32, j) is 1 exactly when the pre-activation at (i, j) is > 0; bits of
+ *   rows i >= m are 0. The pages keep this mask opaque ([P1] paragraph 3, [P3]
+ *   section on the fused forward epilogs); this layout is the library's own.
+ *
+ * Arithmetic. Products are accumulated in fp32 whatever the storage type ([P2] body,
+ * plan step: FP32 accumulator with FP16 inputs/outputs; [P5] section 4.3). Every
+ * narrowing conversion rounds to nearest even. The order of the k reduction is the
+ * kernel's own; results agree with a plain ascending-k fp32 sum to rounding.
+ *
+ * Ownership and threading. The caller owns every tensor pointer and the stream; the
+ * plan owns only its workspace. A plan may be used from one stream at a time (its
+ * workspace is shared between executes). All pointers passed to execute are device
+ * pointers of the device that was current at plan time.
+ *
+ * Errors. Every argument check runs on the host before any HIP call, so invalid
+ * arguments never launch a kernel. Faults inside a kernel surface at the caller's
+ * next synchronisation, as for any asynchronous HIP work ([P1] paragraph 4, third
+ * item: execute is asynchronous and the caller synchronises the stream).
+ */
+#ifndef GEMM_EPILOG_H_
+#define GEMM_EPILOG_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ge_plan* ge_handle_t; /* opaque; owned by the library */
+
+/* Storage types. */
+typedef enum { GE_F32 = 0, GE_F16 = 1, GE_BF16 = 2 } ge_dtype_t;
+
+/* ab: type of A and B; d: type of D (must equal ab); vec: type of bias / bgrad
+ * (equal to d, or GE_F32) - [P1] paragraph 4, first item: with fp16 A and B the
+ * bias is fp16 or fp32. Accumulation is always fp32. */
+typedef struct {
+  ge_dtype_t ab;
+  ge_dtype_t d;
+  ge_dtype_t vec;
+} ge_dtypes_t;
+
+typedef enum {
+  /* D = A.B (no epilogue); also the first kernel of the unfused chain. */
+  GE_EPILOG_NONE = 0,
+  /* D = max(A.B + bias, 0)  ([P2] body, plan step; [P3] section on the fused forward epilogs). */
+  GE_EPILOG_RELU_BIAS = 1,
+  /* D = gelu(A.B + bias), tanh form 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3)))
+   * ([P1] final paragraph and [P2] "other epilogs" paragraph name GELU_BIAS). */
+  GE_EPILOG_GELU_BIAS = 2,
+  /* RELU_BIAS that also writes the packed ReLU mask to aux ([P1] paragraph 3; [P3]
+   * section on the fused forward epilogs). */
+  GE_EPILOG_RELU_AUX_BIAS = 3,
+  /* Backward: D = mask ? A.B : 0 using the mask in aux, and bgrad[i] = sum over j of
+   * that masked fp32 product, before D's rounding ([P3] section "The DRELU_BGRAD path
+   * in the backward pass"). No bias input. */
+  GE_EPILOG_DRELU_BGRAD = 4,
+  /* D = A.B + bias ([P1] paragraph 2). */
+  GE_EPILOG_BIAS = 5,
+  /* Measurement baseline: three kernels GEMM -> T1, T1 + bias -> T2, max(T2, 0) -> D,
+   * with T1 and T2 in D's type held in the plan's workspace ([P5] section 2.2 diagram
+   * of the chain before fusion). */
+  GE_EPILOG_RELU_BIAS_UNFUSED = 100
+} ge_epilog_t;
+
+typedef enum {
+  GE_OK = 0,
+  GE_ERR_INVALID_VALUE = 1, /* m, n or k out of range; unknown enum value */
+  GE_ERR_NOT_SUPPORTED = 2, /* dtype combination or shape outside the supported set */
+  GE_ERR_NULL_POINTER = 3,  /* a pointer the epilogue needs is NULL */
+  GE_ERR_MISALIGNED = 4,    /* a pointer violates its alignment rule */
+  GE_ERR_ALLOC = 5,         /* host or device allocation failed in plan */
+  GE_ERR_HIP = 6            /* a HIP runtime call failed (launch, device query) */
+} ge_status_t;
+
+/*
+ * gemm_epilog_plan - validate a problem and build its plan.
+ *   m, n, k : problem sizes, 1 <= m <= 2^31 - 1, 1 <= n, k <= 2^20.
+ *             n and k must be multiples of 8 for fp16/bf16 and of 4 for fp32
+ *             (16-byte rows); otherwise GE_ERR_NOT_SUPPORTED. m is arbitrary.
+ *   dt      : storage types (see ge_dtypes_t).
+ *   ep      : epilogue.
+ *   out     : receives the handle; untouched on error.
+ * Allocates the workspace on the current device: the per-tile bias-gradient
+ * partial sums for DRELU_BGRAD, T1 and T2 for RELU_BIAS_UNFUSED, nothing otherwise.
+ * Environment: GE_TILE=S|M|L forces a tile configuration (tuning experiments).
+ */
+ge_status_t gemm_epilog_plan(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt, ge_epilog_t ep,
+                             ge_handle_t* out);
+
+/*
+ * gemm_epilog_execute - enqueue the planned computation on `stream` and return.
+ *   A, B   : device inputs (m,k) and (k,n), type dt.ab, 16-byte aligned.
+ *   bias   : device, m values of type dt.vec, aligned to its element size.
+ *            Read by BIAS, RELU_BIAS, GELU_BIAS, RELU_AUX_BIAS, RELU_BIAS_UNFUSED;
+ *            ignored (may be NULL) otherwise.
+ *   D      : device output (m,n), type dt.d, 16-byte aligned.
+ *   aux    : device mask words, gemm_epilog_aux_bytes(m,n) bytes, 16-byte aligned.
+ *            Written by RELU_AUX_BIAS, read by DRELU_BGRAD, ignored otherwise.
+ *   bgrad  : device output, m values of type dt.vec, aligned to its element size.
+ *            Written by DRELU_BGRAD, ignored otherwise.
+ *   stream : a hipStream_t; NULL means the null stream.
+ * Every output element in range is written; nothing outside the stated extents is.
+ * Returns GE_ERR_HIP if a launch fails.
+ */
+ge_status_t gemm_epilog_execute(ge_handle_t h, const void* A, const void* B, const void* bias, void* D,
+                                void* aux, void* bgrad, void* stream);
+
+/* gemm_epilog_free - release a plan and its workspace. NULL is accepted (GE_OK).
+ * Must not be called while an execute on this plan may still be running. */
+ge_status_t gemm_epilog_free(ge_handle_t h);
+
+/* Bytes of the ReLU mask for an (m, n) output: 4 * ceil(m/32) * n (0 if m or n < 1). */
+size_t gemm_epilog_aux_bytes(int64_t m, int64_t n);
+
+/* Bytes of device workspace held by a plan (0 for NULL). */
+size_t gemm_epilog_workspace_bytes(ge_handle_t h);
+
+/* Human-readable name of the kernel configuration a plan chose, e.g.
+ * "f16 RELU_BIAS tile 256x256 waves 2x2". Valid while the plan lives; "" for NULL. */
+const char* gemm_epilog_describe(ge_handle_t h);
+
+/* Static string for a status code. */
+const char* gemm_epilog_status_string(ge_status_t s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM_EPILOG_H_ */

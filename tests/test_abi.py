@@ -1,0 +1,111 @@
+"""C-ABI checks that run without a GPU: the library loads, exports every function that
+include/*.h declares, and rejects invalid arguments on the host before any HIP call."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import gemm_epilogues_epilog_amd as ge
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^[A-Za-z_][\w\s\*]*?\b(gemm_epilog_\w+)\s*\(", text, flags=re.M):
+            names.add(m.group(1))
+    return sorted(names)
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("gemm_epilog_plan", "gemm_epilog_execute", "gemm_epilog_free"):
+        assert required in names
+    assert set(names) == set(ge.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(ge.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} is declared in include/ but not exported"
+
+
+def test_aux_bytes():
+    assert ge.gemm_epilog_aux_bytes(64, 48) == 4 * 2 * 48
+    assert ge.gemm_epilog_aux_bytes(33, 8) == 4 * 2 * 8
+    assert ge.gemm_epilog_aux_bytes(8192, 8192) == 8192 * 8192 // 8
+    assert ge.gemm_epilog_aux_bytes(0, 8) == 0
+    assert ge.gemm_epilog_aux_bytes(8, -1) == 0
+
+
+def test_status_strings():
+    for code, name in ge.STATUS.items():
+        assert ge.gemm_epilog_status_string(code).startswith(name)
+    assert ge.gemm_epilog_status_string(99) == "unknown status"
+
+
+F16 = ("f16", "f16", "f16")
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, 8, 8, F16, "RELU_BIAS"), 1),                      # m < 1
+    ((8, 0, 8, F16, "RELU_BIAS"), 1),                      # n < 1
+    ((8, 8, 0, F16, "RELU_BIAS"), 1),                      # k < 1
+    ((8, 8, (1 << 20) + 8, F16, "RELU_BIAS"), 1),          # k too large
+    ((1 << 31, 8, 8, F16, "RELU_BIAS"), 1),                # m too large
+    ((8, 8, 8, F16, 7), 1),                                # unknown epilogue
+    ((8, 8, 8, (5, 1, 1), "RELU_BIAS"), 1),                # unknown dtype
+    ((8, 8, 8, ("f16", "bf16", "f16"), "RELU_BIAS"), 2),   # D type differs from A/B
+    ((8, 8, 8, ("f16", "f16", "bf16"), "RELU_BIAS"), 2),   # bias neither D's type nor fp32
+    ((8, 12, 8, F16, "RELU_BIAS"), 2),                     # n not a multiple of 8
+    ((8, 8, 20, F16, "RELU_BIAS"), 2),                     # k not a multiple of 8
+    ((8, 6, 8, ("f32", "f32", "f32"), "RELU_BIAS"), 2),    # n not a multiple of 4
+])
+def test_plan_rejects_invalid_arguments(args, status):
+    st, h = ge.gemm_epilog_plan(*args, check=False)
+    assert st == status
+    assert h is None
+
+
+def test_plan_null_out():
+    lib = ge.load()
+    st = lib.gemm_epilog_plan(8, 8, 8, ge.ge_dtypes_t(1, 1, 1), 1, None)
+    assert st == 3
+
+
+def test_execute_null_handle_and_free_null():
+    lib = ge.load()
+    assert lib.gemm_epilog_execute(None, 16, 16, 16, 16, None, None, None) == 3
+    assert ge.gemm_epilog_free(None) == 0
+    assert ge.gemm_epilog_workspace_bytes(None) == 0
+    assert ge.gemm_epilog_describe(None) == ""
+
+
+def test_valid_plan_without_gpu_reports_hip_error():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible: plan succeeds here")
+    st, h = ge.gemm_epilog_plan(64, 48, 32, ("f32", "f32", "f32"), "RELU_AUX_BIAS", check=False)
+    assert st == 6 and h is None
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(ge, "_lib", None)
+    monkeypatch.setattr(ge, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        ge.load()
+
+
+def test_product_path_does_not_import_the_oracle():
+    pkg = os.path.join(ROOT, "gemm_epilogues_epilog_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle|liboracle|oracle\.cpp", text, flags=re.M), \
+                    f"{f} reaches into the oracle"

@@ -1,0 +1,167 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+* integer-valued inputs: every product and sum is exact, so D, the mask and bgrad
+  must equal the oracle bit for bit (all epilogues but GELU, all dtypes, all tile
+  configurations, ragged m, several k-tiles and a ragged k tail);
+* random normal inputs: the tolerances of the fused-epilogue path, plus a tighter
+  rounding-model ratio;
+* guard zones around every output, run-to-run bitwise determinism, host-side errors.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gemm_epilogues_epilog_amd import inputs
+from tests import gpu_runner as R
+from tests.helpers import assert_bgrad, assert_close, assert_mask, tight_ratio, to_np
+
+pytestmark = pytest.mark.gpu
+
+DTS = ["f32", "f16", "bf16"]
+TILES = {"f32": ["S", "M"], "f16": ["S", "M", "L"], "bf16": ["S", "M", "L"]}
+INT_SHAPES = [(1, 8, 8), (33, 136, 72), (200, 264, 200), (300, 520, 136)]
+
+
+def cases_int():
+    for dt in DTS:
+        for tile in TILES[dt]:
+            for shape in INT_SHAPES:
+                yield dt, tile, shape
+
+
+@pytest.mark.parametrize("dt,tile,shape", list(cases_int()))
+def test_integer_exact_all_epilogues(gpu, dt, tile, shape):
+    m, n, k = shape
+    print(f"[case] integer {dt} tile {tile} m={m} n={n} k={k}", flush=True)
+    A, B, bias, A2, B2 = inputs.integer_case(m, n, k, dt)
+    a, b, c = to_np(A), to_np(B), to_np(bias)
+    for ep in ("NONE", "BIAS", "RELU_BIAS", "RELU_BIAS_UNFUSED"):
+        g = R.run(gpu, ep, dt, A, B, bias, tile=tile)
+        o = oracle.gemm_epilog(a, b, ep, bias=c, ab=dt)
+        assert np.array_equal(g["D"].view(np.uint8), o["D"].view(np.uint8)), f"{ep} {g['desc']}"
+    g = R.run(gpu, "RELU_AUX_BIAS", dt, A, B, bias, tile=tile)
+    o = oracle.gemm_epilog(a, b, "RELU_AUX_BIAS", bias=c, ab=dt)
+    assert np.array_equal(g["D"].view(np.uint8), o["D"].view(np.uint8)), g["desc"]
+    assert np.array_equal(g["mask"].view(np.uint32), o["mask"]), g["desc"]
+    mask = torch.from_numpy(o["mask"].view(np.int32).copy())
+    gb = R.run(gpu, "DRELU_BGRAD", dt, A2, B2, mask=mask, tile=tile)
+    ob = oracle.gemm_epilog(to_np(A2), to_np(B2), "DRELU_BGRAD", mask=o["mask"], ab=dt)
+    assert np.array_equal(gb["D"].view(np.uint8), ob["D"].view(np.uint8)), gb["desc"]
+    assert np.array_equal(gb["bgrad"].view(np.uint8), ob["bgrad"].view(np.uint8)), gb["desc"]
+
+
+@pytest.mark.parametrize("dt", DTS)
+def test_integer_exact_fp32_vectors(gpu, dt):
+    # bias and bgrad in fp32 with 16-bit matrices (and fp32 with fp32)
+    m, n, k = 96, 72, 40
+    A, B, bias, A2, B2 = inputs.integer_case(m, n, k, dt, vec="f32")
+    o = oracle.gemm_epilog(to_np(A), to_np(B), "RELU_AUX_BIAS", bias=to_np(bias), ab=dt, vec="f32")
+    g = R.run(gpu, "RELU_AUX_BIAS", dt, A, B, bias, vec="f32")
+    assert np.array_equal(g["D"].view(np.uint8), o["D"].view(np.uint8))
+    assert np.array_equal(g["mask"].view(np.uint32), o["mask"])
+    mask = torch.from_numpy(o["mask"].view(np.int32).copy())
+    gb = R.run(gpu, "DRELU_BGRAD", dt, A2, B2, mask=mask, vec="f32")
+    ob = oracle.gemm_epilog(to_np(A2), to_np(B2), "DRELU_BGRAD", mask=o["mask"], ab=dt, vec="f32")
+    assert np.array_equal(gb["bgrad"], ob["bgrad"])
+
+
+RAND_SHAPES = [(64, 48, 32), (130, 200, 264), (257, 392, 520), (512, 256, 1024)]
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("shape", RAND_SHAPES)
+def test_random_parity(gpu, dt, shape):
+    m, n, k = shape
+    print(f"[case] random {dt} m={m} n={n} k={k}", flush=True)
+    A, B, bias, A2, B2 = inputs.small_case(m, n, k, dt, std=1.0, std_bias=1.0)
+    a, b, c = to_np(A), to_np(B), to_np(bias)
+    wa, wb = oracle.to_f32(a, dt), oracle.to_f32(b, dt)
+    for tile in TILES[dt]:
+        for ep in ("RELU_BIAS", "GELU_BIAS", "BIAS"):
+            g = R.run(gpu, ep, dt, A, B, bias, tile=tile)
+            o = oracle.gemm_epilog(a, b, ep, bias=c, ab=dt)
+            assert_close(g["D"], o["D"], dt, f"{ep} {g['desc']}")
+            slope = 1.13 if ep == "GELU_BIAS" else 1.0
+            extra = 64.0 if (ep == "GELU_BIAS" and dt == "f32") else 0.0
+            r = tight_ratio(g["D"], o["D"], dt, wa, wb, slope)
+            assert r <= 4.0 + extra, f"{ep} {g['desc']}: rounding-model ratio {r}"
+        g = R.run(gpu, "RELU_AUX_BIAS", dt, A, B, bias, tile=tile)
+        o = oracle.gemm_epilog(a, b, "RELU_AUX_BIAS", bias=c, ab=dt, want_pre=True)
+        assert_close(g["D"], o["D"], dt, g["desc"])
+        assert_mask(g["mask"], o["mask"], o["pre"], m)
+        mask = torch.from_numpy(g["mask"].view(np.int32).copy())   # the GPU forward's mask
+        gb = R.run(gpu, "DRELU_BGRAD", dt, A2, B2, mask=mask, tile=tile)
+        ob = oracle.gemm_epilog(to_np(A2), to_np(B2), "DRELU_BGRAD", mask=g["mask"].view(np.uint32), ab=dt)
+        assert_close(gb["D"], ob["D"], dt, gb["desc"])
+        assert_bgrad(gb["bgrad"], ob["bgrad"], ob["absum"], dt)
+
+
+def test_zero_A_closed_form(gpu):
+    m, n, k = 300, 264, 136
+    _, B, bias, _, _ = inputs.small_case(m, n, k, "f16")
+    A = torch.zeros(m, k, dtype=torch.float16)
+    g = R.run(gpu, "RELU_AUX_BIAS", "f16", A, B, bias)
+    bv = bias.float().numpy()
+    assert np.array_equal(g["D"].astype(np.float32), np.repeat(np.maximum(bv, 0)[:, None], n, 1))
+    from tests.helpers import unpack_mask
+    assert np.array_equal(unpack_mask(g["mask"], m), np.repeat((bv > 0)[:, None], n, 1))
+    gb = R.run(gpu, "DRELU_BGRAD", "f16", A, B, mask=torch.from_numpy(g["mask"].view(np.int32).copy()))
+    assert not gb["D"].astype(np.float32).any() and not gb["bgrad"].astype(np.float32).any()
+
+
+def test_deterministic_and_repeatable(gpu):
+    m, n, k = 512, 520, 1032
+    A, B, bias, A2, B2 = inputs.small_case(m, n, k, "bf16")
+    g1 = R.run(gpu, "RELU_AUX_BIAS", "bf16", A, B, bias)
+    g2 = R.run(gpu, "RELU_AUX_BIAS", "bf16", A, B, bias, repeat=3)
+    assert np.array_equal(g1["D"], g2["D"]) and np.array_equal(g1["mask"], g2["mask"])
+    mask = torch.from_numpy(g1["mask"].view(np.int32).copy())
+    b1 = R.run(gpu, "DRELU_BGRAD", "bf16", A2, B2, mask=mask)
+    b2 = R.run(gpu, "DRELU_BGRAD", "bf16", A2, B2, mask=mask, repeat=2)
+    assert np.array_equal(b1["D"], b2["D"]) and np.array_equal(b1["bgrad"], b2["bgrad"])
+
+
+def test_execute_rejects_bad_pointers_on_host(gpu):
+    ge = gpu
+    h = ge.gemm_epilog_plan(64, 64, 64, ("f16", "f16", "f16"), "RELU_AUX_BIAS")
+    try:
+        A = torch.zeros(64 * 64 + 8, dtype=torch.float16, device="cuda")
+        D = torch.zeros(64, 64, dtype=torch.float16, device="cuda")
+        bias = torch.zeros(64, dtype=torch.float16, device="cuda")
+        aux = torch.zeros(2, 64, dtype=torch.int32, device="cuda")
+        mis = A.data_ptr() + 2
+        assert ge.gemm_epilog_execute(h, mis, A, bias, D, aux, None, check=False) == 4
+        assert ge.gemm_epilog_execute(h, A, A, None, D, aux, None, check=False) == 3
+        assert ge.gemm_epilog_execute(h, A, A, bias, D, None, None, check=False) == 3
+        assert ge.gemm_epilog_execute(h, A, A, bias.data_ptr() + 1, D, aux, None, check=False) == 4
+        assert ge.gemm_epilog_execute(h, A, A, bias, D, aux.data_ptr() + 4, None, check=False) == 4
+        assert ge.gemm_epilog_execute(h, A, A, bias, None, aux, None, check=False) == 3
+        torch.cuda.synchronize()
+    finally:
+        ge.gemm_epilog_free(h)
+
+
+def test_matmul_wrapper_round_trip(gpu):
+    m, n, k = 64, 48, 32
+    A, B, bias, A2, B2 = inputs.small_case(m, n, k, "f32", std_bias=0.1)
+    with gpu.Matmul(m, n, k, "f32", "RELU_AUX_BIAS") as mm:
+        D, aux = mm.execute(A.cuda(), B.cuda(), bias.cuda())
+        assert "relu_aux" in aux and aux["relu_aux"].shape == ((m + 31) // 32, n)
+        assert gpu.gemm_epilog_workspace_bytes(mm.handle) == 0
+    with gpu.Matmul(m, n, k, "f32", "DRELU_BGRAD") as mm:
+        dZ, g = mm.execute(A2.cuda(), B2.cuda(), relu_aux=aux["relu_aux"])
+        assert gpu.gemm_epilog_workspace_bytes(mm.handle) > 0
+    torch.cuda.synchronize()
+    ref = oracle.gemm_epilog(A2.numpy(), B2.numpy(), "DRELU_BGRAD", mask=to_np(aux["relu_aux"]), ab="f32")
+    assert_close(to_np(dZ), ref["D"], "f32")
+    assert_bgrad(to_np(g["drelu_bgrad"]), ref["bgrad"], ref["absum"], "f32")
+
+
+def test_stream_argument(gpu):
+    m, n, k = 128, 128, 128
+    A, B, bias, _, _ = inputs.small_case(m, n, k, "f16")
+    s = torch.cuda.Stream()
+    g = R.run(gpu, "RELU_BIAS", "f16", A, B, bias, stream=s)
+    o = oracle.gemm_epilog(to_np(A), to_np(B), "RELU_BIAS", bias=to_np(bias))
+    assert_close(g["D"], o["D"], "f16")
