@@ -68,6 +68,31 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, kBufDword3);
 }
 
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding: vmcnt
+// bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup id -> (m-tile, n-tile). Workgroups are dealt to the 8 XCDs round-robin;
+// renumber them so each XCD walks a contiguous range of tiles, then walk tiles in
+// groups of group_m m-tiles (m fastest inside a group) so tiles that run together
+// share A and B in the XCD's L2.
+__device__ __forceinline__ void tile_coords(const Args& p, int& tm, int& tn) {
+  const int G = p.tiles_m * p.tiles_n;
+  int id = blockIdx.x;
+  const int per = G / 8, rem = G % 8, x = id % 8, local = id / 8;
+  id = (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + local;
+  const int gsz = p.group_m * p.tiles_n;
+  const int g = id / gsz, first_m = g * p.group_m;
+  const int rows = min(p.tiles_m - first_m, p.group_m);
+  const int in = id - g * gsz;
+  tm = first_m + in % rows;
+  tn = in / rows;
+}
+
 // ---- element traits ------------------------------------------------------------
 
 template <int DT> struct Tr;
@@ -149,199 +174,17 @@ __device__ __forceinline__ float activate(float pre) {
   else return pre;
 }
 
-// ---- the fused kernel ----------------------------------------------------------
-
-template <int DT, int EP, int BM, int BN, int WM, int WN>
-struct Cfg {
+// ---- epilogue on the accumulators ---------------------------------------------
+// A wave's accumulators acc[a][b] (32x32 MFMA blocks, fp32) cover rows m0w + 32 b
+// and columns n0w + 32 a. Lane l holds row m0w + 32 b + l % 32; register r holds
+// column n0w + 32 a + 8 (r / 4) + 4 (l / 32) + r % 4. D is written once, from here.
+template <int DT, int EP, int MB, int NB, int WN>
+__device__ __forceinline__ void epilogue(const Args& p, f32x16 (&acc)[NB][MB], int64_t m0w, int n0w, int lane) {
   using T = Tr<DT>;
-  static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
-  static constexpr int NW = WAVES_M * WAVES_N, NT = NW * 64;
-  static constexpr int MB = WM / 32, NB = WN / 32;
-  static constexpr int E = T::E, es = T::es;
-  static constexpr int BK = kRowBytes / es;              // k per tile (= 8 E)
-  static constexpr int STAGE = (BM + BN) * kRowBytes;    // LDS bytes per stage
-  static constexpr int A_LD = BM * 8 / NT;               // A chunks per thread per tile
-  // B: each thread transposes R k-rows x E columns; B_LD such blocks per tile
-  static constexpr int R0 = 8 * BN / NT;
-  static constexpr int R = R0 < E ? R0 : E;
-  static constexpr int B_LD = 8 * BN / (NT * R);
-  static constexpr int NBN = BN / E;                     // E-wide column blocks of the B tile
-  static constexpr int KSTEPS = kRowBytes / 32;          // k-steps (two chunks each) per tile
-  static_assert(BM % WM == 0 && BN % WN == 0 && WM % 32 == 0 && WN % 32 == 0, "tile shape");
-  static_assert((BM * 8) % NT == 0 && A_LD >= 1, "A tile split");
-  static_assert(R >= 1 && (DT == F32 || R >= 2) && E % R == 0 && B_LD >= 1 && (8 * BN) % (NT * R) == 0,
-                "B tile split");
-};
-
-template <int DT, int EP, int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_epilog_kernel(Args p) {
-  using C = Cfg<DT, EP, BM, BN, WM, WN>;
-  using T = typename C::T;
-  constexpr int NT = C::NT, E = C::E, es = C::es, R = C::R;
-  constexpr int MB = C::MB, NB = C::NB;
-
-  __shared__ __attribute__((aligned(16))) char lds[2 * C::STAGE];
-
+  constexpr int es = T::es;
   const int64_t M = p.m;
-  const int N = p.n, K = p.k;
-
-  // ---- tile rasterisation ----------------------------------------------------
-  // Workgroups are dealt to the 8 XCDs round-robin; renumber them so that each XCD
-  // walks a contiguous range of tiles, then walk tiles in groups of group_m m-tiles
-  // (m fastest inside a group) so tiles running together share A and B in L2.
-  const int G = p.tiles_m * p.tiles_n;
-  int id = blockIdx.x;
-  {
-    const int per = G / 8, rem = G % 8, x = id % 8, local = id / 8;
-    id = (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + local;
-  }
-  int tm, tn;
-  {
-    const int gsz = p.group_m * p.tiles_n;
-    const int g = id / gsz, first_m = g * p.group_m;
-    const int rows = min(p.tiles_m - first_m, p.group_m);
-    const int in = id - g * gsz;
-    tm = first_m + in % rows;
-    tn = in / rows;
-  }
-  const int64_t m0 = (int64_t)tm * BM;
-  const int n0 = tn * BN;
-
-  const int t = threadIdx.x;
-  const int lane = t & 63, w = t >> 6;
-  const int wm = w % C::WAVES_M, wn = w / C::WAVES_M;
+  const int N = p.n;
   const int lrow = lane & 31, lhi = lane >> 5;
-
-  // ---- global -> register load plan -----------------------------------------
-  const int a_ch = t & 7;                      // chunk of the A row this thread copies
-  uint32_t a_off[C::A_LD];
-  int a_lds[C::A_LD];
-#pragma unroll
-  for (int i = 0; i < C::A_LD; ++i) {
-    const int row = (t + i * NT) >> 3;
-    a_off[i] = (m0 + row < M) ? (uint32_t)(row * K * es + a_ch * 16) : kOOB;
-    a_lds[i] = row * kRowBytes + ((a_ch ^ (row & 7)) << 4);
-  }
-  uint32_t b_off[C::B_LD];
-  int b_kr[C::B_LD];       // first k-row of the block inside the tile
-  int b_nc[C::B_LD];       // first column of the block inside the tile
-#pragma unroll
-  for (int i = 0; i < C::B_LD; ++i) {
-    const int q = t + i * NT;
-    const int nb = q % C::NBN, kb = q / C::NBN;
-    b_kr[i] = kb * R;
-    b_nc[i] = nb * E;
-    b_off[i] = (n0 + nb * E < N) ? (uint32_t)(kb * R * N * es + nb * 16) : kOOB;
-  }
-
-  const char* Abase = static_cast<const char*>(p.A) + m0 * (int64_t)K * es;
-  const char* Bbase = static_cast<const char*>(p.B) + (int64_t)n0 * es;
-  const int KT = (K + C::BK - 1) / C::BK;
-
-  i32x4 areg[C::A_LD];
-  i32x4 breg[C::B_LD][R];
-
-  auto load_tile = [&](int kt) {
-    const int k0 = kt * C::BK;
-    const __amdgpu_buffer_rsrc_t ra = rsrc(Abase + (int64_t)kt * kRowBytes);
-    const __amdgpu_buffer_rsrc_t rb = rsrc(Bbase + (int64_t)k0 * N * es);
-    const bool a_kok = k0 + a_ch * E < K;
-#pragma unroll
-    for (int i = 0; i < C::A_LD; ++i)
-      areg[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, a_kok ? a_off[i] : kOOB, 0, 0);
-#pragma unroll
-    for (int i = 0; i < C::B_LD; ++i) {
-#pragma unroll
-      for (int kk = 0; kk < R; ++kk) {
-        const bool kok = k0 + b_kr[i] + kk < K;
-        breg[i][kk] = __builtin_amdgcn_raw_buffer_load_b128(rb, kok ? b_off[i] + (uint32_t)(kk * N * es) : kOOB, 0, 0);
-      }
-    }
-  };
-
-  auto store_tile = [&](int stage) {
-    char* sA = lds + stage * C::STAGE;
-    char* sB = sA + BM * kRowBytes;
-#pragma unroll
-    for (int i = 0; i < C::A_LD; ++i) *reinterpret_cast<i32x4*>(sA + a_lds[i]) = areg[i];
-#pragma unroll
-    for (int i = 0; i < C::B_LD; ++i) {
-      // transpose R rows x E columns into E columns x R k-values
-      const int kbyte = b_kr[i] * es;                 // byte offset of the k-run in an LDS row
-      const int chunk = kbyte >> 4, within = kbyte & 15;
-#pragma unroll
-      for (int c = 0; c < E; ++c) {
-        const int row = b_nc[i] + c;
-        char* dst = sB + row * kRowBytes + ((chunk ^ (row & 7)) << 4) + within;
-        if constexpr (es == 4) {
-          if constexpr (R == 4) {
-            i32x4 v = {breg[i][0][c], breg[i][1][c], breg[i][2][c], breg[i][3][c]};
-            *reinterpret_cast<i32x4*>(dst) = v;
-          } else if constexpr (R == 2) {
-            i32x2 v = {breg[i][0][c], breg[i][1][c]};
-            *reinterpret_cast<i32x2*>(dst) = v;
-          } else {
-            *reinterpret_cast<int*>(dst) = breg[i][0][c];
-          }
-        } else {
-          // 16-bit: column c sits in dword c/2 of every row, low half for even c
-          const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-          uint32_t d[R / 2];
-#pragma unroll
-          for (int e = 0; e < R / 2; ++e)
-            d[e] = __builtin_amdgcn_perm((uint32_t)breg[i][2 * e + 1][c >> 1], (uint32_t)breg[i][2 * e][c >> 1], sel);
-          if constexpr (R == 8) {
-            i32x4 v = {(int)d[0], (int)d[1], (int)d[2], (int)d[3]};
-            *reinterpret_cast<i32x4*>(dst) = v;
-          } else if constexpr (R == 4) {
-            i32x2 v = {(int)d[0], (int)d[1]};
-            *reinterpret_cast<i32x2*>(dst) = v;
-          } else {
-            *reinterpret_cast<int*>(dst) = (int)d[0];
-          }
-        }
-      }
-    }
-  };
-
-  f32x16 acc[NB][MB];
-#pragma unroll
-  for (int a = 0; a < NB; ++a)
-#pragma unroll
-    for (int b = 0; b < MB; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
-
-  // ---- main loop: double-buffered LDS, one barrier per k-tile ----------------
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) load_tile(kt + 1);
-    const char* sA = lds + cur * C::STAGE + (wm * WM + lrow) * kRowBytes;
-    const char* sB = lds + cur * C::STAGE + BM * kRowBytes + (wn * WN + lrow) * kRowBytes;
-#pragma unroll
-    for (int s = 0; s < C::KSTEPS; ++s) {
-      const int phys = ((2 * s + lhi) ^ (lrow & 7)) << 4;
-      i32x4 af[MB], bf[NB];
-#pragma unroll
-      for (int b = 0; b < MB; ++b) af[b] = *reinterpret_cast<const i32x4*>(sA + b * 32 * kRowBytes + phys);
-#pragma unroll
-      for (int a = 0; a < NB; ++a) bf[a] = *reinterpret_cast<const i32x4*>(sB + a * 32 * kRowBytes + phys);
-#pragma unroll
-      for (int a = 0; a < NB; ++a)
-#pragma unroll
-        for (int b = 0; b < MB; ++b) acc[a][b] = T::mma(bf[a], af[b], acc[a][b]);
-    }
-    if (kt + 1 < KT) store_tile(cur ^ 1);
-    __syncthreads();
-  }
-
-  // ---- epilogue on the accumulators ------------------------------------------
-  // acc[a][b][r]: row m = m0w + 32 b + lrow, column n = n0w + 32 a + 8 (r/4) + 4 lhi + r%4
-  const int64_t m0w = m0 + wm * WM;
-  const int n0w = n0 + wn * WN;
   char* Dw = static_cast<char*>(p.D) + (m0w * (int64_t)N + n0w) * es;
   const __amdgpu_buffer_rsrc_t rd = rsrc(Dw);
 
@@ -435,7 +278,6 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_epilog_ker
     }
   }
 }
-
 // ---- unfused baseline, kernels 2 and 3 ----------------------------------------
 // T2 = round(T1 + bias[row]) and D = max(T2, 0), 16 bytes per thread, rows of n
 // elements (n is a multiple of the 16-byte element count).

@@ -4,7 +4,8 @@
 
 #include <hip/hip_runtime.h>
 
-#include "kernels.hpp"
+#include "gemm_dtl.hpp"
+#include "gemm_generic.hpp"
 
 namespace gek {
 
@@ -19,19 +20,25 @@ enum CfgId { CFG_S = 0, CFG_M = 1, CFG_L = 2, CFG_COUNT = 3 };
 constexpr TileCfg kTiles[CFG_COUNT] = {
     {64, 64, 32, 32, "S"},
     {128, 128, 64, 64, "M"},
-    {256, 256, 128, 128, "L"},
+    {256, 256, 128, 64, "L"},
 };
 
 inline int threads_of(const TileCfg& c) { return (c.bm / c.wm) * (c.bn / c.wn) * 64; }
 
 using LaunchFn = hipError_t (*)(const Args&, int grid, hipStream_t);
 
+// 16-bit types with tiles of at least 128 columns use the direct-to-LDS kernel;
+// fp32 and the small tile use the register-staged kernel.
 template <int DT, int EP, int BM, int BN, int WM, int WN>
 hipError_t launch_gemm(const Args& a, int grid, hipStream_t s) {
   Args copy = a;
   void* params[] = {&copy};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_epilog_kernel<DT, EP, BM, BN, WM, WN>), dim3(grid),
-                         dim3((BM / WM) * (BN / WN) * 64), params, 0, s);
+  const void* fn;
+  if constexpr (DT != F32 && BN >= 128)
+    fn = reinterpret_cast<const void*>(&gemm_dtl_kernel<DT, EP, BM, BN, WM, WN>);
+  else
+    fn = reinterpret_cast<const void*>(&gemm_epilog_kernel<DT, EP, BM, BN, WM, WN>);
+  return hipLaunchKernel(fn, dim3(grid), dim3((BM / WM) * (BN / WN) * 64), params, 0, s);
 }
 
 template <int DT, int EP>
@@ -40,7 +47,7 @@ LaunchFn pick_cfg(int cfg) {
     case CFG_S: return &launch_gemm<DT, EP, 64, 64, 32, 32>;
     case CFG_M: return &launch_gemm<DT, EP, 128, 128, 64, 64>;
     case CFG_L:
-      if constexpr (DT != F32) return &launch_gemm<DT, EP, 256, 256, 128, 128>;
+      if constexpr (DT != F32) return &launch_gemm<DT, EP, 256, 256, 128, 64>;
       return nullptr;
     default: return nullptr;
   }
