@@ -24,6 +24,56 @@ if ROOT not in sys.path:
 
 PEAK_F16_TFLOPS = 2516.6        # 256 CU x 2.4 GHz x 4096 FLOP/clk/CU, dense fp16/bf16 MFMA
 PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_ffn_f16_4096x11008x4096.txt")
+COPY_PROBE_BYTES = 1 << 30
+
+
+def kernel_source_hash() -> str:
+    """SHA-256 over the HIP sources: HBM-traffic counters taken for one version of the
+    kernels are reported only while the sources are unchanged."""
+    import hashlib
+    csrc = os.path.join(ROOT, "gemm_epilogues_epilog_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp")):
+            h.update(name.encode())
+            h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel_desc: str):
+    """HBM bytes per launch of the headline kernel from the committed counter summary
+    (FETCH_SIZE and WRITE_SIZE scaled by the copy-kernel calibration), or None when the
+    summary is missing or was taken on other kernel sources or another configuration."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith(("#", " ", "|")):
+            key, val = line.split(":", 1)
+            kv[key.strip()] = val.strip()
+    if kv.get("kernel_source_sha") != kernel_source_hash() or kv.get("kernel") != kernel_desc:
+        return None
+    try:
+        return int(float(kv["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_probe(repeats: int = 5):
+    """A plain device-to-device copy of COPY_PROBE_BYTES, run `repeats` times: the
+    calibration kernel for the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = COPY_PROBE_BYTES // 4
+    src = torch.arange(n, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(repeats):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    assert torch.equal(dst[-16:], src[-16:])
+    print(json.dumps({"copy_probe_bytes_read": COPY_PROBE_BYTES, "copy_probe_bytes_written": COPY_PROBE_BYTES,
+                      "repeats": repeats}), flush=True)
 
 
 def log(*a):
@@ -45,14 +95,20 @@ def device_inputs(W, device_rng: bool):
     return A, B, bias
 
 
-def time_execute(ge, handle, args, steps, warmup):
-    """Warm up, then time `steps` executes: host wall clock bracketed by
-    synchronisations, and one HIP event pair per execute on the launch stream."""
+def time_execute(ge, handle, args, steps, warmup, warm_s=0.0):
+    """Warm up (`warmup` executes, continued until `warm_s` seconds have passed), then
+    time `steps` executes: host wall clock bracketed by synchronisations, and one HIP
+    event pair per execute on the launch stream."""
     import torch
     stream = torch.cuda.current_stream()
     sptr = stream.cuda_stream
-    for _ in range(warmup):
+    t_warm = time.perf_counter()
+    done = 0
+    while done < warmup or time.perf_counter() - t_warm < warm_s:
         ge.gemm_epilog_execute(handle, *args, stream=sptr)
+        done += 1
+        if done % 50 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = time.perf_counter()
@@ -87,7 +143,7 @@ def run_variant(ge, W, epilog, dtype, steps, warmup, device_rng, backward=False)
         torch.cuda.synchronize()
         ge.gemm_epilog_free(hf)
         bias = None
-    r = time_execute(ge, h, (A, B, bias, D, aux, bg), steps, warmup)
+    r = time_execute(ge, h, (A, B, bias, D, aux, bg), steps, warmup, warm_s=0.3)
     desc = ge.gemm_epilog_describe(h)
     ge.gemm_epilog_free(h)
     t = r["event_ms_median"] * 1e-3
@@ -100,7 +156,8 @@ def run_variant(ge, W, epilog, dtype, steps, warmup, device_rng, backward=False)
 
 
 def cpu_baseline(W, budget_s: float):
-    """The CPU oracle on whole 256-row slabs of W until ~budget_s seconds of work."""
+    """The CPU oracle on the whole headline workload, repeated until about budget_s
+    seconds have passed (at least one full pass); inputs are drawn before timing."""
     import numpy as np
     import torch
     import oracle
@@ -108,32 +165,31 @@ def cpu_baseline(W, budget_s: float):
     def to_np(t):
         return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
 
-    B = to_np(W.b())
-    bias = to_np(W.bias())
-    threads = oracle.default_threads()
-    rows = 0
-    flops = 0
+    a, b, bias = to_np(W.a()), to_np(W.b()), to_np(W.bias())
+    threads = min(oracle.default_threads(), (W.m + 31) // 32)   # the oracle splits 32-row groups
+    passes = 0
     t0 = time.perf_counter()
-    while rows < W.m and time.perf_counter() - t0 < budget_s:
-        r1 = min(W.m, rows + 256)
-        a = to_np(W.a(rows, r1))
-        oracle.gemm_epilog(a, B, W.epilog, bias=bias[rows:r1], ab=W.dtype)
-        flops += 2 * (r1 - rows) * W.n * W.k
-        rows = r1
+    while passes == 0 or time.perf_counter() - t0 < budget_s:
+        oracle.gemm_epilog(a, b, W.epilog, bias=bias, ab=W.dtype, nthreads=threads)
+        passes += 1
     dt = time.perf_counter() - t0
-    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"rows 0..{rows} of {W.m} ({rows * W.n * W.k * 2 / 1e9:.1f} GFLOP of {W.name} "
-                      f"{W.epilog}), {dt:.1f} s, input slabs regenerated per 256 rows inside the timing"}
+    return {"value": round(passes * W.flops() / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{passes} full pass(es) of {W.name} {W.epilog} ({W.flops() / 1e9:.1f} GFLOP each) "
+                      f"in {dt:.1f} s, {threads} threads, inputs drawn before timing"}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=1000,
+                    help="untimed executes first; ~0.3 s lets the clock settle under load")
     ap.add_argument("--no-variants", action="store_true", help="time only the headline kernel")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
-    ap.add_argument("--traffic", default=None, help="JSON file with measured HBM bytes per launch")
+    ap.add_argument("--skip-cpu", action="store_true", help="leave out the cpu_baseline leg (profiling runs)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run the 1 GiB copy that calibrates the HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -146,6 +202,9 @@ def main():
 
     ge.load()
     torch.cuda.set_device(0)
+    if args.copy_probe:
+        copy_probe()
+        return
     prop = torch.cuda.get_device_properties(0)
     W = inputs.WORKLOADS[inputs.HEADLINE]
     log(f"[bench] device {prop.name} {getattr(prop, 'gcnArchName', '')} CUs {prop.multi_processor_count}")
@@ -164,15 +223,11 @@ def main():
     achieved = flops / (r["event_ms_mean"] * 1e-3) / 1e12
     log(f"[bench] headline: {r}")
 
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        tr = json.load(open(args.traffic))
-        if tr.get("kernel") == kernel_desc:
-            traffic = tr.get("bytes_per_launch")
+    traffic = read_traffic(kernel_desc)
 
     variants = {}
     if not args.no_variants:
-        vsteps, vwarm = max(5, args.steps // 2), max(2, args.warmup // 2)
+        vsteps, vwarm = max(5, args.steps // 4), 5
         plan = [
             ("ffn_unfused_f16", inputs.HEADLINE, "RELU_BIAS_UNFUSED", "f16", False),
             ("ffn_aux_f16", inputs.HEADLINE, "RELU_AUX_BIAS", "f16", False),
@@ -196,7 +251,7 @@ def main():
     del A, B, D
     torch.cuda.empty_cache()
     log("[bench] cpu baseline (oracle)")
-    cpu = cpu_baseline(W, args.cpu_budget)
+    cpu = None if args.skip_cpu else cpu_baseline(W, args.cpu_budget)
     log(f"[bench] cpu: {cpu}")
 
     out = {

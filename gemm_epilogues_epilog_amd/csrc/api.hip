@@ -73,13 +73,12 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Pick the largest tile that still gives every compute unit at least one tile;
-// fall back to the small tile for small problems.
+// fall back to the smaller register-staged tiles for small problems.
 int choose_cfg(int64_t m, int n, ge_dtype_t ab, int cus) {
   const char* env = std::getenv("GE_TILE");
   if (env && env[0]) {
-    if (env[0] == 'S') return gek::CFG_S;
-    if (env[0] == 'M') return gek::CFG_M;
-    if (env[0] == 'L' && ab != GE_F32) return gek::CFG_L;
+    for (int c = 0; c < gek::CFG_COUNT; ++c)
+      if (std::strcmp(env, gek::kTiles[c].name) == 0 && (ab != GE_F32 || !gek::cfg_is_dtl(c))) return c;
   }
   auto tiles = [&](int c) { return cdiv(m, gek::kTiles[c].bm) * cdiv(n, gek::kTiles[c].bn); };
   if (ab != GE_F32 && tiles(gek::CFG_L) >= cus) return gek::CFG_L;
@@ -182,7 +181,9 @@ ge_status_t gemm_epilog_plan(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt, ge
   }
   h->desc = std::string(dt_name(dt.ab)) + " " + ep_name(ep) + " tile " + std::to_string(tc.bm) + "x" +
             std::to_string(tc.bn) + " waves " + std::to_string(tc.bm / tc.wm) + "x" +
-            std::to_string(tc.bn / tc.wn) + " grid " + std::to_string(h->tiles_m * h->tiles_n);
+            std::to_string(tc.bn / tc.wn) + (gek::cfg_is_dtl(h->cfg) ? " bk " + std::to_string(tc.bk) + " stages " +
+                                                 std::to_string(tc.stages) + " " + tc.loop : std::string()) +
+            " grid " + std::to_string(h->tiles_m * h->tiles_n);
   *out = h;
   return GE_OK;
 }

@@ -1,10 +1,10 @@
 // Fused kernel for fp16 / bf16 with direct-to-LDS operand copies (gfx950).
 //
-// Per k-tile (64 values of k) every wave issues buffer loads that write straight
-// into LDS (no register staging, no VALU work on the copy path):
-//   A tile: BM rows of 128 bytes (row = m, k contiguous), the eight 16-byte chunks
-//           of each row XOR-swizzled by swz_a(row).
-//   B tile: 64 rows of 2 BN bytes (row = k, n contiguous, as B is stored), the
+// Operands. Per k-tile (BK values of k) every wave issues buffer loads that write
+// straight into LDS (no register staging, no VALU work on the copy path):
+//   A tile: BM rows of 2 BK bytes (row = m, k contiguous), the 16-byte chunks of
+//           each row XOR-swizzled by swz_a(row).
+//   B tile: BK rows of 2 BN bytes (row = k, n contiguous, as B is stored), the
 //           16-byte chunks XOR-swizzled by swz_b(row).
 // Fragments: A with ds_read_b128 (8 consecutive k of one row), B with two
 // ds_read_b64_tr_b16 per fragment. In each 16-lane group of that instruction lane j
@@ -13,27 +13,21 @@
 // lane j therefore holds column j at rows k0 .. k0+3, which is the MFMA operand
 // layout (k contiguous per lane) produced from the n-contiguous tile.
 //
-// Both LDS stages are filled one k-tile ahead; one barrier per k-tile separates
-// "everyone finished reading stage s" from "stage s is refilled". Fragment
-// registers are double-buffered so the reads of k-step s+1 overlap the MFMAs of
-// k-step s.
+// Pipeline. STAGES LDS stages form a ring. The copies are inline assembly, ordered
+// by hand with vmcnt / lgkmcnt waits and workgroup barriers (the two main loops
+// below describe their schedules): the compiler would otherwise make every LDS read
+// wait for every copy still in flight.
+//
+// Epilogue. After the last k-tile the stage memory becomes per-wave scratch: each
+// wave writes its finished (activated, rounded) WM x WN tile there with a swizzle
+// that keeps the 8-byte writes conflict-free, reads it back as 16-byte row pieces
+// and stores whole 2 WN-byte row segments of D, so every store instruction covers
+// full cache lines instead of 32 rows x 16 bytes.
 #pragma once
 
 #include "kernels.hpp"
 
 namespace gek {
-
-// 16-byte chunk swizzles. A rows are 128 bytes (8 chunks): rows r .. r+15 read at
-// the same logical chunk hit 16 distinct 16-byte bank groups whether the LDS
-// serves 8 or 16 lanes of a ds_read_b128 per cycle. Depends on row % 16 only.
-__device__ __forceinline__ int swz_a(int row) { return (row & 7) ^ ((row >> 3) & 1); }
-// B rows are 2 BN bytes. A transposed read touches rows k0 .. k0+3 (k0 % 4 == 0) at
-// the same 32 columns; XOR with g in {0, 6, 10, 12} puts those rows in distinct
-// 32-byte and 64-byte bank groups.
-__device__ __forceinline__ int swz_b(int row) {
-  const int u = row & 3;
-  return u == 0 ? 0 : u == 1 ? 6 : u == 2 ? 10 : 12;
-}
 
 typedef short s16x4 __attribute__((__vector_size__(4 * sizeof(short))));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -44,107 +38,316 @@ __device__ __forceinline__ i32x2 ds_read_tr(const char* p) {
   return __builtin_bit_cast(i32x2, v);
 }
 
-template <int DT, int EP, int BM, int BN, int WM, int WN>
+// 16-byte chunk swizzle of A rows. A ds_read_b128 is served 16 lanes (256 bytes) at
+// a time; lanes 0-15 read rows r .. r+15 (r % 16 == 0) at one logical chunk, which
+// must land in 16 distinct 16-byte bank groups.
+//   128-byte rows (8 chunks): bank group = 8 (row % 2) + chunk; XOR with a value
+//     that differs across the 8 rows of equal parity.
+//   64-byte rows (4 chunks): bank group = 4 (row % 4) + chunk; XOR with row / 4.
+template <int ROWB>
+__device__ __forceinline__ int swz_a(int row) {
+  static_assert(ROWB == 64 || ROWB == 128, "A row bytes");
+  if constexpr (ROWB == 128) return (row & 7) ^ ((row >> 3) & 1);
+  else return (row >> 2) & 3;
+}
+// B rows are 2 BN bytes. A transposed read touches rows k0 .. k0+3 (k0 % 4 == 0) at
+// the same 32 columns; XOR with g in {0, 6, 10, 12} puts those rows in distinct
+// 32-byte and 64-byte bank groups.
+__device__ __forceinline__ int swz_b(int row) {
+  const int u = row & 3;
+  return u == 0 ? 0 : u == 1 ? 6 : u == 2 ? 10 : 12;
+}
+
+template <int BM, int BN, int WM, int WN, int BK, int STAGES>
 struct DtlCfg {
   static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
   static constexpr int NW = WAVES_M * WAVES_N, NT = NW * 64;
   static constexpr int MB = WM / 32, NB = WN / 32;
-  static constexpr int BK = 64;                          // k per tile (128 bytes of fp16/bf16)
-  static constexpr int A_BYTES = BM * kRowBytes;
-  static constexpr int B_ROWB = BN * 2;                  // bytes per B row in LDS
+  static constexpr int KSTEPS = BK / 16;                  // MFMA k-steps per tile
+  static constexpr int A_ROWB = BK * 2;                   // bytes per A row in LDS
+  static constexpr int A_BYTES = BM * A_ROWB;
+  static constexpr int A_CHUNKS = A_ROWB / 16;
+  static constexpr int A_RPI = 1024 / A_ROWB;             // A rows per copy instruction
+  static constexpr int B_ROWB = BN * 2;                   // bytes per B row in LDS
   static constexpr int B_BYTES = BK * B_ROWB;
+  static constexpr int B_CHUNKS = B_ROWB / 16;
+  static constexpr int B_RPI = 1024 / B_ROWB;
   static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int A_INST = A_BYTES / 1024 / NW;     // 1 KB direct-to-LDS copies per wave
+  static constexpr int A_INST = A_BYTES / 1024 / NW;      // 1 KB copies per wave per tile
   static constexpr int B_INST = B_BYTES / 1024 / NW;
-  static constexpr int B_CHUNKS = B_ROWB / 16;           // 16-byte chunks per B row
-  static constexpr int B_RPI = 1024 / B_ROWB;            // B rows per copy instruction
-  static_assert(DT == F16 || DT == BF16, "16-bit types only");
+  static constexpr int INST = A_INST + B_INST;
+  static constexpr int SCRATCH = WM * WN * 2;             // epilogue bytes per wave
+  static constexpr int LDS = STAGES * STAGE;
+  static_assert(BK == 32 || BK == 64, "k-tile");
   static_assert(BN >= 128 && BN % 64 == 0, "B rows must hold at least 16 chunks");
   static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "copy split");
-  static_assert(2 * STAGE <= 160 * 1024, "LDS");
+  static_assert(STAGES >= 2 && LDS <= 160 * 1024, "LDS");
+  static_assert(NW * SCRATCH <= LDS, "epilogue scratch");
+  static_assert((STAGES - 2) * INST < 64, "vmcnt range");
 };
 
-template <int DT, int EP, int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_dtl_kernel(Args p) {
-  using C = DtlCfg<DT, EP, BM, BN, WM, WN>;
+// s_waitcnt vmcnt(n * INST) for a run-time n in [0, MAXN] (larger n waits for MAXN).
+template <int INST, int MAXN>
+__device__ __forceinline__ void wait_tiles(int n) {
+  if constexpr (MAXN <= 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (n >= MAXN) wait_vmcnt<MAXN * INST>();
+    else wait_tiles<INST, MAXN - 1>(n);
+  }
+}
+
+// ---- epilogue through LDS ------------------------------------------------------
+// The accumulators (lane l: row 32 b + l % 32 of the wave tile, columns
+// 32 a + 8 (r / 4) + 4 (l / 32) + r % 4) are finished in registers and written to
+// the wave's scratch as 8-byte units: unit p of row `row` goes to unit
+// p ^ swz(row), where swz spreads the 32 rows written by one half-wave over all 32
+// 8-byte bank slots. Read-back takes 16 bytes (units 2c, 2c+1 -> stored at the
+// aligned pair 2 (c ^ (s >> 1)), in swapped order when s is odd).
+template <int WN>
+struct EpiLayout {
+  static constexpr int RB = WN * 2;          // scratch row bytes
+  static constexpr int U = RB / 8;           // 8-byte units per row
+  static constexpr int LPR = RB / 16;        // lanes per row on read-back
+  static constexpr int RPI = 64 / LPR;       // rows per read-back instruction
+  static_assert(U == 16 || U == 32, "scratch row");
+  __device__ static __forceinline__ int swz(int row) { return U == 16 ? ((row >> 1) & 15) : (row & 31); }
+};
+
+template <int DT, int EP, int MB, int NB, int WN>
+__device__ __forceinline__ void epilogue_lds(const Args& p, f32x16 (&acc)[NB][MB], int64_t m0w, int n0w, int lane,
+                                             char* scratch) {
   using T = Tr<DT>;
-  constexpr int MB = C::MB, NB = C::NB;
-
-  // One LDS object per stage: the compiler then knows that copies in flight into
-  // one stage do not alias fragment reads of the other and waits only where needed.
-  __shared__ __attribute__((aligned(1024))) char stage0[C::STAGE];
-  __shared__ __attribute__((aligned(1024))) char stage1[C::STAGE];
-
+  using L = EpiLayout<WN>;
+  constexpr int WM = MB * 32;
   const int64_t M = p.m;
-  const int N = p.n, K = p.k;
-  int tm, tn;
-  tile_coords(p, tm, tn);
-  const int64_t m0 = (int64_t)tm * BM;
-  const int n0 = tn * BN;
-
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = w % C::WAVES_M, wn = w / C::WAVES_M;
+  const int N = p.n;
   const int lrow = lane & 31, lhi = lane >> 5;
 
-  // ---- copy plan: per-lane source offsets (tile-relative, constant over k) ----
+  // ---- phase 1: finish every accumulator and stage it in scratch ----
+  if constexpr (EP == DRELU_BGRAD) {
+    const uint32_t mybit = 1u << lrow;
+#pragma unroll
+    for (int b = 0; b < MB; ++b) {
+      const int row = 32 * b + lrow;
+      const int64_t mrow = m0w + row;
+      const int64_t grp = (m0w + 32 * b) >> 5;
+      const bool gok = grp * 32 < M;
+      const int s = L::swz(row);
+      float rowsum = 0.0f;
+#pragma unroll
+      for (int a = 0; a < NB; ++a) {
+        const int ncol = n0w + 32 * a + lrow;
+        uint32_t word = 0;
+        if (gok && ncol < N) word = p.aux[grp * N + ncol];
+        float dz[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int idx = 8 * (r >> 2) + (r & 3);
+          const uint32_t wl = __builtin_amdgcn_readlane(word, idx);
+          const uint32_t wh = __builtin_amdgcn_readlane(word, idx + 4);
+          const uint32_t wr = lhi ? wh : wl;
+          dz[r] = (wr & mybit) ? acc[a][b][r] : 0.0f;
+          rowsum += dz[r];
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int unit = (8 * a + 2 * g + lhi) ^ s;
+          const i32x2 v = {(int)T::pack2(dz[4 * g], dz[4 * g + 1]), (int)T::pack2(dz[4 * g + 2], dz[4 * g + 3])};
+          *reinterpret_cast<i32x2*>(scratch + row * L::RB + unit * 8) = v;
+        }
+      }
+      rowsum += __shfl_xor(rowsum, 32);
+      if (lhi == 0 && mrow < M && n0w < N) p.partial[(int64_t)(n0w / WN) * M + mrow] = rowsum;
+    }
+  } else {
+#pragma unroll
+    for (int b = 0; b < MB; ++b) {
+      const int row = 32 * b + lrow;
+      const int64_t mrow = m0w + row;
+      const bool mok = mrow < M;
+      const int s = L::swz(row);
+      float bv = 0.0f;
+      if constexpr (EP != NONE) {
+        if (mok) bv = load_vec(p.bias, p.vec_dt, mrow);
+      }
+#pragma unroll
+      for (int a = 0; a < NB; ++a) {
+        float pre[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pre[r] = acc[a][b][r] + bv;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          float y[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] = activate<EP>(pre[4 * g + e]);
+          const int unit = (8 * a + 2 * g + lhi) ^ s;
+          const i32x2 v = {(int)T::pack2(y[0], y[1]), (int)T::pack2(y[2], y[3])};
+          *reinterpret_cast<i32x2*>(scratch + row * L::RB + unit * 8) = v;
+        }
+        if constexpr (EP == RELU_AUX_BIAS) {
+          // ballot r: bits 0-31 = rows of column 8(r/4) + r%4, bits 32-63 = column +4
+          uint32_t word = 0;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const uint64_t bal = __ballot(mok && pre[r] > 0.0f);
+            const int cl = 8 * (r >> 2) + (r & 3);
+            if (lane == cl) word = (uint32_t)bal;
+            if (lane == cl + 4) word = (uint32_t)(bal >> 32);
+          }
+          const int64_t grp = (m0w + 32 * b) >> 5;
+          const int ncol = n0w + 32 * a + lane;
+          if (lane < 32 && grp * 32 < M && ncol < N) p.aux[grp * N + ncol] = word;
+        }
+      }
+    }
+  }
+
+  // ---- phase 2: whole row segments from scratch to D ----
+  char* Dw = static_cast<char*>(p.D) + (m0w * (int64_t)N + n0w) * 2;
+  const __amdgpu_buffer_rsrc_t rd = rsrc(Dw);
+  const int c = lane % L::LPR;
+  const bool cok = n0w + 8 * c < N;
+#pragma unroll
+  for (int i = 0; i < WM / L::RPI; ++i) {
+    const int row = i * L::RPI + lane / L::LPR;
+    const int s = L::swz(row);
+    const i32x4 raw = *reinterpret_cast<const i32x4*>(scratch + row * L::RB + ((c ^ (s >> 1)) << 4));
+    const i32x4 v = (s & 1) ? i32x4{raw[2], raw[3], raw[0], raw[1]} : raw;
+    const bool ok = cok && (m0w + row < M);
+    const uint32_t off = ok ? (uint32_t)(((int64_t)row * N + 8 * c) * 2) : kOOB;
+    __builtin_amdgcn_raw_buffer_store_b128(v, rd, off, 0, 0);
+  }
+}
+
+// ---- operand copies and fragment reads shared by both main loops ---------------
+template <int DT, int BM, int BN, int WM, int WN, int BK, int STAGES>
+struct Operands {
+  using C = DtlCfg<BM, BN, WM, WN, BK, STAGES>;
+  static constexpr int MB = C::MB, NB = C::NB;
+  static constexpr int A_PART = C::A_INST / C::KSTEPS, B_PART = C::B_INST / C::KSTEPS;
+
+  const char* Abase;
+  const char* Bbase;
+  int N, K, w;
+  uint32_t lds_base;
   uint32_t a_src[C::A_INST];
   int a_chunk[C::A_INST];
-#pragma unroll
-  for (int j = 0; j < C::A_INST; ++j) {
-    const int row = (w * C::A_INST + j) * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ swz_a(row);
-    a_chunk[j] = c;
-    a_src[j] = (m0 + row < M) ? (uint32_t)(row * K * 2 + c * 16) : kOOB;
-  }
   uint32_t b_src[C::B_INST];
   int b_row[C::B_INST];
-#pragma unroll
-  for (int j = 0; j < C::B_INST; ++j) {
-    const int row = (w * C::B_INST + j) * C::B_RPI + lane / C::B_CHUNKS;
-    const int c = (lane % C::B_CHUNKS) ^ swz_b(row);
-    b_row[j] = row;
-    b_src[j] = (n0 + c * 8 < N) ? (uint32_t)(row * N * 2 + c * 16) : kOOB;
-  }
+  int a_rd[C::KSTEPS];
+  int b_rd[NB];
 
-  const char* Abase = static_cast<const char*>(p.A) + m0 * (int64_t)K * 2;
-  const char* Bbase = static_cast<const char*>(p.B) + (int64_t)n0 * 2;
-  const int KT = (K + C::BK - 1) / C::BK;
-
-  auto issue_copies = [&](int kt, char* st) {
-    const int k0 = kt * C::BK;
-    const __amdgpu_buffer_rsrc_t ra = rsrc(Abase + (int64_t)k0 * 2);
-    const __amdgpu_buffer_rsrc_t rb = rsrc(Bbase + (int64_t)k0 * N * 2);
-    char* sA = st;
-    char* sB = sA + C::A_BYTES;
-    const bool tail = k0 + C::BK > K;
+  __device__ __forceinline__ Operands(const Args& p, int64_t m0, int n0, int w_, int wm, int wn, int lane,
+                                      uint32_t lds) {
+    const int64_t M = p.m;
+    N = p.n;
+    K = p.k;
+    w = w_;
+    lds_base = lds;
+    Abase = static_cast<const char*>(p.A) + m0 * (int64_t)K * 2;
+    Bbase = static_cast<const char*>(p.B) + (int64_t)n0 * 2;
+    // copy plan: per-lane source offsets (tile-relative, constant over k)
 #pragma unroll
     for (int j = 0; j < C::A_INST; ++j) {
-      const uint32_t off = (tail && k0 + a_chunk[j] * 8 >= K) ? kOOB : a_src[j];
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(sA + (w * C::A_INST + j) * 1024), 16, off, 0, 0, 0);
+      const int row = (w * C::A_INST + j) * C::A_RPI + lane / C::A_CHUNKS;
+      const int c = (lane % C::A_CHUNKS) ^ swz_a<C::A_ROWB>(row);
+      a_chunk[j] = c;
+      a_src[j] = (m0 + row < M) ? (uint32_t)(row * K * 2 + c * 16) : kOOB;
     }
 #pragma unroll
     for (int j = 0; j < C::B_INST; ++j) {
-      const uint32_t off = (tail && k0 + b_row[j] >= K) ? kOOB : b_src[j];
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(sB + (w * C::B_INST + j) * 1024), 16, off, 0, 0, 0);
+      const int row = (w * C::B_INST + j) * C::B_RPI + lane / C::B_CHUNKS;
+      const int c = (lane % C::B_CHUNKS) ^ swz_b(row);
+      b_row[j] = row;
+      b_src[j] = (n0 + c * 8 < N) ? (uint32_t)(row * N * 2 + c * 16) : kOOB;
     }
-  };
-
-  // ---- fragment read addresses (stage-relative) -----------------------------
-  int a_rd[4];
+    // fragment read addresses (stage-relative)
+    const int lrow = lane & 31, lhi = lane >> 5;
 #pragma unroll
-  for (int s = 0; s < 4; ++s)
-    a_rd[s] = (wm * WM + lrow) * kRowBytes + (((2 * s + lhi) ^ swz_a(lrow)) << 4);
-  int b_rd[NB];
-  {
+    for (int s = 0; s < C::KSTEPS; ++s)
+      a_rd[s] = (wm * WM + lrow) * C::A_ROWB + (((2 * s + lhi) ^ swz_a<C::A_ROWB>(lrow)) << 4);
     const int g = lane >> 4, i = lane & 15;
-    const int row = 8 * lhi + (i >> 2);              // + 16 s + 4 t
+    const int row = 8 * lhi + (i >> 2);   // + 16 s (+ 4 for the second read)
 #pragma unroll
     for (int a = 0; a < NB; ++a) {
       const int n = wn * WN + a * 32 + 16 * (g & 1) + 4 * (i & 3);
       b_rd[a] = C::A_BYTES + row * C::B_ROWB + (((n >> 3) ^ swz_b(row)) << 4) + ((n & 7) << 1);
     }
   }
+
+  // Copies of part `part` (of KSTEPS) of k-tile kt into LDS stage `stage`.
+  __device__ __forceinline__ void issue_part(int kt, int stage, int part) const {
+    const int k0 = kt * BK;
+    const i32x4 ra = make_srd(Abase + (int64_t)k0 * 2);
+    const i32x4 rb = make_srd(Bbase + (int64_t)k0 * N * 2);
+    const uint32_t sA = lds_base + stage * C::STAGE;
+    const uint32_t sB = sA + C::A_BYTES;
+    const bool tail = k0 + BK > K;
+#pragma unroll
+    for (int q = 0; q < A_PART; ++q) {
+      const int j = part * A_PART + q;
+      const uint32_t off = (tail && k0 + a_chunk[j] * 8 >= K) ? kOOB : a_src[j];
+      copy_to_lds_b128(ra, off, sA + (w * C::A_INST + j) * 1024);
+    }
+#pragma unroll
+    for (int q = 0; q < B_PART; ++q) {
+      const int j = part * B_PART + q;
+      const uint32_t off = (tail && k0 + b_row[j] >= K) ? kOOB : b_src[j];
+      copy_to_lds_b128(rb, off, sB + (w * C::B_INST + j) * 1024);
+    }
+  }
+  __device__ __forceinline__ void issue_tile(int kt, int stage) const {
+#pragma unroll
+    for (int part = 0; part < C::KSTEPS; ++part) issue_part(kt, stage, part);
+  }
+
+  // Fragments of k-step s from the stage at `base`.
+  __device__ __forceinline__ void read_step(const char* base, int s, i32x4 (&fa)[MB], i32x4 (&fb)[NB]) const {
+#pragma unroll
+    for (int b = 0; b < MB; ++b) fa[b] = *reinterpret_cast<const i32x4*>(base + a_rd[s] + b * 32 * C::A_ROWB);
+#pragma unroll
+    for (int a = 0; a < NB; ++a) {
+      const char* q = base + b_rd[a] + 16 * s * C::B_ROWB;
+      const i32x2 lo = ds_read_tr(q);
+      const i32x2 hi = ds_read_tr(q + 4 * C::B_ROWB);
+      fb[a] = i32x4{lo[0], lo[1], hi[0], hi[1]};
+    }
+  }
+};
+
+template <int DT, int MB, int NB>
+__device__ __forceinline__ void mma_step(f32x16 (&acc)[NB][MB], const i32x4 (&fa)[MB], const i32x4 (&fb)[NB]) {
+#pragma unroll
+  for (int a = 0; a < NB; ++a)
+#pragma unroll
+    for (int b = 0; b < MB; ++b) acc[a][b] = Tr<DT>::mma(fb[a], fa[b], acc[a][b]);
+}
+
+// ---- lockstep main loop --------------------------------------------------------
+// All waves run the same schedule. At the end of k-tile t every wave waits until
+// its own copies of tile t+1 have landed and its reads of tile t are done, one
+// barrier publishes tile t+1 and releases stage t % STAGES, and the copies of tile
+// t + STAGES go to that stage at once.
+template <int DT, int EP, int BM, int BN, int WM, int WN, int BK, int STAGES>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_dtl_kernel(Args p) {
+  using C = DtlCfg<BM, BN, WM, WN, BK, STAGES>;
+  using O = Operands<DT, BM, BN, WM, WN, BK, STAGES>;
+  static_assert(DT == F16 || DT == BF16, "16-bit types only");
+  static_assert(C::KSTEPS % 2 == 0, "every tile starts on fragment buffer 0");
+  constexpr int MB = C::MB, NB = C::NB;
+
+  __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
+
+  int tm, tn;
+  tile_coords(p, tm, tn);
+  const int64_t m0 = (int64_t)tm * BM;
+  const int n0 = tn * BN;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = w % C::WAVES_M, wn = w / C::WAVES_M;
+  const O op(p, m0, n0, w, wm, wn, lane, (uint32_t)(uintptr_t)(lds_void*)smem);
+  const int KT = (p.k + BK - 1) / BK;
 
   f32x16 acc[NB][MB];
 #pragma unroll
@@ -153,60 +356,135 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_dtl_kernel
     for (int b = 0; b < MB; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
-
   i32x4 fa[2][MB];
   i32x4 fb[2][NB];
-  auto read_frags = [&](const char* base, int s, int buf) {
-#pragma unroll
-    for (int b = 0; b < MB; ++b) fa[buf][b] = *reinterpret_cast<const i32x4*>(base + a_rd[s] + b * 32 * kRowBytes);
-#pragma unroll
-    for (int a = 0; a < NB; ++a) {
-      const char* q = base + b_rd[a] + 16 * s * C::B_ROWB;
-      const i32x2 lo = ds_read_tr(q);
-      const i32x2 hi = ds_read_tr(q + 4 * C::B_ROWB);
-      fb[buf][a] = i32x4{lo[0], lo[1], hi[0], hi[1]};
-    }
-  };
 
-  // ---- prologue: tiles 0 and 1 in flight, tile 0 complete -------------------
-  issue_copies(0, stage0);
-  if (KT > 1) issue_copies(1, stage1);
-  if (KT > 1) {
-    wait_vmcnt<C::A_INST + C::B_INST>();   // tile 0 landed, tile 1 may be in flight
-  } else {
-    wait_vmcnt<0>();
-  }
-  __syncthreads();
-  read_frags(stage0, 0, 0);
-
-  // One k-tile on stage `cur` (the other stage holds or receives tile kt+1).
-  auto tile = [&](int kt, char* cur, char* nxt) {
+  // prologue: every stage filled, tile 0 complete
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+  for (int t = 0; t < STAGES; ++t)
+    if (t < KT) op.issue_tile(t, t);
+  wait_tiles<C::INST, STAGES - 1>(min(STAGES - 1, KT - 1));
+  barrier_only();
+  op.read_step(smem, 0, fa[0], fb[0]);
+
+  auto tile = [&](int kt, int u) {
+    const char* cur = smem + u * C::STAGE;
+    const char* nxt = smem + ((u + 1) % STAGES) * C::STAGE;
+#pragma unroll
+    for (int s = 0; s < C::KSTEPS; ++s) {
       const int buf = s & 1;
-      if (s < 3) {
-        read_frags(cur, s + 1, buf ^ 1);
+      if (s < C::KSTEPS - 1) {
+        op.read_step(cur, s + 1, fa[buf ^ 1], fb[buf ^ 1]);
       } else {
-        // step 3 is in registers: once every wave is here, `cur` may be refilled;
-        // the barrier's wait also makes tile kt+1 (in `nxt`) complete
-        __syncthreads();
-        if (kt + 2 < KT) issue_copies(kt + 2, cur);
-        if (kt + 1 < KT) read_frags(nxt, 0, 0);
+        // the last step is in registers: publish tile kt+1 and release stage u
+        wait_lgkmcnt<0>();                                               // reads of stage u done
+        wait_tiles<C::INST, STAGES - 2>(min(STAGES - 2, KT - 2 - kt));   // tile kt+1 landed
+        barrier_only();
+        if (kt + STAGES < KT) op.issue_tile(kt + STAGES, u);
+        if (kt + 1 < KT) op.read_step(nxt, 0, fa[0], fb[0]);
       }
-#pragma unroll
-      for (int a = 0; a < NB; ++a)
-#pragma unroll
-        for (int b = 0; b < MB; ++b) acc[a][b] = T::mma(fb[buf][a], fa[buf][b], acc[a][b]);
+      mma_step<DT, MB, NB>(acc, fa[buf], fb[buf]);
       // keep each k-step's reads next to its MFMAs (no hoisting across steps)
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  for (int kt = 0; kt < KT; kt += 2) {
-    tile(kt, stage0, stage1);
-    if (kt + 1 < KT) tile(kt + 1, stage1, stage0);
+  for (int kt = 0; kt < KT; kt += STAGES) {
+#pragma unroll
+    for (int u = 0; u < STAGES; ++u)
+      if (kt + u < KT) tile(kt + u, u);
   }
 
-  epilogue<DT, EP, MB, NB, WN>(p, acc, m0 + wm * WM, n0 + wn * WN, lane);
+  // every wave is done with the stages: reuse them as per-wave epilogue scratch
+  wait_lgkmcnt<0>();
+  barrier_only();
+  epilogue_lds<DT, EP, MB, NB, WN>(p, acc, m0 + wm * WM, n0 + wn * WN, lane, smem + w * C::SCRATCH);
+}
+
+// ---- ping-pong main loop -------------------------------------------------------
+// The workgroup's waves form two groups, G0 = waves 0 .. NW/2-1 and G1 = the rest;
+// waves are dealt to the four SIMDs in order, so every SIMD runs one wave of each
+// group. The groups alternate between a memory phase M(t) (read all fragments of
+// k-tile t into registers, issue this wave's copies of tile t + STAGES - 1, wait for
+// the reads) and a compute phase C(t) (all MFMAs of tile t back to back), offset by
+// one phase, with one workgroup barrier between phases:
+//
+//   phase   0      1      2      3      4     ...
+//   G0     M(0)   C(0)   M(1)   C(1)   M(2)
+//   G1      -     M(0)   C(0)   M(1)   C(1)
+//
+// so in every phase one wave per SIMD issues MFMAs while the other issues LDS reads
+// and copies. Tile t lives in stage t % STAGES; G1 reads it last, in phase 2t+1, so
+// from phase 2t+2 its stage may be refilled with tile t + STAGES, whose copies are
+// issued in M(t+1) of both groups and must have landed at the barrier that opens
+// phase 2(t + STAGES).
+template <int DT, int EP, int BM, int BN, int WM, int WN, int BK, int STAGES>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_pp_kernel(Args p) {
+  using C = DtlCfg<BM, BN, WM, WN, BK, STAGES>;
+  using O = Operands<DT, BM, BN, WM, WN, BK, STAGES>;
+  static_assert(DT == F16 || DT == BF16, "16-bit types only");
+  static_assert(C::NW == 8, "two groups of one wave per SIMD");
+  static_assert(STAGES >= 3, "copies of tile t + STAGES - 1 go out in M(t)");
+  constexpr int MB = C::MB, NB = C::NB, KS = C::KSTEPS;
+
+  __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
+
+  int tm, tn;
+  tile_coords(p, tm, tn);
+  const int64_t m0 = (int64_t)tm * BM;
+  const int n0 = tn * BN;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = w % C::WAVES_M, wn = w / C::WAVES_M;
+  const bool g1 = w >= C::NW / 2;
+  const O op(p, m0, n0, w, wm, wn, lane, (uint32_t)(uintptr_t)(lds_void*)smem);
+  const int KT = (p.k + BK - 1) / BK;
+
+  f32x16 acc[NB][MB];
+#pragma unroll
+  for (int a = 0; a < NB; ++a)
+#pragma unroll
+    for (int b = 0; b < MB; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+  i32x4 fa[KS][MB];
+  i32x4 fb[KS][NB];
+
+  // prologue: tiles 0 .. STAGES-2 in flight; tile 0 published by the first barrier
+#pragma unroll
+  for (int t = 0; t < STAGES - 1; ++t)
+    if (t < KT) op.issue_tile(t, t);
+  wait_tiles<C::INST, STAGES - 2>(min(STAGES - 2, KT - 1));
+  barrier_only();
+  if (g1) barrier_only();   // G1 sits out phase 0
+
+  // Before the barrier that opens phase 2(t+1), every wave has issued the copies of
+  // tiles up to t + STAGES - 1 (G0 in M(t), G1 in M(t)); tile t+1 must have landed,
+  // so the copies of tiles t+2 .. t+STAGES-1 may still be in flight.
+  auto wait_tile_after = [&](int t) {
+    wait_tiles<C::INST, STAGES - 2>(min(STAGES - 2, KT - 2 - t));
+  };
+
+  for (int t = 0; t < KT; ++t) {
+    const char* cur = smem + (t % STAGES) * C::STAGE;
+    // ---- M(t) ----
+#pragma unroll
+    for (int s = 0; s < KS; ++s) op.read_step(cur, s, fa[s], fb[s]);
+    if (t + STAGES - 1 < KT) op.issue_tile(t + STAGES - 1, (t + STAGES - 1) % STAGES);
+    wait_lgkmcnt<0>();
+    if (g1) wait_tile_after(t);   // G1's M(t) ends right before phase 2(t+1)
+    barrier_only();
+    // ---- C(t) ----
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) mma_step<DT, MB, NB>(acc, fa[s], fb[s]);
+    __builtin_amdgcn_s_setprio(0);
+    if (!g1) wait_tile_after(t);  // G0's C(t) ends right before phase 2(t+1)
+    barrier_only();
+  }
+  if (!g1) barrier_only();   // G0 sits out the last phase (G1's final C)
+
+  // every wave is done with the stages: reuse them as per-wave epilogue scratch
+  epilogue_lds<DT, EP, MB, NB, WN>(p, acc, m0 + wm * WM, n0 + wn * WN, lane, smem + w * C::SCRATCH);
 }
 
 }  // namespace gek

@@ -76,6 +76,42 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// s_waitcnt lgkmcnt(N) with the other counters left alone.
+template <int N>
+__device__ __forceinline__ void wait_lgkmcnt() {
+  static_assert(N >= 0 && N < 16, "lgkmcnt range");
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (N << 8));
+}
+
+// Workgroup barrier that is also a compiler barrier for memory operations. It does
+// not wait for outstanding memory operations: callers wait explicitly first.
+__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
+
+// Buffer descriptor (V#) as four SGPR values: base, no stride, 2^31 - 1 bytes of
+// range, 32-bit data format. Offsets at or above kOOB are out of range.
+__device__ __forceinline__ i32x4 make_srd(const void* base) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+  r[2] = 0x7fffffff;
+  r[3] = kBufDword3;
+  return r;
+}
+
+// Direct global -> LDS copy of 16 bytes per lane: lane l reads srd.base + voff and
+// writes LDS bytes [lds + 16 l, lds + 16 l + 16). Out-of-range offsets write zeros.
+// Issued as inline assembly so that the compiler does not treat the copy as a write
+// that every later LDS read must wait for; the caller orders it with wait_vmcnt and
+// barrier_only. Loads complete in issue order, so the compiler's own vmcnt waits
+// stay correct with these extra loads in flight (they can only wait longer).
+__device__ __forceinline__ void copy_to_lds_b128(const i32x4& srd, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(srd), "s"(lds)
+               : "memory", "m0");
+}
+
 // Workgroup id -> (m-tile, n-tile). Workgroups are dealt to the 8 XCDs round-robin;
 // renumber them so each XCD walks a contiguous range of tiles, then walk tiles in
 // groups of group_m m-tiles (m fastest inside a group) so tiles that run together

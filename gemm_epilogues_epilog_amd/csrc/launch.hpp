@@ -9,48 +9,65 @@
 
 namespace gek {
 
-// Workgroup tile (BM x BN) and wave tile (WM x WN) of each configuration.
+// Workgroup tile (BM x BN), wave tile (WM x WN), k-tile and LDS stages of each
+// configuration. S and M use the register-staged kernel (any type); the L family
+// uses the direct-to-LDS kernel (16-bit types only).
 struct TileCfg {
-  int bm, bn, wm, wn;
+  int bm, bn, wm, wn, bk, stages;
   const char* name;
+  const char* loop;   // main loop of the direct-to-LDS kernels
 };
 
-enum CfgId { CFG_S = 0, CFG_M = 1, CFG_L = 2, CFG_COUNT = 3 };
+enum CfgId { CFG_S = 0, CFG_M = 1, CFG_L = 2, CFG_W4 = 3, CFG_P = 4, CFG_P5 = 5, CFG_COUNT = 6 };
 
 constexpr TileCfg kTiles[CFG_COUNT] = {
-    {64, 64, 32, 32, "S"},
-    {128, 128, 64, 64, "M"},
-    {256, 256, 128, 64, "L"},
+    {64, 64, 32, 32, 0, 2, "S", ""},
+    {128, 128, 64, 64, 0, 2, "M", ""},
+    {256, 256, 128, 64, 64, 2, "L", "lockstep"},     // 8 waves
+    {256, 256, 128, 128, 64, 2, "W4", "lockstep"},   // 4 waves of 128 x 128
+    {256, 256, 128, 64, 32, 4, "P", "ping-pong"},    // 8 waves in two groups
+    {256, 256, 128, 64, 32, 5, "P5", "ping-pong"},
 };
 
-inline int threads_of(const TileCfg& c) { return (c.bm / c.wm) * (c.bn / c.wn) * 64; }
+inline bool cfg_is_dtl(int c) { return c >= CFG_L; }
 
 using LaunchFn = hipError_t (*)(const Args&, int grid, hipStream_t);
 
-// 16-bit types with tiles of at least 128 columns use the direct-to-LDS kernel;
-// fp32 and the small tile use the register-staged kernel.
 template <int DT, int EP, int BM, int BN, int WM, int WN>
-hipError_t launch_gemm(const Args& a, int grid, hipStream_t s) {
+hipError_t launch_generic(const Args& a, int grid, hipStream_t s) {
+  Args copy = a;
+  void* params[] = {&copy};
+  const void* fn = reinterpret_cast<const void*>(&gemm_epilog_kernel<DT, EP, BM, BN, WM, WN>);
+  return hipLaunchKernel(fn, dim3(grid), dim3((BM / WM) * (BN / WN) * 64), params, 0, s);
+}
+
+template <int DT, int EP, int BM, int BN, int WM, int WN, int BK, int ST, bool PP>
+hipError_t launch_dtl(const Args& a, int grid, hipStream_t s) {
   Args copy = a;
   void* params[] = {&copy};
   const void* fn;
-  if constexpr (DT != F32 && BN >= 128)
-    fn = reinterpret_cast<const void*>(&gemm_dtl_kernel<DT, EP, BM, BN, WM, WN>);
-  else
-    fn = reinterpret_cast<const void*>(&gemm_epilog_kernel<DT, EP, BM, BN, WM, WN>);
+  if constexpr (PP) fn = reinterpret_cast<const void*>(&gemm_pp_kernel<DT, EP, BM, BN, WM, WN, BK, ST>);
+  else fn = reinterpret_cast<const void*>(&gemm_dtl_kernel<DT, EP, BM, BN, WM, WN, BK, ST>);
   return hipLaunchKernel(fn, dim3(grid), dim3((BM / WM) * (BN / WN) * 64), params, 0, s);
 }
 
 template <int DT, int EP>
 LaunchFn pick_cfg(int cfg) {
   switch (cfg) {
-    case CFG_S: return &launch_gemm<DT, EP, 64, 64, 32, 32>;
-    case CFG_M: return &launch_gemm<DT, EP, 128, 128, 64, 64>;
-    case CFG_L:
-      if constexpr (DT != F32) return &launch_gemm<DT, EP, 256, 256, 128, 64>;
-      return nullptr;
-    default: return nullptr;
+    case CFG_S: return &launch_generic<DT, EP, 64, 64, 32, 32>;
+    case CFG_M: return &launch_generic<DT, EP, 128, 128, 64, 64>;
+    default: break;
   }
+  if constexpr (DT != F32) {
+    switch (cfg) {
+      case CFG_L: return &launch_dtl<DT, EP, 256, 256, 128, 64, 64, 2, false>;
+      case CFG_W4: return &launch_dtl<DT, EP, 256, 256, 128, 128, 64, 2, false>;
+      case CFG_P: return &launch_dtl<DT, EP, 256, 256, 128, 64, 32, 4, true>;
+      case CFG_P5: return &launch_dtl<DT, EP, 256, 256, 128, 64, 32, 5, true>;
+      default: break;
+    }
+  }
+  return nullptr;
 }
 
 template <int DT>
