@@ -152,6 +152,10 @@ ge_status_t gemm_epilog_plan(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt, ge
   h->tiles_m = (int)cdiv(m, tc.bm);
   h->tiles_n = (int)cdiv(n, tc.bn);
   h->group_m = 8;
+  if (const char* g = std::getenv("GE_GROUP_M")) {
+    const int v = std::atoi(g);
+    if (v >= 1 && v <= 1024) h->group_m = v;
+  }
   const int kernel_ep = ep == GE_EPILOG_RELU_BIAS_UNFUSED ? (int)gek::NONE : (int)ep;
   h->gemm = lookup(dt.ab, kernel_ep, h->cfg);
   if (!h->gemm) {

@@ -25,6 +25,8 @@
 // full cache lines instead of 32 rows x 16 bytes.
 #pragma once
 
+#include <type_traits>
+
 #include "kernels.hpp"
 
 namespace gek {
@@ -297,6 +299,20 @@ struct Operands {
       copy_to_lds_b128(rb, off, sB + (w * C::B_INST + j) * 1024);
     }
   }
+  // Copy instruction j of k-tile kt, j in [0, INST): A instructions first, then B.
+  __device__ __forceinline__ void issue_one(int kt, int stage, int j) const {
+    const int k0 = kt * BK;
+    const bool tail = k0 + BK > K;
+    const uint32_t sA = lds_base + stage * C::STAGE;
+    if (j < C::A_INST) {
+      const uint32_t off = (tail && k0 + a_chunk[j] * 8 >= K) ? kOOB : a_src[j];
+      copy_to_lds_b128(make_srd(Abase + (int64_t)k0 * 2), off, sA + (w * C::A_INST + j) * 1024);
+    } else {
+      const int jb = j - C::A_INST;
+      const uint32_t off = (tail && k0 + b_row[jb] >= K) ? kOOB : b_src[jb];
+      copy_to_lds_b128(make_srd(Bbase + (int64_t)k0 * N * 2), off, sA + C::A_BYTES + (w * C::B_INST + jb) * 1024);
+    }
+  }
   __device__ __forceinline__ void issue_tile(int kt, int stage) const {
 #pragma unroll
     for (int part = 0; part < C::KSTEPS; ++part) issue_part(kt, stage, part);
@@ -316,6 +332,29 @@ struct Operands {
   }
 };
 
+// Fragments of one k-step read one instruction at a time, in the order the step's
+// MFMAs consume them: B0 (two transposed halves), A0 .. A(MB-1), then B1 .. B(NB-1).
+template <int MB, int NB>
+struct Frags {
+  static constexpr int PIECES = MB + 2 * NB;
+  i32x4 a[MB];
+  i32x2 b[NB][2];
+  __device__ __forceinline__ i32x4 bfrag(int n) const { return i32x4{b[n][0][0], b[n][0][1], b[n][1][0], b[n][1][1]}; }
+};
+
+template <class O, int MB, int NB>
+__device__ __forceinline__ void read_piece(const O& op, const char* base, int s, int q, Frags<MB, NB>& f) {
+  constexpr int BROW = O::C::B_ROWB, AROW = O::C::A_ROWB;
+  if (q < 2) {
+    f.b[0][q] = ds_read_tr(base + op.b_rd[0] + 16 * s * BROW + q * 4 * BROW);
+  } else if (q < 2 + MB) {
+    f.a[q - 2] = *reinterpret_cast<const i32x4*>(base + op.a_rd[s] + (q - 2) * 32 * AROW);
+  } else {
+    const int n = (q - 2 - MB) / 2 + 1, h = (q - 2 - MB) % 2;
+    f.b[n][h] = ds_read_tr(base + op.b_rd[n] + 16 * s * BROW + h * 4 * BROW);
+  }
+}
+
 template <int DT, int MB, int NB>
 __device__ __forceinline__ void mma_step(f32x16 (&acc)[NB][MB], const i32x4 (&fa)[MB], const i32x4 (&fb)[NB]) {
 #pragma unroll
@@ -326,16 +365,29 @@ __device__ __forceinline__ void mma_step(f32x16 (&acc)[NB][MB], const i32x4 (&fa
 
 // ---- lockstep main loop --------------------------------------------------------
 // All waves run the same schedule. At the end of k-tile t every wave waits until
-// its own copies of tile t+1 have landed and its reads of tile t are done, one
-// barrier publishes tile t+1 and releases stage t % STAGES, and the copies of tile
-// t + STAGES go to that stage at once.
-template <int DT, int EP, int BM, int BN, int WM, int WN, int BK, int STAGES>
+// its own copies of tile t+1 have landed and its reads of tile t are done, and one
+// barrier publishes tile t+1 and releases stage t % STAGES.
+//   SPREAD = false: the copies of tile t + STAGES go to that stage at once.
+//   SPREAD = true:  the copies of tile t + STAGES - 1 are issued during tile t, one
+//                   at a time between its MFMAs, into the stage tile t-1 released,
+//                   so no wave queues a burst of copies behind the texture unit.
+//   ILV = true:     each MFMA of a k-step is followed by one fragment read of the
+//                   next step, in consumption order, instead of a block of reads.
+template <int DT, int EP, int BM, int BN, int WM, int WN, int BK, int STAGES, bool SPREAD, bool ILV>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_dtl_kernel(Args p) {
   using C = DtlCfg<BM, BN, WM, WN, BK, STAGES>;
   using O = Operands<DT, BM, BN, WM, WN, BK, STAGES>;
+  using F = Frags<C::MB, C::NB>;
   static_assert(DT == F16 || DT == BF16, "16-bit types only");
   static_assert(C::KSTEPS % 2 == 0, "every tile starts on fragment buffer 0");
-  constexpr int MB = C::MB, NB = C::NB;
+  static_assert(!SPREAD || STAGES >= 3, "spread copies run STAGES - 2 tiles ahead");
+  constexpr int MB = C::MB, NB = C::NB, KS = C::KSTEPS;
+  constexpr int NMMA = MB * NB;                          // MFMAs per k-step
+  static_assert(!SPREAD || C::INST % KS == 0, "copies split evenly over the k-steps");
+  constexpr int PER_STEP = C::INST / KS;                 // spread copies per k-step
+  static_assert(!SPREAD || NMMA % PER_STEP == 0, "copies spread evenly over the MFMAs");
+  constexpr int EVERY = SPREAD ? NMMA / PER_STEP : 1;
+  static_assert(!ILV || F::PIECES <= NMMA, "one fragment read per MFMA");
 
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
 
@@ -356,42 +408,92 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_dtl_kernel
     for (int b = 0; b < MB; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
-  i32x4 fa[2][MB];
-  i32x4 fb[2][NB];
+  F fr[2];
 
-  // prologue: every stage filled, tile 0 complete
+  auto read_all = [&](const char* base, int s, F& f) {
 #pragma unroll
-  for (int t = 0; t < STAGES; ++t)
-    if (t < KT) op.issue_tile(t, t);
-  wait_tiles<C::INST, STAGES - 1>(min(STAGES - 1, KT - 1));
-  barrier_only();
-  op.read_step(smem, 0, fa[0], fb[0]);
+    for (int q = 0; q < F::PIECES; ++q) read_piece(op, base, s, q, f);
+  };
 
-  auto tile = [&](int kt, int u) {
+  // prologue: tile 0 complete, the next tiles in flight
+  constexpr int AHEAD = SPREAD ? STAGES - 1 : STAGES;   // tiles issued before the loop
+#pragma unroll
+  for (int t = 0; t < AHEAD; ++t)
+    if (t < KT) op.issue_tile(t, t);
+  wait_tiles<C::INST, AHEAD - 1>(min(AHEAD - 1, KT - 1));
+  barrier_only();
+  read_all(smem, 0, fr[0]);
+
+  // Copies issued after tile kt+1's when tile kt reaches its barrier (the most there
+  // can be in a steady tile).
+  auto wait_next_tile = [&](int kt, auto steady_tag) {
+    if constexpr (decltype(steady_tag)::value) {
+      if constexpr (SPREAD) wait_vmcnt<((STAGES - 3) * KS + KS - 1) * PER_STEP>();
+      else wait_vmcnt<(STAGES - 2) * C::INST>();
+    } else if constexpr (SPREAD) {
+      const int whole = max(0, min(STAGES - 3, KT - 2 - kt));
+      const int n = whole * KS + (kt + STAGES - 1 < KT ? KS - 1 : 0);   // in units of PER_STEP
+      wait_tiles<PER_STEP, (STAGES - 3) * KS + KS - 1>(n);
+    } else {
+      wait_tiles<C::INST, STAGES - 2>(min(STAGES - 2, KT - 2 - kt));
+    }
+  };
+
+  // STEADY tiles (all but the last STAGES) read ahead and copy without checks, so the
+  // MFMA stream carries no branches.
+  auto tile = [&](auto steady_tag, int kt, int u) {
+    constexpr bool STEADY = decltype(steady_tag)::value;
     const char* cur = smem + u * C::STAGE;
     const char* nxt = smem + ((u + 1) % STAGES) * C::STAGE;
+    const int kc = kt + STAGES - 1;                 // SPREAD: tile copied during this one
+    const int uc = (u + STAGES - 1) % STAGES;       // ... into the stage tile kt-1 released
+    const bool copy = STEADY || kc < KT;
 #pragma unroll
-    for (int s = 0; s < C::KSTEPS; ++s) {
+    for (int s = 0; s < KS; ++s) {
       const int buf = s & 1;
-      if (s < C::KSTEPS - 1) {
-        op.read_step(cur, s + 1, fa[buf ^ 1], fb[buf ^ 1]);
-      } else {
+      const bool last = s == KS - 1;
+      if (last) {
         // the last step is in registers: publish tile kt+1 and release stage u
-        wait_lgkmcnt<0>();                                               // reads of stage u done
-        wait_tiles<C::INST, STAGES - 2>(min(STAGES - 2, KT - 2 - kt));   // tile kt+1 landed
+        wait_lgkmcnt<0>();      // this wave's reads of stage u are done
+        wait_next_tile(kt, steady_tag);   // this wave's copies of tile kt+1 have landed
         barrier_only();
-        if (kt + STAGES < KT) op.issue_tile(kt + STAGES, u);
-        if (kt + 1 < KT) op.read_step(nxt, 0, fa[0], fb[0]);
+        if constexpr (!SPREAD) {
+          if (STEADY || kt + STAGES < KT) op.issue_tile(kt + STAGES, u);
+        }
       }
-      mma_step<DT, MB, NB>(acc, fa[buf], fb[buf]);
+      const char* rbase = last ? nxt : cur;
+      const int rs = last ? 0 : s + 1;
+      const bool reads = STEADY || !last || kt + 1 < KT;
+      if constexpr (!ILV) {
+        if (reads) read_all(rbase, rs, fr[buf ^ 1]);
+      }
+#pragma unroll
+      for (int i = 0; i < NMMA; ++i) {
+        const int a = i / MB, b = i % MB;
+        acc[a][b] = Tr<DT>::mma(fr[buf].bfrag(a), fr[buf].a[b], acc[a][b]);
+        if constexpr (ILV) {
+          if (i < F::PIECES && reads) read_piece(op, rbase, rs, i, fr[buf ^ 1]);
+        }
+        if constexpr (SPREAD) {
+          if (i % EVERY == 0 && copy) op.issue_one(kc, uc, (i / EVERY) * KS + s);
+        }
+        if constexpr (ILV || SPREAD) __builtin_amdgcn_sched_barrier(0);
+      }
       // keep each k-step's reads next to its MFMAs (no hoisting across steps)
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  for (int kt = 0; kt < KT; kt += STAGES) {
+  // A tile is steady when its reads of tile kt+1 and its copies (of tile kt + STAGES,
+  // or kt + STAGES - 1 when spread) stay below KT.
+  int kt = 0;
+  for (; kt + 2 * STAGES <= KT; kt += STAGES) {
+#pragma unroll
+    for (int u = 0; u < STAGES; ++u) tile(std::true_type{}, kt + u, u);
+  }
+  for (; kt < KT; kt += STAGES) {
 #pragma unroll
     for (int u = 0; u < STAGES; ++u)
-      if (kt + u < KT) tile(kt + u, u);
+      if (kt + u < KT) tile(std::false_type{}, kt + u, u);
   }
 
   // every wave is done with the stages: reuse them as per-wave epilogue scratch

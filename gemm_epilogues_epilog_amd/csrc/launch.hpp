@@ -18,15 +18,17 @@ struct TileCfg {
   const char* loop;   // main loop of the direct-to-LDS kernels
 };
 
-enum CfgId { CFG_S = 0, CFG_M = 1, CFG_L = 2, CFG_W4 = 3, CFG_P = 4, CFG_P5 = 5, CFG_COUNT = 6 };
+enum CfgId { CFG_S = 0, CFG_M, CFG_L, CFG_LI, CFG_LS, CFG_W4, CFG_W4S, CFG_P, CFG_COUNT };
 
 constexpr TileCfg kTiles[CFG_COUNT] = {
     {64, 64, 32, 32, 0, 2, "S", ""},
     {128, 128, 64, 64, 0, 2, "M", ""},
-    {256, 256, 128, 64, 64, 2, "L", "lockstep"},     // 8 waves
-    {256, 256, 128, 128, 64, 2, "W4", "lockstep"},   // 4 waves of 128 x 128
-    {256, 256, 128, 64, 32, 4, "P", "ping-pong"},    // 8 waves in two groups
-    {256, 256, 128, 64, 32, 5, "P5", "ping-pong"},
+    {256, 256, 128, 64, 64, 2, "L", "lockstep"},                      // 8 waves
+    {256, 256, 128, 64, 64, 2, "LI", "lockstep interleaved"},
+    {256, 256, 128, 64, 32, 4, "LS", "lockstep spread interleaved"},
+    {256, 256, 128, 128, 64, 2, "W4", "lockstep"},                    // 4 waves of 128 x 128
+    {256, 256, 128, 128, 32, 4, "W4S", "lockstep spread interleaved"},
+    {256, 256, 128, 64, 32, 4, "P", "ping-pong"},                     // 8 waves in two groups
 };
 
 inline bool cfg_is_dtl(int c) { return c >= CFG_L; }
@@ -41,13 +43,18 @@ hipError_t launch_generic(const Args& a, int grid, hipStream_t s) {
   return hipLaunchKernel(fn, dim3(grid), dim3((BM / WM) * (BN / WN) * 64), params, 0, s);
 }
 
-template <int DT, int EP, int BM, int BN, int WM, int WN, int BK, int ST, bool PP>
+enum Loop { LOCKSTEP = 0, LOCKSTEP_ILV = 1, LOCKSTEP_SPREAD_ILV = 2, PINGPONG = 3 };
+
+template <int DT, int EP, int BM, int BN, int WM, int WN, int BK, int ST, int LOOP>
 hipError_t launch_dtl(const Args& a, int grid, hipStream_t s) {
   Args copy = a;
   void* params[] = {&copy};
   const void* fn;
-  if constexpr (PP) fn = reinterpret_cast<const void*>(&gemm_pp_kernel<DT, EP, BM, BN, WM, WN, BK, ST>);
-  else fn = reinterpret_cast<const void*>(&gemm_dtl_kernel<DT, EP, BM, BN, WM, WN, BK, ST>);
+  if constexpr (LOOP == PINGPONG)
+    fn = reinterpret_cast<const void*>(&gemm_pp_kernel<DT, EP, BM, BN, WM, WN, BK, ST>);
+  else
+    fn = reinterpret_cast<const void*>(
+        &gemm_dtl_kernel<DT, EP, BM, BN, WM, WN, BK, ST, LOOP == LOCKSTEP_SPREAD_ILV, LOOP != LOCKSTEP>);
   return hipLaunchKernel(fn, dim3(grid), dim3((BM / WM) * (BN / WN) * 64), params, 0, s);
 }
 
@@ -60,10 +67,12 @@ LaunchFn pick_cfg(int cfg) {
   }
   if constexpr (DT != F32) {
     switch (cfg) {
-      case CFG_L: return &launch_dtl<DT, EP, 256, 256, 128, 64, 64, 2, false>;
-      case CFG_W4: return &launch_dtl<DT, EP, 256, 256, 128, 128, 64, 2, false>;
-      case CFG_P: return &launch_dtl<DT, EP, 256, 256, 128, 64, 32, 4, true>;
-      case CFG_P5: return &launch_dtl<DT, EP, 256, 256, 128, 64, 32, 5, true>;
+      case CFG_L: return &launch_dtl<DT, EP, 256, 256, 128, 64, 64, 2, LOCKSTEP>;
+      case CFG_LI: return &launch_dtl<DT, EP, 256, 256, 128, 64, 64, 2, LOCKSTEP_ILV>;
+      case CFG_LS: return &launch_dtl<DT, EP, 256, 256, 128, 64, 32, 4, LOCKSTEP_SPREAD_ILV>;
+      case CFG_W4: return &launch_dtl<DT, EP, 256, 256, 128, 128, 64, 2, LOCKSTEP>;
+      case CFG_W4S: return &launch_dtl<DT, EP, 256, 256, 128, 128, 32, 4, LOCKSTEP_SPREAD_ILV>;
+      case CFG_P: return &launch_dtl<DT, EP, 256, 256, 128, 64, 32, 4, PINGPONG>;
       default: break;
     }
   }
