@@ -10,6 +10,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdlib>
 #include <cstring>
 #include <new>
@@ -33,6 +34,11 @@ struct ge_plan {
   int partial_cols;
   void* t1;                // unfused intermediates
   void* t2;
+  int dp_tiles;            // split tail: tiles computed whole (all tiles when not split)
+  int sk_units, sk_wgs;    // split tail: k-tiles per split workgroup, split workgroups
+  float* sk_partial;       // split tail: one fp32 tile per split workgroup
+  uint32_t* sk_flag;       // split tail: epoch of each published partial
+  uint32_t epoch;          // execute counter, 1 .. 2^31 - 1
   std::string desc;
 };
 
@@ -71,6 +77,12 @@ const char* ep_name(ge_epilog_t e) {
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// An environment switch set to "0" (tuning experiments).
+bool env_off(const char* name) {
+  const char* v = std::getenv(name);
+  return v && v[0] == '0' && v[1] == 0;
+}
 
 // Pick the largest tile that still gives every compute unit at least one tile;
 // fall back to the smaller register-staged tiles for small problems.
@@ -163,31 +175,72 @@ ge_status_t gemm_epilog_plan(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt, ge
     return GE_ERR_NOT_SUPPORTED;
   }
 
-  // ---- workspace ----
+  // ---- split tail: a last round of tiles at most half full shares its K loop ----
+  // (split runs start at different k, so they share less of A and B in L2 than whole
+  // tiles do and run about 1.4x slower per k-tile: splitting pays when it saves more
+  // than that, i.e. when the last round is at most half full)
+  const int tiles = h->tiles_m * h->tiles_n;
+  h->dp_tiles = tiles;
+  if (gek::cfg_can_split(h->cfg) && !env_off("GE_STREAMK")) {
+    const int kt = (int)cdiv(k, tc.bk);
+    const int rem = tiles % cus;
+    if (rem != 0 && (int64_t)rem * 2 <= (int64_t)cus && kt >= 2) {
+      const int64_t units = (int64_t)rem * kt;
+      // runs of at least a quarter tile: an owner then adds at most about four partials
+      const int64_t per = std::max(cdiv(units, cus), cdiv(kt, 4));
+      if (per < kt) {   // a run of k-tiles then holds at most one tile start
+        h->dp_tiles = tiles - rem;
+        h->sk_units = (int)per;
+        h->sk_wgs = (int)cdiv(units, per);
+      }
+    }
+  }
+
+  // ---- workspace: [DRELU_BGRAD row sums | unfused T1, T2][split partials][split flags] ----
   const size_t es = elem_size(dt.d);
+  size_t main_bytes = 0;
   if (ep == GE_EPILOG_DRELU_BGRAD) {
     h->partial_cols = (int)cdiv(n, tc.wn);
-    h->ws_bytes = (size_t)h->partial_cols * (size_t)m * sizeof(float);
+    main_bytes = (size_t)h->partial_cols * (size_t)m * sizeof(float);
   } else if (ep == GE_EPILOG_RELU_BIAS_UNFUSED) {
-    h->ws_bytes = 2 * (size_t)m * (size_t)n * es;
+    main_bytes = 2 * (size_t)m * (size_t)n * es;
   }
+  main_bytes = (main_bytes + 255) & ~(size_t)255;
+  const size_t sk_part_bytes = (size_t)h->sk_wgs * gek::sk_slot_bytes(tc);
+  const size_t sk_flag_bytes = ((size_t)h->sk_wgs * sizeof(uint32_t) + 255) & ~(size_t)255;
+  h->ws_bytes = main_bytes + sk_part_bytes + sk_flag_bytes;
   if (h->ws_bytes) {
     if (hipMalloc(&h->ws, h->ws_bytes) != hipSuccess) {
       delete h;
       return GE_ERR_ALLOC;
     }
+    char* base = static_cast<char*>(h->ws);
     if (ep == GE_EPILOG_DRELU_BGRAD) {
-      h->partial = static_cast<float*>(h->ws);
-    } else {
-      h->t1 = h->ws;
-      h->t2 = static_cast<char*>(h->ws) + (size_t)m * (size_t)n * es;
+      h->partial = reinterpret_cast<float*>(base);
+    } else if (ep == GE_EPILOG_RELU_BIAS_UNFUSED) {
+      h->t1 = base;
+      h->t2 = base + (size_t)m * (size_t)n * es;
+    }
+    if (h->sk_wgs) {
+      h->sk_partial = reinterpret_cast<float*>(base + main_bytes);
+      h->sk_flag = reinterpret_cast<uint32_t*>(base + main_bytes + sk_part_bytes);
+      // epochs start at 1, so cleared flags never match
+      if (hipMemset(h->sk_flag, 0, sk_flag_bytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+        hipFree(h->ws);
+        delete h;
+        return GE_ERR_HIP;
+      }
     }
   }
   h->desc = std::string(dt_name(dt.ab)) + " " + ep_name(ep) + " tile " + std::to_string(tc.bm) + "x" +
             std::to_string(tc.bn) + " waves " + std::to_string(tc.bm / tc.wm) + "x" +
             std::to_string(tc.bn / tc.wn) + (gek::cfg_is_dtl(h->cfg) ? " bk " + std::to_string(tc.bk) + " stages " +
                                                  std::to_string(tc.stages) + " " + tc.loop : std::string()) +
-            " grid " + std::to_string(h->tiles_m * h->tiles_n);
+            " grid " + std::to_string(h->tiles_m * h->tiles_n) +
+            (h->sk_wgs ? " (" + std::to_string(h->dp_tiles) + " whole + " + std::to_string(tiles - h->dp_tiles) +
+                             " split over " + std::to_string(h->sk_wgs) + "x" + std::to_string(h->sk_units) +
+                             " k-tiles)"
+                       : std::string());
   *out = h;
   return GE_OK;
 }
@@ -227,6 +280,13 @@ ge_status_t gemm_epilog_execute(ge_handle_t h, const void* A, const void* B, con
   a.tiles_m = h->tiles_m;
   a.tiles_n = h->tiles_n;
   a.group_m = h->group_m;
+  a.dp_tiles = h->dp_tiles;
+  a.sk_units = h->sk_units;
+  a.sk_wgs = h->sk_wgs;
+  a.sk_partial = h->sk_partial;
+  a.sk_flag = h->sk_flag;
+  h->epoch = h->epoch % 0x7fffffffu + 1u;
+  a.epoch = h->epoch;
   const int grid = h->tiles_m * h->tiles_n;
 
   if (h->gemm(a, grid, s) != hipSuccess) return GE_ERR_HIP;

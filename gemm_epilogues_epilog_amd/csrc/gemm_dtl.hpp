@@ -373,8 +373,13 @@ __device__ __forceinline__ void mma_step(f32x16 (&acc)[NB][MB], const i32x4 (&fa
 //                   so no wave queues a burst of copies behind the texture unit.
 //   ILV = true:     each MFMA of a k-step is followed by one fragment read of the
 //                   next step, in consumption order, instead of a block of reads.
-template <int DT, int EP, int BM, int BN, int WM, int WN, int BK, int STAGES, bool SPREAD, bool ILV>
-__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_dtl_kernel(Args p) {
+//
+// lockstep_tile accumulates the k-tiles [kb, kb + nt) of one output tile into acc.
+// It expects no copy of its own in flight and every wave done with the LDS; on
+// return every copy has landed, but reads of the last stage may still be in flight.
+template <int DT, int BM, int BN, int WM, int WN, int BK, int STAGES, bool SPREAD, bool ILV>
+__device__ __forceinline__ void lockstep_tile(const Args& p, char* smem, int64_t m0, int n0, int kb, int nt,
+                                              f32x16 (&acc)[WN / 32][WM / 32]) {
   using C = DtlCfg<BM, BN, WM, WN, BK, STAGES>;
   using O = Operands<DT, BM, BN, WM, WN, BK, STAGES>;
   using F = Frags<C::MB, C::NB>;
@@ -389,19 +394,12 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_dtl_kernel
   constexpr int EVERY = SPREAD ? NMMA / PER_STEP : 1;
   static_assert(!ILV || F::PIECES <= NMMA, "one fragment read per MFMA");
 
-  __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
-
-  int tm, tn;
-  tile_coords(p, tm, tn);
-  const int64_t m0 = (int64_t)tm * BM;
-  const int n0 = tn * BN;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = w % C::WAVES_M, wn = w / C::WAVES_M;
   const O op(p, m0, n0, w, wm, wn, lane, (uint32_t)(uintptr_t)(lds_void*)smem);
-  const int KT = (p.k + BK - 1) / BK;
+  const int KT = nt;   // k-tiles of this call; k-tile t is global k-tile kb + t
 
-  f32x16 acc[NB][MB];
 #pragma unroll
   for (int a = 0; a < NB; ++a)
 #pragma unroll
@@ -419,7 +417,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_dtl_kernel
   constexpr int AHEAD = SPREAD ? STAGES - 1 : STAGES;   // tiles issued before the loop
 #pragma unroll
   for (int t = 0; t < AHEAD; ++t)
-    if (t < KT) op.issue_tile(t, t);
+    if (t < KT) op.issue_tile(kb + t, t);
   wait_tiles<C::INST, AHEAD - 1>(min(AHEAD - 1, KT - 1));
   barrier_only();
   read_all(smem, 0, fr[0]);
@@ -454,11 +452,11 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_dtl_kernel
       const bool last = s == KS - 1;
       if (last) {
         // the last step is in registers: publish tile kt+1 and release stage u
-        wait_lgkmcnt<0>();      // this wave's reads of stage u are done
+        wait_lgkmcnt<0>();                // this wave's reads of stage u are done
         wait_next_tile(kt, steady_tag);   // this wave's copies of tile kt+1 have landed
         barrier_only();
         if constexpr (!SPREAD) {
-          if (STEADY || kt + STAGES < KT) op.issue_tile(kt + STAGES, u);
+          if (STEADY || kt + STAGES < KT) op.issue_tile(kb + kt + STAGES, u);
         }
       }
       const char* rbase = last ? nxt : cur;
@@ -475,7 +473,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_dtl_kernel
           if (i < F::PIECES && reads) read_piece(op, rbase, rs, i, fr[buf ^ 1]);
         }
         if constexpr (SPREAD) {
-          if (i % EVERY == 0 && copy) op.issue_one(kc, uc, (i / EVERY) * KS + s);
+          if (i % EVERY == 0 && copy) op.issue_one(kb + kc, uc, (i / EVERY) * KS + s);
         }
         if constexpr (ILV || SPREAD) __builtin_amdgcn_sched_barrier(0);
       }
@@ -495,11 +493,175 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_dtl_kernel
     for (int u = 0; u < STAGES; ++u)
       if (kt + u < KT) tile(std::false_type{}, kt + u, u);
   }
+}
+
+// One workgroup per output tile.
+template <int DT, int EP, int BM, int BN, int WM, int WN, int BK, int STAGES, bool SPREAD, bool ILV>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_dtl_kernel(Args p) {
+  using C = DtlCfg<BM, BN, WM, WN, BK, STAGES>;
+  __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
+  int tm, tn;
+  tile_coords(p, tm, tn);
+  const int64_t m0 = (int64_t)tm * BM;
+  const int n0 = tn * BN;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = w % C::WAVES_M, wn = w / C::WAVES_M;
+
+  f32x16 acc[C::NB][C::MB];
+  lockstep_tile<DT, BM, BN, WM, WN, BK, STAGES, SPREAD, ILV>(p, smem, m0, n0, 0, (p.k + BK - 1) / BK, acc);
 
   // every wave is done with the stages: reuse them as per-wave epilogue scratch
   wait_lgkmcnt<0>();
   barrier_only();
-  epilogue_lds<DT, EP, MB, NB, WN>(p, acc, m0 + wm * WM, n0 + wn * WN, lane, smem + w * C::SCRATCH);
+  epilogue_lds<DT, EP, C::MB, C::NB, WN>(p, acc, m0 + wm * WM, n0 + wn * WN, lane, smem + w * C::SCRATCH);
+}
+
+// ---- split tail of the tile grid -------------------------------------------------
+// With T tiles on P compute units, T % P tiles would run as a last, partly empty
+// round. gemm_sk_kernel runs dp_tiles = P * floor(T / P) tiles whole (one per
+// workgroup, as gemm_dtl_kernel does) and hands the K loop of the remaining tiles to
+// sk_wgs more workgroups, in equal runs of sk_units k-tiles taken in order over
+// (tile, k-tile). Because sk_units < KT, a run holds at most one tile start: before
+// it lies at most one piece that does not start at k = 0 (a partial), from it on the
+// piece that does (the owner piece). The workgroup computes its partial first, stores
+// it as fp32 in its slot and publishes it with the execute's epoch, then computes its
+// owner piece, adds the partials of the runs that hold the rest of that tile and runs
+// the epilogue. No workgroup waits before publishing its partial, so every wait ends
+// once the workgroups it waits for have been scheduled. Runs are renumbered so each
+// XCD takes a contiguous range of them.
+//
+// A partial slot holds, per wave, the fp32 accumulators as 4-float groups q, lane-
+// minor (one 1 KB store per group). Partials cross XCDs, whose L2 caches are not
+// coherent with each other: they are written and read with device-scope (sc1) buffer
+// instructions, which write through to and read from the memory side, so publishing
+// needs no writeback or invalidation of a whole L2.
+template <int MB, int NB>
+struct PartialLayout {
+  static constexpr int QUADS = NB * MB * 4;                     // 4-float groups per lane
+  static constexpr int WAVE_BYTES = QUADS * 64 * 16;
+  __device__ static __forceinline__ uint32_t off(int w, int q, int lane) {
+    return (uint32_t)(w * WAVE_BYTES + (q * 64 + lane) * 16);
+  }
+};
+constexpr int kDeviceScope = 16;   // cache-policy bit sc1 of a buffer instruction
+
+// Spin limit of the owner's wait (about a second): a partial that never arrives
+// turns the tile into NaN instead of hanging the device.
+constexpr int kSkSpinLimit = 1 << 20;
+
+template <int DT, int EP, int BM, int BN, int WM, int WN, int BK, int STAGES, bool SPREAD, bool ILV>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_sk_kernel(Args p) {
+  using C = DtlCfg<BM, BN, WM, WN, BK, STAGES>;
+  using PL = PartialLayout<C::MB, C::NB>;
+  constexpr int MB = C::MB, NB = C::NB;
+  __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = w % C::WAVES_M, wn = w / C::WAVES_M;
+  const int KT = (p.k + BK - 1) / BK;
+  const size_t slot_bytes = (size_t)C::NW * PL::WAVE_BYTES;
+
+  // ---- this workgroup's pieces: a whole tile, or a run's partial and owner piece ----
+  const bool split = (int)blockIdx.x >= p.dp_tiles;
+  int r = 0;              // run
+  int pa_t = 0, pa_kb = 0, pa_nt = 0;   // partial piece (pa_nt == 0: none)
+  int pos, kb, nt;        // whole tile or owner piece (nt == 0: none)
+  if (!split) {
+    pos = xcd_remap(blockIdx.x, p.dp_tiles);
+    kb = 0;
+    nt = KT;
+  } else {
+    r = xcd_remap(blockIdx.x - p.dp_tiles, p.sk_wgs);
+    const int u0 = r * p.sk_units;
+    const int u1 = min((p.tiles_m * p.tiles_n - p.dp_tiles) * KT, u0 + p.sk_units);
+    const int ts = (u0 + KT - 1) / KT * KT;   // first tile start at or after u0
+    if (u0 < min(ts, u1)) {
+      pa_t = u0 / KT;
+      pa_kb = u0 - pa_t * KT;
+      pa_nt = min(ts, u1) - u0;
+    }
+    pos = p.dp_tiles + ts / KT;
+    kb = 0;
+    nt = max(0, u1 - ts);
+  }
+
+  f32x16 acc[NB][MB];
+  if (pa_nt > 0) {
+    int tm, tn;
+    raster(p, p.dp_tiles + pa_t, tm, tn);
+    lockstep_tile<DT, BM, BN, WM, WN, BK, STAGES, SPREAD, ILV>(p, smem, (int64_t)tm * BM, tn * BN, pa_kb, pa_nt, acc);
+    // store the partial at device scope, then publish it once every wave's stores
+    // have completed
+    const __amdgpu_buffer_rsrc_t slot = rsrc(reinterpret_cast<char*>(p.sk_partial) + (size_t)r * slot_bytes);
+#pragma unroll
+    for (int a = 0; a < NB; ++a)
+#pragma unroll
+      for (int bb = 0; bb < MB; ++bb)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const i32x4 v = {__float_as_int(acc[a][bb][4 * r4]), __float_as_int(acc[a][bb][4 * r4 + 1]),
+                           __float_as_int(acc[a][bb][4 * r4 + 2]), __float_as_int(acc[a][bb][4 * r4 + 3])};
+          __builtin_amdgcn_raw_buffer_store_b128(v, slot, PL::off(w, (a * MB + bb) * 4 + r4, lane), 0, kDeviceScope);
+        }
+    wait_vmcnt<0>();
+    wait_lgkmcnt<0>();   // also: every wave is done with the LDS before the next piece
+    barrier_only();
+    if (threadIdx.x == 0) __hip_atomic_store(p.sk_flag + r, p.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (nt == 0) return;
+
+  int tm, tn;
+  raster(p, pos, tm, tn);
+  lockstep_tile<DT, BM, BN, WM, WN, BK, STAGES, SPREAD, ILV>(p, smem, (int64_t)tm * BM, tn * BN, kb, nt, acc);
+  if (split) {
+    // the owner: add the partials of the runs that hold the rest of the tile
+    const int t = pos - p.dp_tiles;
+    const int last = min(((t + 1) * KT - 1) / p.sk_units, p.sk_wgs - 1);
+    bool lost = false;
+    for (int o = r + 1; o <= last; ++o) {
+      int spins = 0;
+      // the partial's loads are issued only after its flag has been seen (control
+      // dependency) and read the memory side (device scope)
+      while (__hip_atomic_load(p.sk_flag + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != p.epoch) {
+        if (++spins > kSkSpinLimit) {
+          lost = true;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(8);
+      }
+      const __amdgpu_buffer_rsrc_t slot = rsrc(reinterpret_cast<char*>(p.sk_partial) + (size_t)o * slot_bytes);
+      // sixteen loads in flight at a time, then the adds
+      constexpr int BATCH = 16;
+      static_assert(PL::QUADS % BATCH == 0, "load batches");
+#pragma unroll
+      for (int q0 = 0; q0 < PL::QUADS; q0 += BATCH) {
+        i32x4 v[BATCH];
+#pragma unroll
+        for (int j = 0; j < BATCH; ++j)
+          v[j] = __builtin_amdgcn_raw_buffer_load_b128(slot, PL::off(w, q0 + j, lane), 0, kDeviceScope);
+#pragma unroll
+        for (int j = 0; j < BATCH; ++j) {
+          const int q = q0 + j, a = q / (4 * MB), bb = (q / 4) % MB, r4 = q % 4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[a][bb][4 * r4 + e] += __int_as_float(v[j][e]);
+        }
+      }
+    }
+    if (lost) {
+#pragma unroll
+      for (int a = 0; a < NB; ++a)
+#pragma unroll
+        for (int bb = 0; bb < MB; ++bb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[a][bb][e] = __builtin_nanf("");
+    }
+  }
+  // every wave is done with the stages: reuse them as per-wave epilogue scratch
+  wait_lgkmcnt<0>();
+  barrier_only();
+  epilogue_lds<DT, EP, MB, NB, WN>(p, acc, (int64_t)tm * BM + wm * WM, tn * BN + wn * WN, lane,
+                                   smem + w * C::SCRATCH);
 }
 
 // ---- ping-pong main loop -------------------------------------------------------

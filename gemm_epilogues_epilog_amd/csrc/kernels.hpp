@@ -40,6 +40,7 @@ enum Ep { NONE = 0, RELU_BIAS = 1, GELU_BIAS = 2, RELU_AUX_BIAS = 3, DRELU_BGRAD
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
@@ -62,6 +63,15 @@ struct Args {
   int32_t tiles_m;
   int32_t tiles_n;
   int32_t group_m;    // tile rasterisation: m-tiles per group
+  // Split tail of the tile grid (direct-to-LDS kernels only; dp_tiles == all tiles
+  // when unused): workgroups past the first dp_tiles share the remaining tiles'
+  // k-tiles evenly, sk_units each.
+  int32_t dp_tiles;   // tiles computed whole, one per workgroup
+  int32_t sk_units;   // k-tiles per split workgroup
+  int32_t sk_wgs;     // split workgroups
+  uint32_t epoch;     // changes every execute; marks this execute's partials
+  float* sk_partial;  // per split workgroup: one tile of fp32 partial accumulators
+  uint32_t* sk_flag;  // per split workgroup: epoch of its published partial
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base) {
@@ -112,21 +122,27 @@ __device__ __forceinline__ void copy_to_lds_b128(const i32x4& srd, uint32_t voff
                : "memory", "m0");
 }
 
-// Workgroup id -> (m-tile, n-tile). Workgroups are dealt to the 8 XCDs round-robin;
-// renumber them so each XCD walks a contiguous range of tiles, then walk tiles in
-// groups of group_m m-tiles (m fastest inside a group) so tiles that run together
-// share A and B in the XCD's L2.
-__device__ __forceinline__ void tile_coords(const Args& p, int& tm, int& tn) {
-  const int G = p.tiles_m * p.tiles_n;
-  int id = blockIdx.x;
+// Workgroups are dealt to the 8 XCDs round-robin (id % 8). Renumber ids 0 .. G-1 so
+// each XCD walks a contiguous range of positions.
+__device__ __forceinline__ int xcd_remap(int id, int G) {
   const int per = G / 8, rem = G % 8, x = id % 8, local = id / 8;
-  id = (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + local;
+  return (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + local;
+}
+
+// Position in the tile order -> (m-tile, n-tile): groups of group_m m-tiles, m fastest
+// inside a group, so tiles that run together share A and B in an XCD's L2.
+__device__ __forceinline__ void raster(const Args& p, int pos, int& tm, int& tn) {
   const int gsz = p.group_m * p.tiles_n;
-  const int g = id / gsz, first_m = g * p.group_m;
+  const int g = pos / gsz, first_m = g * p.group_m;
   const int rows = min(p.tiles_m - first_m, p.group_m);
-  const int in = id - g * gsz;
+  const int in = pos - g * gsz;
   tm = first_m + in % rows;
   tn = in / rows;
+}
+
+// Workgroup id -> (m-tile, n-tile) when every workgroup computes one whole tile.
+__device__ __forceinline__ void tile_coords(const Args& p, int& tm, int& tn) {
+  raster(p, xcd_remap(blockIdx.x, p.tiles_m * p.tiles_n), tm, tn);
 }
 
 // ---- element traits ------------------------------------------------------------

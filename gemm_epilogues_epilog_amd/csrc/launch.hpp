@@ -32,6 +32,9 @@ constexpr TileCfg kTiles[CFG_COUNT] = {
 };
 
 inline bool cfg_is_dtl(int c) { return c >= CFG_L; }
+// Configurations whose kernel can split the last round's K loop (8-wave lockstep
+// loops; the 4-wave tile has no registers left for the partial sums).
+inline bool cfg_can_split(int c) { return c == CFG_L || c == CFG_LI || c == CFG_LS; }
 
 using LaunchFn = hipError_t (*)(const Args&, int grid, hipStream_t);
 
@@ -45,18 +48,30 @@ hipError_t launch_generic(const Args& a, int grid, hipStream_t s) {
 
 enum Loop { LOCKSTEP = 0, LOCKSTEP_ILV = 1, LOCKSTEP_SPREAD_ILV = 2, PINGPONG = 3 };
 
+// `grid` is the number of tiles; with a split tail (a.dp_tiles < tiles) the grid is
+// dp_tiles + sk_wgs workgroups of the split-tail kernel.
 template <int DT, int EP, int BM, int BN, int WM, int WN, int BK, int ST, int LOOP>
 hipError_t launch_dtl(const Args& a, int grid, hipStream_t s) {
   Args copy = a;
   void* params[] = {&copy};
   const void* fn;
-  if constexpr (LOOP == PINGPONG)
+  constexpr bool SPREAD = LOOP == LOCKSTEP_SPREAD_ILV, ILV = LOOP != LOCKSTEP;
+  if constexpr (LOOP == PINGPONG) {
     fn = reinterpret_cast<const void*>(&gemm_pp_kernel<DT, EP, BM, BN, WM, WN, BK, ST>);
-  else
-    fn = reinterpret_cast<const void*>(
-        &gemm_dtl_kernel<DT, EP, BM, BN, WM, WN, BK, ST, LOOP == LOCKSTEP_SPREAD_ILV, LOOP != LOCKSTEP>);
+  } else {
+    fn = reinterpret_cast<const void*>(&gemm_dtl_kernel<DT, EP, BM, BN, WM, WN, BK, ST, SPREAD, ILV>);
+    if constexpr ((BM / WM) * (BN / WN) == 8) {   // the split tail exists for the 8-wave tiles
+      if (a.dp_tiles < grid) {
+        fn = reinterpret_cast<const void*>(&gemm_sk_kernel<DT, EP, BM, BN, WM, WN, BK, ST, SPREAD, ILV>);
+        grid = a.dp_tiles + a.sk_wgs;
+      }
+    }
+  }
   return hipLaunchKernel(fn, dim3(grid), dim3((BM / WM) * (BN / WN) * 64), params, 0, s);
 }
+
+// Partial-accumulator bytes of one split workgroup of a configuration (one tile, fp32).
+inline size_t sk_slot_bytes(const TileCfg& c) { return (size_t)c.bm * c.bn * sizeof(float); }
 
 template <int DT, int EP>
 LaunchFn pick_cfg(int cfg) {

@@ -14,16 +14,22 @@ GUARD = 256   # guard elements (multiple of 16 bytes for every dtype)
 
 @contextmanager
 def tile_env(tile):
-    old = os.environ.get("GE_TILE")
+    """Force a tile configuration for the plans made inside. A "-nosk" suffix also turns
+    off the split tail (GE_STREAMK=0)."""
+    saved = {k: os.environ.get(k) for k in ("GE_TILE", "GE_STREAMK")}
     if tile:
-        os.environ["GE_TILE"] = tile
+        name, _, opt = tile.partition("-")
+        os.environ["GE_TILE"] = name
+        if opt == "nosk":
+            os.environ["GE_STREAMK"] = "0"
     try:
         yield
     finally:
-        if old is None:
-            os.environ.pop("GE_TILE", None)
-        else:
-            os.environ["GE_TILE"] = old
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
 
 
 def guarded(numel, dtype, fill):

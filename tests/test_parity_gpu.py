@@ -19,7 +19,7 @@ from tests.helpers import assert_bgrad, assert_close, assert_mask, tight_ratio, 
 pytestmark = pytest.mark.gpu
 
 DTS = ["f32", "f16", "bf16"]
-TILES = {"f32": ["S", "M"], "f16": ["S", "M", "L", "LI", "LS", "W4", "W4S", "P"], "bf16": ["S", "M", "L", "LI", "LS", "W4", "W4S", "P"]}
+TILES = {"f32": ["S", "M"], "f16": ["S", "M", "L", "L-nosk", "LI", "LS", "W4", "W4S", "P"], "bf16": ["S", "M", "L", "L-nosk", "LI", "LS", "W4", "W4S", "P"]}
 INT_SHAPES = [(1, 8, 8), (33, 136, 72), (200, 264, 200), (300, 520, 136)]
 
 
@@ -165,3 +165,28 @@ def test_stream_argument(gpu):
     g = R.run(gpu, "RELU_BIAS", "f16", A, B, bias, stream=s)
     o = oracle.gemm_epilog(to_np(A), to_np(B), "RELU_BIAS", bias=to_np(bias))
     assert_close(g["D"], o["D"], "f16")
+
+
+def test_split_tail_plan_and_determinism(gpu):
+    """4352 x 4096 (272 tiles on 256 compute units) splits its last round of 16 tiles;
+    the split result matches the unsplit one within rounding and repeats bit for bit,
+    and the 7B-FFN shape (last round 69% full) is not split."""
+    ge = gpu
+    h = ge.gemm_epilog_plan(4096, 11008, 4096, ("f16", "f16", "f16"), "RELU_BIAS")
+    try:
+        assert "split" not in ge.gemm_epilog_describe(h)
+    finally:
+        ge.gemm_epilog_free(h)
+    m, n, k = 4352, 4096, 1024
+    A, B, bias, _, _ = inputs.small_case(m, n, k, "f16", std=k ** -0.5, std_bias=0.02)
+    g1 = R.run(gpu, "RELU_AUX_BIAS", "f16", A, B, bias, repeat=2)
+    assert "split" in g1["desc"]
+    g2 = R.run(gpu, "RELU_AUX_BIAS", "f16", A, B, bias)
+    assert torch.equal(g1["D_dev"], g2["D_dev"]) and torch.equal(g1["mask_dev"], g2["mask_dev"])
+    g0 = R.run(gpu, "RELU_AUX_BIAS", "f16", A, B, bias, tile="L-nosk")
+    assert "split" not in g0["desc"]
+    assert_close(g1["D"], g0["D"], "f16", "split vs unsplit")
+    rows = np.r_[0:32, 4096:4352]   # the first row group and the split tiles' rows
+    o = oracle.gemm_epilog(to_np(A)[rows], to_np(B), "RELU_AUX_BIAS", bias=to_np(bias)[rows], want_pre=True)
+    assert_close(g1["D"][rows], o["D"], "f16", "split vs oracle")
+

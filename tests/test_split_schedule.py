@@ -1,0 +1,90 @@
+"""Model of the split-tail schedule of the direct-to-LDS kernels (CPU only).
+
+The plan gives the last, partly empty round of T tiles on P compute units
+(T % P tiles) to runs of sk_units k-tiles, one workgroup per run, which computes its
+partial piece (if any) before its owner piece (if any). This model restates the
+plan's choice and the kernel's piece arithmetic and checks the invariants the kernel
+relies on: every (tile, k-tile) is computed exactly once, each tile has exactly one
+owner piece starting at k = 0, each run publishes at most one partial (which never
+starts at k = 0), and the runs an owner waits for are exactly the runs that hold the
+rest of its tile, each of which publishes before it waits for anything."""
+import pytest
+
+
+def plan(tiles, kt, cus=256):
+    rem = tiles % cus
+    if not (rem != 0 and rem * 2 <= cus and kt >= 2):
+        return None
+    units = rem * kt
+    per = max(-(-units // cus), -(-kt // 4))
+    if per >= kt:
+        return None
+    return tiles - rem, per, -(-units // per)
+
+
+def xcd_remap(i, g):
+    per, rem, x, local = g // 8, g % 8, i % 8, i // 8
+    return (x * (per + 1) if x < rem else rem * (per + 1) + (x - rem) * per) + local
+
+
+def pieces(tiles, kt, cus=256):
+    """(run, kind, tile, kb, nt) in the order one run's workgroup computes them."""
+    dp, u, wgs = plan(tiles, kt, cus)
+    total = (tiles - dp) * kt
+    for wid in range(wgs):
+        r = xcd_remap(wid, wgs)
+        u0 = r * u
+        u1 = min(total, u0 + u)
+        ts = -(-u0 // kt) * kt
+        if u0 < min(ts, u1):
+            t = u0 // kt
+            yield r, "partial", t, u0 - t * kt, min(ts, u1) - u0
+        if ts < u1:
+            yield r, "owner", ts // kt, 0, u1 - ts
+
+
+def check(tiles, kt, cus=256):
+    dp, u, wgs = plan(tiles, kt, cus)
+    total = (tiles - dp) * kt
+    assert sorted(xcd_remap(i, wgs) for i in range(wgs)) == list(range(wgs))
+    assert wgs * u >= total > (wgs - 1) * u
+    cover, owners, partial_of = set(), {}, {}
+    last_kind = {}
+    for r, kind, t, kb, nt in pieces(tiles, kt, cus):
+        assert kb + nt <= kt
+        for kk in range(kb, kb + nt):
+            assert (t, kk) not in cover
+            cover.add((t, kk))
+        if kind == "owner":
+            assert kb == 0 and t not in owners
+            owners[t] = r
+        else:
+            assert kb > 0 and r not in partial_of and r not in last_kind   # partial comes first
+            partial_of[r] = t
+        last_kind[r] = kind
+    assert len(cover) == total
+    for t in range(tiles - dp):
+        r = owners[t]
+        last = min(((t + 1) * kt - 1) // u, wgs - 1)
+        partners = list(range(r + 1, last + 1))
+        assert sorted(o for o, tt in partial_of.items() if tt == t) == partners
+
+
+def test_sparse_last_round_splits():
+    # 4352 x 4096 with 256 x 256 tiles: 272 tiles, the last round holds 16
+    dp, u, wgs = plan(272, 64)
+    assert (dp, u, wgs) == (256, 16, 64)
+    check(272, 64)
+
+
+def test_full_or_mostly_full_rounds_do_not_split():
+    assert plan(1024, 128) is None and plan(8192, 256) is None and plan(512, 64) is None
+    assert plan(688, 64) is None   # 4096 x 11008: last round 69% full
+    assert plan(255, 64) is None
+
+
+@pytest.mark.parametrize("tiles", list(range(1, 1100, 13)))
+@pytest.mark.parametrize("kt", [2, 3, 5, 8, 33, 64, 128])
+def test_schedule_invariants(tiles, kt):
+    if plan(tiles, kt) is not None:
+        check(tiles, kt)
