@@ -60,10 +60,12 @@ __device__ __forceinline__ int swz_b(int row) {
   return u == 0 ? 0 : u == 1 ? 6 : u == 2 ? 10 : 12;
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int STAGES>
+// CW: how many waves (the first CW) issue the operand copies; 0 = all of them.
+template <int BM, int BN, int WM, int WN, int BK, int STAGES, int CW_ = 0>
 struct DtlCfg {
   static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN;
   static constexpr int NW = WAVES_M * WAVES_N, NT = NW * 64;
+  static constexpr int CW = CW_ ? CW_ : NW;
   static constexpr int MB = WM / 32, NB = WN / 32;
   static constexpr int KSTEPS = BK / 16;                  // MFMA k-steps per tile
   static constexpr int A_ROWB = BK * 2;                   // bytes per A row in LDS
@@ -75,14 +77,15 @@ struct DtlCfg {
   static constexpr int B_CHUNKS = B_ROWB / 16;
   static constexpr int B_RPI = 1024 / B_ROWB;
   static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int A_INST = A_BYTES / 1024 / NW;      // 1 KB copies per wave per tile
-  static constexpr int B_INST = B_BYTES / 1024 / NW;
+  static constexpr int A_INST = A_BYTES / 1024 / CW;      // 1 KB copies per copy wave per tile
+  static constexpr int B_INST = B_BYTES / 1024 / CW;
   static constexpr int INST = A_INST + B_INST;
   static constexpr int SCRATCH = WM * WN * 2;             // epilogue bytes per wave
   static constexpr int LDS = STAGES * STAGE;
   static_assert(BK == 32 || BK == 64, "k-tile");
   static_assert(BN >= 128 && BN % 64 == 0, "B rows must hold at least 16 chunks");
-  static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "copy split");
+  static_assert(CW >= 1 && CW <= NW, "copy waves");
+  static_assert(A_BYTES % (1024 * CW) == 0 && B_BYTES % (1024 * CW) == 0, "copy split");
   static_assert(STAGES >= 2 && LDS <= 160 * 1024, "LDS");
   static_assert(NW * SCRATCH <= LDS, "epilogue scratch");
   static_assert((STAGES - 2) * INST < 64, "vmcnt range");
@@ -223,9 +226,9 @@ __device__ __forceinline__ void epilogue_lds(const Args& p, f32x16 (&acc)[NB][MB
 }
 
 // ---- operand copies and fragment reads shared by both main loops ---------------
-template <int DT, int BM, int BN, int WM, int WN, int BK, int STAGES>
+template <int DT, int BM, int BN, int WM, int WN, int BK, int STAGES, int CW = 0>
 struct Operands {
-  using C = DtlCfg<BM, BN, WM, WN, BK, STAGES>;
+  using C = DtlCfg<BM, BN, WM, WN, BK, STAGES, CW>;
   static constexpr int MB = C::MB, NB = C::NB;
   static constexpr int A_PART = C::A_INST / C::KSTEPS, B_PART = C::B_INST / C::KSTEPS;
 
@@ -377,11 +380,11 @@ __device__ __forceinline__ void mma_step(f32x16 (&acc)[NB][MB], const i32x4 (&fa
 // lockstep_tile accumulates the k-tiles [kb, kb + nt) of one output tile into acc.
 // It expects no copy of its own in flight and every wave done with the LDS; on
 // return every copy has landed, but reads of the last stage may still be in flight.
-template <int DT, int BM, int BN, int WM, int WN, int BK, int STAGES, bool SPREAD, bool ILV>
+template <int DT, int BM, int BN, int WM, int WN, int BK, int STAGES, bool SPREAD, bool ILV, int CW>
 __device__ __forceinline__ void lockstep_tile(const Args& p, char* smem, int64_t m0, int n0, int kb, int nt,
                                               f32x16 (&acc)[WN / 32][WM / 32]) {
-  using C = DtlCfg<BM, BN, WM, WN, BK, STAGES>;
-  using O = Operands<DT, BM, BN, WM, WN, BK, STAGES>;
+  using C = DtlCfg<BM, BN, WM, WN, BK, STAGES, CW>;
+  using O = Operands<DT, BM, BN, WM, WN, BK, STAGES, CW>;
   using F = Frags<C::MB, C::NB>;
   static_assert(DT == F16 || DT == BF16, "16-bit types only");
   static_assert(C::KSTEPS % 2 == 0, "every tile starts on fragment buffer 0");
@@ -399,6 +402,7 @@ __device__ __forceinline__ void lockstep_tile(const Args& p, char* smem, int64_t
   const int wm = w % C::WAVES_M, wn = w / C::WAVES_M;
   const O op(p, m0, n0, w, wm, wn, lane, (uint32_t)(uintptr_t)(lds_void*)smem);
   const int KT = nt;   // k-tiles of this call; k-tile t is global k-tile kb + t
+  const bool copier = w < C::CW;   // waves past CW issue no copies and wait for none
 
 #pragma unroll
   for (int a = 0; a < NB; ++a)
@@ -415,10 +419,12 @@ __device__ __forceinline__ void lockstep_tile(const Args& p, char* smem, int64_t
 
   // prologue: tile 0 complete, the next tiles in flight
   constexpr int AHEAD = SPREAD ? STAGES - 1 : STAGES;   // tiles issued before the loop
+  if (copier) {
 #pragma unroll
-  for (int t = 0; t < AHEAD; ++t)
-    if (t < KT) op.issue_tile(kb + t, t);
-  wait_tiles<C::INST, AHEAD - 1>(min(AHEAD - 1, KT - 1));
+    for (int t = 0; t < AHEAD; ++t)
+      if (t < KT) op.issue_tile(kb + t, t);
+    wait_tiles<C::INST, AHEAD - 1>(min(AHEAD - 1, KT - 1));
+  }
   barrier_only();
   read_all(smem, 0, fr[0]);
 
@@ -453,10 +459,10 @@ __device__ __forceinline__ void lockstep_tile(const Args& p, char* smem, int64_t
       if (last) {
         // the last step is in registers: publish tile kt+1 and release stage u
         wait_lgkmcnt<0>();                // this wave's reads of stage u are done
-        wait_next_tile(kt, steady_tag);   // this wave's copies of tile kt+1 have landed
+        if (copier) wait_next_tile(kt, steady_tag);   // this wave's copies of tile kt+1 have landed
         barrier_only();
         if constexpr (!SPREAD) {
-          if (STEADY || kt + STAGES < KT) op.issue_tile(kb + kt + STAGES, u);
+          if (copier && (STEADY || kt + STAGES < KT)) op.issue_tile(kb + kt + STAGES, u);
         }
       }
       const char* rbase = last ? nxt : cur;
@@ -473,7 +479,7 @@ __device__ __forceinline__ void lockstep_tile(const Args& p, char* smem, int64_t
           if (i < F::PIECES && reads) read_piece(op, rbase, rs, i, fr[buf ^ 1]);
         }
         if constexpr (SPREAD) {
-          if (i % EVERY == 0 && copy) op.issue_one(kb + kc, uc, (i / EVERY) * KS + s);
+          if (i % EVERY == 0 && copy && copier) op.issue_one(kb + kc, uc, (i / EVERY) * KS + s);
         }
         if constexpr (ILV || SPREAD) __builtin_amdgcn_sched_barrier(0);
       }
@@ -496,7 +502,7 @@ __device__ __forceinline__ void lockstep_tile(const Args& p, char* smem, int64_t
 }
 
 // One workgroup per output tile.
-template <int DT, int EP, int BM, int BN, int WM, int WN, int BK, int STAGES, bool SPREAD, bool ILV>
+template <int DT, int EP, int BM, int BN, int WM, int WN, int BK, int STAGES, bool SPREAD, bool ILV, int CW>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_dtl_kernel(Args p) {
   using C = DtlCfg<BM, BN, WM, WN, BK, STAGES>;
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
@@ -509,7 +515,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_dtl_kernel
   const int wm = w % C::WAVES_M, wn = w / C::WAVES_M;
 
   f32x16 acc[C::NB][C::MB];
-  lockstep_tile<DT, BM, BN, WM, WN, BK, STAGES, SPREAD, ILV>(p, smem, m0, n0, 0, (p.k + BK - 1) / BK, acc);
+  lockstep_tile<DT, BM, BN, WM, WN, BK, STAGES, SPREAD, ILV, CW>(p, smem, m0, n0, 0, (p.k + BK - 1) / BK, acc);
 
   // every wave is done with the stages: reuse them as per-wave epilogue scratch
   wait_lgkmcnt<0>();
@@ -550,7 +556,7 @@ constexpr int kDeviceScope = 16;   // cache-policy bit sc1 of a buffer instructi
 // turns the tile into NaN instead of hanging the device.
 constexpr int kSkSpinLimit = 1 << 20;
 
-template <int DT, int EP, int BM, int BN, int WM, int WN, int BK, int STAGES, bool SPREAD, bool ILV>
+template <int DT, int EP, int BM, int BN, int WM, int WN, int BK, int STAGES, bool SPREAD, bool ILV, int CW>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_sk_kernel(Args p) {
   using C = DtlCfg<BM, BN, WM, WN, BK, STAGES>;
   using PL = PartialLayout<C::MB, C::NB>;
@@ -590,7 +596,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_sk_kernel(
   if (pa_nt > 0) {
     int tm, tn;
     raster(p, p.dp_tiles + pa_t, tm, tn);
-    lockstep_tile<DT, BM, BN, WM, WN, BK, STAGES, SPREAD, ILV>(p, smem, (int64_t)tm * BM, tn * BN, pa_kb, pa_nt, acc);
+    lockstep_tile<DT, BM, BN, WM, WN, BK, STAGES, SPREAD, ILV, CW>(p, smem, (int64_t)tm * BM, tn * BN, pa_kb, pa_nt, acc);
     // store the partial at device scope, then publish it once every wave's stores
     // have completed
     const __amdgpu_buffer_rsrc_t slot = rsrc(reinterpret_cast<char*>(p.sk_partial) + (size_t)r * slot_bytes);
@@ -613,7 +619,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_sk_kernel(
 
   int tm, tn;
   raster(p, pos, tm, tn);
-  lockstep_tile<DT, BM, BN, WM, WN, BK, STAGES, SPREAD, ILV>(p, smem, (int64_t)tm * BM, tn * BN, kb, nt, acc);
+  lockstep_tile<DT, BM, BN, WM, WN, BK, STAGES, SPREAD, ILV, CW>(p, smem, (int64_t)tm * BM, tn * BN, kb, nt, acc);
   if (split) {
     // the owner: add the partials of the runs that hold the rest of the tile
     const int t = pos - p.dp_tiles;

@@ -18,23 +18,25 @@ struct TileCfg {
   const char* loop;   // main loop of the direct-to-LDS kernels
 };
 
-enum CfgId { CFG_S = 0, CFG_M, CFG_L, CFG_LI, CFG_LS, CFG_W4, CFG_W4S, CFG_P, CFG_COUNT };
+enum CfgId { CFG_S = 0, CFG_M, CFG_L, CFG_LA, CFG_LI, CFG_LS, CFG_LSH, CFG_W4, CFG_W4S, CFG_P, CFG_COUNT };
 
 constexpr TileCfg kTiles[CFG_COUNT] = {
     {64, 64, 32, 32, 0, 2, "S", ""},
     {128, 128, 64, 64, 0, 2, "M", ""},
-    {256, 256, 128, 64, 64, 2, "L", "lockstep"},                      // 8 waves
+    {256, 256, 128, 64, 64, 2, "L", "lockstep, copies on waves 0-3"},   // 8 waves (default)
+    {256, 256, 128, 64, 64, 2, "LA", "lockstep"},
     {256, 256, 128, 64, 64, 2, "LI", "lockstep interleaved"},
     {256, 256, 128, 64, 32, 4, "LS", "lockstep spread interleaved"},
-    {256, 256, 128, 128, 64, 2, "W4", "lockstep"},                    // 4 waves of 128 x 128
+    {256, 256, 128, 64, 32, 4, "LSH", "lockstep spread interleaved, copies on waves 0-3"},
+    {256, 256, 128, 128, 64, 2, "W4", "lockstep"},                      // 4 waves of 128 x 128
     {256, 256, 128, 128, 32, 4, "W4S", "lockstep spread interleaved"},
-    {256, 256, 128, 64, 32, 4, "P", "ping-pong"},                     // 8 waves in two groups
+    {256, 256, 128, 64, 32, 4, "P", "ping-pong"},                       // 8 waves in two groups
 };
 
 inline bool cfg_is_dtl(int c) { return c >= CFG_L; }
 // Configurations whose kernel can split the last round's K loop (8-wave lockstep
 // loops; the 4-wave tile has no registers left for the partial sums).
-inline bool cfg_can_split(int c) { return c == CFG_L || c == CFG_LI || c == CFG_LS; }
+inline bool cfg_can_split(int c) { return c >= CFG_L && c <= CFG_LSH; }
 
 using LaunchFn = hipError_t (*)(const Args&, int grid, hipStream_t);
 
@@ -46,23 +48,26 @@ hipError_t launch_generic(const Args& a, int grid, hipStream_t s) {
   return hipLaunchKernel(fn, dim3(grid), dim3((BM / WM) * (BN / WN) * 64), params, 0, s);
 }
 
-enum Loop { LOCKSTEP = 0, LOCKSTEP_ILV = 1, LOCKSTEP_SPREAD_ILV = 2, PINGPONG = 3 };
+// Main loop of a configuration: the lockstep loop's switches (interleaved reads,
+// spread copies, copies on half the waves) or the ping-pong loop.
+enum Loop { LOCKSTEP = 0, LOCKSTEP_ILV = 1, LOCKSTEP_SPREAD_ILV = 2, PINGPONG = 3, LOCKSTEP_HALF = 4,
+            LOCKSTEP_SPREAD_ILV_HALF = 5 };
 
-// `grid` is the number of tiles; with a split tail (a.dp_tiles < tiles) the grid is
-// dp_tiles + sk_wgs workgroups of the split-tail kernel.
 template <int DT, int EP, int BM, int BN, int WM, int WN, int BK, int ST, int LOOP>
 hipError_t launch_dtl(const Args& a, int grid, hipStream_t s) {
   Args copy = a;
   void* params[] = {&copy};
   const void* fn;
-  constexpr bool SPREAD = LOOP == LOCKSTEP_SPREAD_ILV, ILV = LOOP != LOCKSTEP;
+  constexpr bool SPREAD = LOOP == LOCKSTEP_SPREAD_ILV || LOOP == LOCKSTEP_SPREAD_ILV_HALF;
+  constexpr bool ILV = LOOP == LOCKSTEP_ILV || SPREAD;
+  constexpr int CW = (LOOP == LOCKSTEP_HALF || LOOP == LOCKSTEP_SPREAD_ILV_HALF) ? (BM / WM) * (BN / WN) / 2 : 0;
   if constexpr (LOOP == PINGPONG) {
     fn = reinterpret_cast<const void*>(&gemm_pp_kernel<DT, EP, BM, BN, WM, WN, BK, ST>);
   } else {
-    fn = reinterpret_cast<const void*>(&gemm_dtl_kernel<DT, EP, BM, BN, WM, WN, BK, ST, SPREAD, ILV>);
+    fn = reinterpret_cast<const void*>(&gemm_dtl_kernel<DT, EP, BM, BN, WM, WN, BK, ST, SPREAD, ILV, CW>);
     if constexpr ((BM / WM) * (BN / WN) == 8) {   // the split tail exists for the 8-wave tiles
       if (a.dp_tiles < grid) {
-        fn = reinterpret_cast<const void*>(&gemm_sk_kernel<DT, EP, BM, BN, WM, WN, BK, ST, SPREAD, ILV>);
+        fn = reinterpret_cast<const void*>(&gemm_sk_kernel<DT, EP, BM, BN, WM, WN, BK, ST, SPREAD, ILV, CW>);
         grid = a.dp_tiles + a.sk_wgs;
       }
     }
@@ -82,9 +87,11 @@ LaunchFn pick_cfg(int cfg) {
   }
   if constexpr (DT != F32) {
     switch (cfg) {
-      case CFG_L: return &launch_dtl<DT, EP, 256, 256, 128, 64, 64, 2, LOCKSTEP>;
+      case CFG_L: return &launch_dtl<DT, EP, 256, 256, 128, 64, 64, 2, LOCKSTEP_HALF>;
+      case CFG_LA: return &launch_dtl<DT, EP, 256, 256, 128, 64, 64, 2, LOCKSTEP>;
       case CFG_LI: return &launch_dtl<DT, EP, 256, 256, 128, 64, 64, 2, LOCKSTEP_ILV>;
       case CFG_LS: return &launch_dtl<DT, EP, 256, 256, 128, 64, 32, 4, LOCKSTEP_SPREAD_ILV>;
+      case CFG_LSH: return &launch_dtl<DT, EP, 256, 256, 128, 64, 32, 4, LOCKSTEP_SPREAD_ILV_HALF>;
       case CFG_W4: return &launch_dtl<DT, EP, 256, 256, 128, 128, 64, 2, LOCKSTEP>;
       case CFG_W4S: return &launch_dtl<DT, EP, 256, 256, 128, 128, 32, 4, LOCKSTEP_SPREAD_ILV>;
       case CFG_P: return &launch_dtl<DT, EP, 256, 256, 128, 64, 32, 4, PINGPONG>;

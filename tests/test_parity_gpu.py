@@ -19,7 +19,7 @@ from tests.helpers import assert_bgrad, assert_close, assert_mask, tight_ratio, 
 pytestmark = pytest.mark.gpu
 
 DTS = ["f32", "f16", "bf16"]
-TILES = {"f32": ["S", "M"], "f16": ["S", "M", "L", "L-nosk", "LI", "LS", "W4", "W4S", "P"], "bf16": ["S", "M", "L", "L-nosk", "LI", "LS", "W4", "W4S", "P"]}
+TILES = {"f32": ["S", "M"], "f16": ["S", "M", "L", "L-nosk", "LA", "LI", "LS", "LSH", "W4", "W4S", "P"], "bf16": ["S", "M", "L", "L-nosk", "LA", "LI", "LS", "LSH", "W4", "W4S", "P"]}
 INT_SHAPES = [(1, 8, 8), (33, 136, 72), (200, 264, 200), (300, 520, 136)]
 
 
