@@ -38,6 +38,7 @@ struct ge_plan {
   int sk_units, sk_wgs;    // split tail: k-tiles per split workgroup, split workgroups
   float* sk_partial;       // split tail: one fp32 tile per split workgroup
   uint32_t* sk_flag;       // split tail: epoch of each published partial
+  int persist_grid = 0;    // persistent workgroups (0: one workgroup per tile)
   uint32_t epoch;          // execute counter, 1 .. 2^31 - 1
   std::string desc;
 };
@@ -196,6 +197,12 @@ ge_status_t gemm_epilog_plan(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt, ge
     }
   }
 
+  // ---- persistent kernel: one workgroup per compute unit walks the tiles ----
+  if (gek::cfg_can_persist(h->cfg) && h->dp_tiles == tiles && !env_off("GE_PERSIST")) {
+    const int kt = (int)cdiv(k, tc.bk);
+    if (k % tc.bk == 0 && kt % tc.stages == 0 && kt >= 2 * tc.stages) h->persist_grid = std::min(tiles, cus);
+  }
+
   // ---- workspace: [DRELU_BGRAD row sums | unfused T1, T2][split partials][split flags] ----
   const size_t es = elem_size(dt.d);
   size_t main_bytes = 0;
@@ -237,6 +244,7 @@ ge_status_t gemm_epilog_plan(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt, ge
             std::to_string(tc.bn / tc.wn) + (gek::cfg_is_dtl(h->cfg) ? " bk " + std::to_string(tc.bk) + " stages " +
                                                  std::to_string(tc.stages) + " " + tc.loop : std::string()) +
             " grid " + std::to_string(h->tiles_m * h->tiles_n) +
+            (h->persist_grid ? " on " + std::to_string(h->persist_grid) + " persistent workgroups" : std::string()) +
             (h->sk_wgs ? " (" + std::to_string(h->dp_tiles) + " whole + " + std::to_string(tiles - h->dp_tiles) +
                              " split over " + std::to_string(h->sk_wgs) + "x" + std::to_string(h->sk_units) +
                              " k-tiles)"
@@ -285,6 +293,7 @@ ge_status_t gemm_epilog_execute(ge_handle_t h, const void* A, const void* B, con
   a.sk_wgs = h->sk_wgs;
   a.sk_partial = h->sk_partial;
   a.sk_flag = h->sk_flag;
+  a.persist_grid = h->persist_grid;
   h->epoch = h->epoch % 0x7fffffffu + 1u;
   a.epoch = h->epoch;
   const int grid = h->tiles_m * h->tiles_n;

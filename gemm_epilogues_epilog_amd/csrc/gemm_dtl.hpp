@@ -225,6 +225,99 @@ __device__ __forceinline__ void epilogue_lds(const Args& p, f32x16 (&acc)[NB][MB
   }
 }
 
+// Epilogue of one 32-row block b of a wave's tile through 32 rows of scratch
+// (WN * 64 bytes), for kernels that keep the operand stages busy during the epilogue.
+// The block is finished and staged as in epilogue_lds, then stored as whole row
+// segments. `bv` is the bias of row 32 b + lane % 32 (unused by DRELU_BGRAD and NONE);
+// for DRELU_BGRAD, mw[a] is the mask word of column n0w + 32 a + lane % 32 of the
+// block's row group (0 outside the output).
+// Consecutive calls may share the scratch: the stores of a block consume every value
+// read back from it, so the next block's writes follow those reads.
+template <int DT, int EP, int MB, int NB, int WN>
+__device__ __forceinline__ void epilogue_block(const Args& p, const f32x16 (&acc)[NB][MB], int b, float bv,
+                                               const uint32_t (&mw)[NB], int64_t m0w, int n0w, int lane,
+                                               char* scratch) {
+  using T = Tr<DT>;
+  using L = EpiLayout<WN>;
+  const int64_t M = p.m;
+  const int N = p.n;
+  const int lrow = lane & 31, lhi = lane >> 5;
+  const int64_t mrow = m0w + 32 * b + lrow;
+  const bool mok = mrow < M;
+  const int64_t grp = (m0w + 32 * b) >> 5;
+  const int s = L::swz(lrow);
+
+  if constexpr (EP == DRELU_BGRAD) {
+    const uint32_t mybit = 1u << lrow;
+    float rowsum = 0.0f;
+#pragma unroll
+    for (int a = 0; a < NB; ++a) {
+      const uint32_t word = mw[a];
+      float dz[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int idx = 8 * (r >> 2) + (r & 3);
+        const uint32_t wl = __builtin_amdgcn_readlane(word, idx);
+        const uint32_t wh = __builtin_amdgcn_readlane(word, idx + 4);
+        const uint32_t wr = lhi ? wh : wl;
+        dz[r] = (wr & mybit) ? acc[a][b][r] : 0.0f;
+        rowsum += dz[r];
+      }
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int unit = (8 * a + 2 * g + lhi) ^ s;
+        const i32x2 v = {(int)T::pack2(dz[4 * g], dz[4 * g + 1]), (int)T::pack2(dz[4 * g + 2], dz[4 * g + 3])};
+        *reinterpret_cast<i32x2*>(scratch + lrow * L::RB + unit * 8) = v;
+      }
+    }
+    rowsum += __shfl_xor(rowsum, 32);
+    if (lhi == 0 && mok && n0w < N) p.partial[(int64_t)(n0w / WN) * M + mrow] = rowsum;
+  } else {
+#pragma unroll
+    for (int a = 0; a < NB; ++a) {
+      float pre[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) pre[r] = acc[a][b][r] + bv;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = activate<EP>(pre[4 * g + e]);
+        const int unit = (8 * a + 2 * g + lhi) ^ s;
+        const i32x2 v = {(int)T::pack2(y[0], y[1]), (int)T::pack2(y[2], y[3])};
+        *reinterpret_cast<i32x2*>(scratch + lrow * L::RB + unit * 8) = v;
+      }
+      if constexpr (EP == RELU_AUX_BIAS) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint64_t bal = __ballot(mok && pre[r] > 0.0f);
+          const int cl = 8 * (r >> 2) + (r & 3);
+          if (lane == cl) word = (uint32_t)bal;
+          if (lane == cl + 4) word = (uint32_t)(bal >> 32);
+        }
+        const int ncol = n0w + 32 * a + lane;
+        if (lane < 32 && grp * 32 < M && ncol < N) p.aux[grp * N + ncol] = word;
+      }
+    }
+  }
+
+  char* Dw = static_cast<char*>(p.D) + ((m0w + 32 * b) * (int64_t)N + n0w) * 2;
+  const __amdgpu_buffer_rsrc_t rd = rsrc(Dw);
+  const int c = lane % L::LPR;
+  const bool cok = n0w + 8 * c < N;
+#pragma unroll
+  for (int i = 0; i < 32 / L::RPI; ++i) {
+    const int row = i * L::RPI + lane / L::LPR;
+    const int sw = L::swz(row);
+    const i32x4 raw = *reinterpret_cast<const i32x4*>(scratch + row * L::RB + ((c ^ (sw >> 1)) << 4));
+    const i32x4 v = (sw & 1) ? i32x4{raw[2], raw[3], raw[0], raw[1]} : raw;
+    const bool ok = cok && (m0w + 32 * b + row < M);
+    const uint32_t off = ok ? (uint32_t)(((int64_t)row * N + 8 * c) * 2) : kOOB;
+    __builtin_amdgcn_raw_buffer_store_b128(v, rd, off, 0, 0);
+  }
+}
+
 // ---- operand copies and fragment reads shared by both main loops ---------------
 template <int DT, int BM, int BN, int WM, int WN, int BK, int STAGES, int CW = 0>
 struct Operands {
@@ -245,14 +338,30 @@ struct Operands {
 
   __device__ __forceinline__ Operands(const Args& p, int64_t m0, int n0, int w_, int wm, int wn, int lane,
                                       uint32_t lds) {
-    const int64_t M = p.m;
     N = p.n;
     K = p.k;
     w = w_;
     lds_base = lds;
+    retarget(p, m0, n0, lane);
+    // fragment read addresses (stage-relative)
+    const int lrow = lane & 31, lhi = lane >> 5;
+#pragma unroll
+    for (int s = 0; s < C::KSTEPS; ++s)
+      a_rd[s] = (wm * WM + lrow) * C::A_ROWB + (((2 * s + lhi) ^ swz_a<C::A_ROWB>(lrow)) << 4);
+    const int g = lane >> 4, i = lane & 15;
+    const int row = 8 * lhi + (i >> 2);   // + 16 s (+ 4 for the second read)
+#pragma unroll
+    for (int a = 0; a < NB; ++a) {
+      const int n = wn * WN + a * 32 + 16 * (g & 1) + 4 * (i & 3);
+      b_rd[a] = C::A_BYTES + row * C::B_ROWB + (((n >> 3) ^ swz_b(row)) << 4) + ((n & 7) << 1);
+    }
+  }
+
+  // Copy plan of the tile at (m0, n0): per-lane source offsets, constant over k.
+  __device__ __forceinline__ void retarget(const Args& p, int64_t m0, int n0, int lane) {
+    const int64_t M = p.m;
     Abase = static_cast<const char*>(p.A) + m0 * (int64_t)K * 2;
     Bbase = static_cast<const char*>(p.B) + (int64_t)n0 * 2;
-    // copy plan: per-lane source offsets (tile-relative, constant over k)
 #pragma unroll
     for (int j = 0; j < C::A_INST; ++j) {
       const int row = (w * C::A_INST + j) * C::A_RPI + lane / C::A_CHUNKS;
@@ -266,18 +375,6 @@ struct Operands {
       const int c = (lane % C::B_CHUNKS) ^ swz_b(row);
       b_row[j] = row;
       b_src[j] = (n0 + c * 8 < N) ? (uint32_t)(row * N * 2 + c * 16) : kOOB;
-    }
-    // fragment read addresses (stage-relative)
-    const int lrow = lane & 31, lhi = lane >> 5;
-#pragma unroll
-    for (int s = 0; s < C::KSTEPS; ++s)
-      a_rd[s] = (wm * WM + lrow) * C::A_ROWB + (((2 * s + lhi) ^ swz_a<C::A_ROWB>(lrow)) << 4);
-    const int g = lane >> 4, i = lane & 15;
-    const int row = 8 * lhi + (i >> 2);   // + 16 s (+ 4 for the second read)
-#pragma unroll
-    for (int a = 0; a < NB; ++a) {
-      const int n = wn * WN + a * 32 + 16 * (g & 1) + 4 * (i & 3);
-      b_rd[a] = C::A_BYTES + row * C::B_ROWB + (((n >> 3) ^ swz_b(row)) << 4) + ((n & 7) << 1);
     }
   }
 
@@ -521,6 +618,248 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_dtl_kernel
   wait_lgkmcnt<0>();
   barrier_only();
   epilogue_lds<DT, EP, C::MB, C::NB, WN>(p, acc, m0 + wm * WM, n0 + wn * WN, lane, smem + w * C::SCRATCH);
+}
+
+// Operand copies of the persistent kernel, for K a multiple of BK. A copy
+// instruction idx covers A_RPI rows of A (or B_RPI rows of B); its lanes' offsets
+// inside those rows depend only on the parity of idx (the chunk swizzles repeat with
+// period two in idx), so two offsets per operand stay in VGPRs and the row block goes
+// into the buffer descriptor's base. Rows of A past m fall outside the descriptor's
+// range and read as zero; B columns past n get an out-of-range offset.
+template <int BM, int BN, int WM, int WN, int BK, int STAGES, int CW>
+struct CopyPlan {
+  using C = DtlCfg<BM, BN, WM, WN, BK, STAGES, CW>;
+  static_assert(C::A_RPI % 8 == 0 || C::A_ROWB == 64, "A swizzle period");
+  static_assert(C::B_RPI % 2 == 0, "B swizzle period");
+
+  const char* Atile;   // A row m0 of the current tile
+  const char* Btile;   // B column n0 of the current tile
+  int64_t rows_left;   // rows of A from this wave's first copied row to m
+  int N, K, w;
+  uint32_t lds_base;
+  uint32_t a_lane[2], b_lane[2];
+
+  __device__ __forceinline__ CopyPlan(const Args& p, int w_, int lane, uint32_t lds) {
+    N = p.n;
+    K = p.k;
+    w = w_;
+    lds_base = lds;
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      const int row = par * C::A_RPI + lane / C::A_CHUNKS;
+      const int c = (lane % C::A_CHUNKS) ^ swz_a<C::A_ROWB>(row);
+      a_lane[par] = (uint32_t)((lane / C::A_CHUNKS) * K * 2 + c * 16);
+    }
+  }
+  __device__ __forceinline__ void retarget(const Args& p, int64_t m0, int n0, int lane) {
+    Atile = static_cast<const char*>(p.A) + m0 * (int64_t)K * 2;
+    Btile = static_cast<const char*>(p.B) + (int64_t)n0 * 2;
+    rows_left = p.m - m0 - (int64_t)w * C::A_INST * C::A_RPI;
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      const int row = par * C::B_RPI + lane / C::B_CHUNKS;
+      const int c = (lane % C::B_CHUNKS) ^ swz_b(row);
+      b_lane[par] = (n0 + c * 8 < N) ? (uint32_t)((lane / C::B_CHUNKS) * N * 2 + c * 16) : kOOB;
+    }
+  }
+  __device__ __forceinline__ void issue_tile(int kt, int stage) const {
+    const int64_t k0 = (int64_t)kt * BK;
+    const uint32_t sA = lds_base + stage * C::STAGE;
+    const uint32_t sB = sA + C::A_BYTES;
+#pragma unroll
+    for (int j = 0; j < C::A_INST; ++j) {
+      const int idx = w * C::A_INST + j;
+      const int par = ((C::A_INST % 2 == 0) ? j : idx) & 1;
+      const int64_t left = rows_left - (int64_t)j * C::A_RPI;
+      const uint32_t range = left >= C::A_RPI ? 0x7fffffffu : left > 0 ? (uint32_t)(left * K * 2) : 0u;
+      const char* base = Atile + k0 * 2 + (int64_t)idx * C::A_RPI * K * 2;
+      copy_to_lds_b128(make_srd(base, range), par ? a_lane[1] : a_lane[0], sA + idx * 1024);
+    }
+#pragma unroll
+    for (int j = 0; j < C::B_INST; ++j) {
+      const int idx = w * C::B_INST + j;
+      const int par = ((C::B_INST % 2 == 0) ? j : idx) & 1;
+      const char* base = Btile + (k0 + (int64_t)idx * C::B_RPI) * N * 2;
+      copy_to_lds_b128(make_srd(base, 0x7fffffffu), par ? b_lane[1] : b_lane[0], sB + idx * 1024);
+    }
+  }
+};
+
+// ---- persistent lockstep kernel --------------------------------------------------
+// gridDim.x workgroups (one per compute unit) walk the tile order with that stride.
+// The k loop runs on from one tile into the next: during a tile's last STAGES
+// k-tiles the copy waves fetch the next tile's first STAGES k-tiles, so its operand
+// latency hides behind the end of this tile and its epilogue. The epilogue works in
+// 32-row blocks through LDS of its own (32 rows per wave), leaving the stages to
+// those copies, and its stores drain while the next tile computes.
+// Schedule per k-tile as in lockstep_tile with interleaved reads, plus: the first PRE
+// MFMAs of a k-tile's last step are issued before its waits and barrier, so the
+// matrix cores stay busy while the waves meet there. Every wave runs every vmcnt
+// wait (the waves that copy nothing have only old stores and bias loads in flight),
+// which also lets the compiler treat the bias loads as done by the epilogue.
+// Requires K % BK == 0, KT % STAGES == 0 and KT >= 2 STAGES: k-tile t of every tile
+// sits in stage t % STAGES.
+template <int DT, int EP, int BM, int BN, int WM, int WN, int BK, int STAGES, int CW, int PRE>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_persist_kernel(Args p) {
+  using C = DtlCfg<BM, BN, WM, WN, BK, STAGES, CW>;
+  using O = Operands<DT, BM, BN, WM, WN, BK, STAGES, CW>;
+  using F = Frags<C::MB, C::NB>;
+  constexpr int MB = C::MB, NB = C::NB, KS = C::KSTEPS, NMMA = MB * NB;
+  constexpr int EPI_BYTES = 32 * WN * 2;   // epilogue rows of one wave
+  static_assert(DT == F16 || DT == BF16, "16-bit types only");
+  static_assert(C::LDS + C::NW * EPI_BYTES <= 160 * 1024, "LDS");
+  static_assert(KS % 2 == 0, "every k-tile starts on fragment buffer 0");
+  static_assert(PRE >= 0 && PRE < NMMA && F::PIECES <= NMMA, "MFMA slots");
+  __shared__ __attribute__((aligned(1024))) char smem[C::LDS + C::NW * EPI_BYTES];
+
+  const int T = p.tiles_m * p.tiles_n;
+  const int KT = (p.k + BK - 1) / BK;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = w % C::WAVES_M, wn = w / C::WAVES_M;
+  const bool copier = w < C::CW;
+  char* scratch = smem + C::LDS + w * EPI_BYTES;
+
+  int v = blockIdx.x;
+  int tm, tn;
+  raster(p, xcd_remap(v, T), tm, tn);
+  int64_t m0 = (int64_t)tm * BM;
+  int n0 = tn * BN;
+  const uint32_t lds = (uint32_t)(uintptr_t)(lds_void*)smem;
+  const O op(p, m0, n0, w, wm, wn, lane, lds);   // fragment reads only
+  CopyPlan<BM, BN, WM, WN, BK, STAGES, CW> cp(p, w, lane, lds);
+  cp.retarget(p, m0, n0, lane);
+
+  // Epilogue inputs, loaded when a tile starts and used in its epilogue (after the
+  // k loop's vmcnt waits, so the epilogue never waits on the copies in flight then):
+  // bias bits of rows 32 b + lane % 32 (converted in the epilogue), or for
+  // DRELU_BGRAD the mask words of columns 32 a + lane % 32 of row group b.
+  uint32_t bbits[MB];
+  uint32_t mwords[MB][NB];
+  auto load_bias = [&]() {
+    const int l = opaque(lane);
+#pragma unroll
+    for (int b = 0; b < MB; ++b) {
+      const int64_t row = m0 + wm * WM + 32 * b + (l & 31);
+      bbits[b] = 0;
+      if constexpr (EP != NONE && EP != DRELU_BGRAD) {
+        if (row < p.m) bbits[b] = load_vec_bits(p.bias, p.vec_dt, row);
+      }
+      if constexpr (EP == DRELU_BGRAD) {
+        const int64_t grp = (m0 + wm * WM + 32 * b) >> 5;
+#pragma unroll
+        for (int a = 0; a < NB; ++a) {
+          const int ncol = n0 + wn * WN + 32 * a + (l & 31);
+          mwords[b][a] = (grp * 32 < p.m && ncol < p.n) ? p.aux[grp * p.n + ncol] : 0u;
+        }
+      }
+    }
+  };
+  f32x16 acc[NB][MB];
+  auto zero_acc = [&]() {
+#pragma unroll
+    for (int a = 0; a < NB; ++a)
+#pragma unroll
+      for (int b = 0; b < MB; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+  };
+  F fr[2];
+  auto read_all = [&](const char* base, int s, F& f) {
+#pragma unroll
+    for (int q = 0; q < F::PIECES; ++q) read_piece(op, base, s, q, f);
+  };
+
+  // One k-tile in stage u. NEXT = false: copies of this tile's k-tile kt + STAGES;
+  // NEXT = true (the last STAGES k-tiles): copies of the next tile's k-tile
+  // kt + STAGES - KT when there is a next tile, and no reads past the last k-tile.
+  auto ktile = [&](auto next_tag, int kt, int u, bool more) {
+    constexpr bool NEXT = decltype(next_tag)::value;
+    const char* cur = smem + u * C::STAGE;
+    const char* nxt = smem + ((u + 1) % STAGES) * C::STAGE;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int buf = s & 1;
+      const bool last = s == KS - 1;
+      if (last) {
+#pragma unroll
+        for (int i = 0; i < PRE; ++i) {
+          const int a = i / MB, b = i % MB;
+          acc[a][b] = Tr<DT>::mma(fr[buf].bfrag(a), fr[buf].a[b], acc[a][b]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // publish k-tile kt+1 (this tile's or the next tile's first) and release stage u
+        wait_lgkmcnt<0>();
+        if constexpr (NEXT) wait_tiles<C::INST, STAGES - 2>(more ? STAGES - 2 : min(STAGES - 2, KT - 2 - kt));
+        else wait_vmcnt<(STAGES - 2) * C::INST>();
+        barrier_only();
+        if (copier) {
+          if constexpr (NEXT) {
+            if (more) cp.issue_tile(kt + STAGES - KT, u);
+          } else {
+            cp.issue_tile(kt + STAGES, u);
+          }
+        }
+      }
+      const char* rbase = last ? nxt : cur;
+      const int rs = last ? 0 : s + 1;
+      const bool reads = !NEXT || !last || kt + 1 < KT;
+      const int i0 = last ? PRE : 0;
+      const int per = (F::PIECES + NMMA - i0 - 1) / (NMMA - i0);
+#pragma unroll
+      for (int i = i0; i < NMMA; ++i) {
+        const int a = i / MB, b = i % MB;
+        acc[a][b] = Tr<DT>::mma(fr[buf].bfrag(a), fr[buf].a[b], acc[a][b]);
+#pragma unroll
+        for (int e = 0; e < per; ++e) {
+          const int q = (i - i0) * per + e;
+          if (q < F::PIECES && reads) read_piece(op, rbase, rs, q, fr[buf ^ 1]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // prologue: the first tile's first STAGES k-tiles
+  load_bias();
+  zero_acc();
+  if (copier) {
+#pragma unroll
+    for (int t = 0; t < STAGES; ++t) cp.issue_tile(t, t);
+  }
+  wait_vmcnt<0>();
+  barrier_only();
+  read_all(smem, 0, fr[0]);
+
+  for (;;) {
+    const int vn = v + (int)gridDim.x;
+    const bool more = vn < T;
+    int tmn = 0, tnn = 0;
+    if (more) raster(p, xcd_remap(vn, T), tmn, tnn);
+    int kt = 0;
+    do {
+#pragma unroll
+      for (int u = 0; u < STAGES; ++u) ktile(std::false_type{}, kt + u, u, more);
+      kt += STAGES;
+    } while (kt < KT - STAGES);
+    if (more) cp.retarget(p, (int64_t)tmn * BM, tnn * BN, opaque(lane));
+#pragma unroll
+    for (int u = 0; u < STAGES; ++u) ktile(std::true_type{}, KT - STAGES + u, u, more);
+
+    const int elane = opaque(lane);   // the epilogue's lane arithmetic stays out of the k loop
+#pragma unroll
+    for (int b = 0; b < MB; ++b)
+      epilogue_block<DT, EP, MB, NB, WN>(p, acc, b, vec_value(bbits[b], p.vec_dt), mwords[b], m0 + wm * WM,
+                                         n0 + wn * WN, elane, scratch);
+    if (!more) break;
+    v = vn;
+    m0 = (int64_t)tmn * BM;
+    n0 = tnn * BN;
+    load_bias();
+    zero_acc();
+    read_all(smem, 0, fr[0]);   // k-tile 0 of the new tile, published by the last barrier
+  }
 }
 
 // ---- split tail of the tile grid -------------------------------------------------

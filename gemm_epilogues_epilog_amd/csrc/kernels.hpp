@@ -72,6 +72,9 @@ struct Args {
   uint32_t epoch;     // changes every execute; marks this execute's partials
   float* sk_partial;  // per split workgroup: one tile of fp32 partial accumulators
   uint32_t* sk_flag;  // per split workgroup: epoch of its published partial
+  // Persistent kernels: workgroups launched (one per compute unit), each walking the
+  // tile order with that stride; 0 when the plan launches one workgroup per tile.
+  int32_t persist_grid;
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base) {
@@ -93,18 +96,26 @@ __device__ __forceinline__ void wait_lgkmcnt() {
   __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (N << 8));
 }
 
+// v, through an empty volatile asm: the compiler cannot see that the result equals
+// v, so values derived from it are computed where they are used instead of being
+// hoisted out of a loop and kept live (or spilled) across it.
+__device__ __forceinline__ int opaque(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 // Workgroup barrier that is also a compiler barrier for memory operations. It does
 // not wait for outstanding memory operations: callers wait explicitly first.
 __device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
 
-// Buffer descriptor (V#) as four SGPR values: base, no stride, 2^31 - 1 bytes of
-// range, 32-bit data format. Offsets at or above kOOB are out of range.
-__device__ __forceinline__ i32x4 make_srd(const void* base) {
+// Buffer descriptor (V#) as four SGPR values: base, no stride, `range` bytes (2^31 - 1
+// by default), 32-bit data format. Offsets at or above kOOB are out of range.
+__device__ __forceinline__ i32x4 make_srd(const void* base, uint32_t range = 0x7fffffffu) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
   i32x4 r;
   r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
   r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
-  r[2] = 0x7fffffff;
+  r[2] = __builtin_amdgcn_readfirstlane((int)range);
   r[3] = kBufDword3;
   return r;
 }
@@ -114,11 +125,13 @@ __device__ __forceinline__ i32x4 make_srd(const void* base) {
 // Issued as inline assembly so that the compiler does not treat the copy as a write
 // that every later LDS read must wait for; the caller orders it with wait_vmcnt and
 // barrier_only. Loads complete in issue order, so the compiler's own vmcnt waits
-// stay correct with these extra loads in flight (they can only wait longer).
+// stay correct with these extra loads in flight (they can only wait longer). `lds`
+// must be uniform; readfirstlane keeps it in an SGPR where the compiler cannot prove
+// that by itself.
 __device__ __forceinline__ void copy_to_lds_b128(const i32x4& srd, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :
-               : "v"(voff), "s"(srd), "s"(lds)
+               : "v"(voff), "s"(srd), "s"(__builtin_amdgcn_readfirstlane(lds))
                : "memory", "m0");
 }
 
@@ -136,8 +149,9 @@ __device__ __forceinline__ void raster(const Args& p, int pos, int& tm, int& tn)
   const int g = pos / gsz, first_m = g * p.group_m;
   const int rows = min(p.tiles_m - first_m, p.group_m);
   const int in = pos - g * gsz;
-  tm = first_m + in % rows;
-  tn = in / rows;
+  // the divisions run on the vector unit: pin the (uniform) results to SGPRs
+  tm = __builtin_amdgcn_readfirstlane(first_m + in % rows);
+  tn = __builtin_amdgcn_readfirstlane(in / rows);
 }
 
 // Workgroup id -> (m-tile, n-tile) when every workgroup computes one whole tile.
@@ -192,6 +206,19 @@ template <> struct Tr<F32> {
     return c;
   }
 };
+
+// Element i of a bias vector as raw bits (fp32 bits, or the 16-bit value
+// zero-extended), and their value: split so that a load can be issued long before
+// its value is needed without the conversion forcing an early wait.
+__device__ __forceinline__ uint32_t load_vec_bits(const void* p, int vec_dt, int64_t i) {
+  if (vec_dt == F32) return static_cast<const uint32_t*>(p)[i];
+  return static_cast<const uint16_t*>(p)[i];
+}
+__device__ __forceinline__ float vec_value(uint32_t bits, int vec_dt) {
+  if (vec_dt == F32) return __uint_as_float(bits);
+  if (vec_dt == F16) return Tr<F16>::widen((uint16_t)bits);
+  return Tr<BF16>::widen((uint16_t)bits);
+}
 
 __device__ __forceinline__ float load_vec(const void* p, int vec_dt, int64_t i) {
   if (vec_dt == F32) return static_cast<const float*>(p)[i];

@@ -18,12 +18,13 @@ struct TileCfg {
   const char* loop;   // main loop of the direct-to-LDS kernels
 };
 
-enum CfgId { CFG_S = 0, CFG_M, CFG_L, CFG_LA, CFG_LI, CFG_LS, CFG_LSH, CFG_W4, CFG_W4S, CFG_P, CFG_COUNT };
+enum CfgId { CFG_S = 0, CFG_M, CFG_L, CFG_LH, CFG_LA, CFG_LI, CFG_LS, CFG_LSH, CFG_W4, CFG_W4S, CFG_P, CFG_COUNT };
 
 constexpr TileCfg kTiles[CFG_COUNT] = {
     {64, 64, 32, 32, 0, 2, "S", ""},
     {128, 128, 64, 64, 0, 2, "M", ""},
-    {256, 256, 128, 64, 64, 2, "L", "lockstep, copies on waves 0-3"},   // 8 waves (default)
+    {256, 256, 128, 64, 64, 2, "L", "persistent lockstep interleaved, copies on waves 0-3"},   // 8 waves (default)
+    {256, 256, 128, 64, 64, 2, "LH", "lockstep, copies on waves 0-3"},
     {256, 256, 128, 64, 64, 2, "LA", "lockstep"},
     {256, 256, 128, 64, 64, 2, "LI", "lockstep interleaved"},
     {256, 256, 128, 64, 32, 4, "LS", "lockstep spread interleaved"},
@@ -38,6 +39,10 @@ inline bool cfg_is_dtl(int c) { return c >= CFG_L; }
 // loops; the 4-wave tile has no registers left for the partial sums).
 inline bool cfg_can_split(int c) { return c >= CFG_L && c <= CFG_LSH; }
 
+// Configurations with a persistent kernel, used when the tile grid is not split and
+// k spans a whole number of stage rings, at least two.
+inline bool cfg_can_persist(int c) { return c == CFG_L; }
+
 using LaunchFn = hipError_t (*)(const Args&, int grid, hipStream_t);
 
 template <int DT, int EP, int BM, int BN, int WM, int WN>
@@ -51,7 +56,10 @@ hipError_t launch_generic(const Args& a, int grid, hipStream_t s) {
 // Main loop of a configuration: the lockstep loop's switches (interleaved reads,
 // spread copies, copies on half the waves) or the ping-pong loop.
 enum Loop { LOCKSTEP = 0, LOCKSTEP_ILV = 1, LOCKSTEP_SPREAD_ILV = 2, PINGPONG = 3, LOCKSTEP_HALF = 4,
-            LOCKSTEP_SPREAD_ILV_HALF = 5 };
+            LOCKSTEP_SPREAD_ILV_HALF = 5, PERSIST = 6 };
+
+// MFMAs of a k-tile's last step that the persistent loop issues before its barrier.
+constexpr int kPersistPre = 4;
 
 template <int DT, int EP, int BM, int BN, int WM, int WN, int BK, int ST, int LOOP>
 hipError_t launch_dtl(const Args& a, int grid, hipStream_t s) {
@@ -59,8 +67,9 @@ hipError_t launch_dtl(const Args& a, int grid, hipStream_t s) {
   void* params[] = {&copy};
   const void* fn;
   constexpr bool SPREAD = LOOP == LOCKSTEP_SPREAD_ILV || LOOP == LOCKSTEP_SPREAD_ILV_HALF;
-  constexpr bool ILV = LOOP == LOCKSTEP_ILV || SPREAD;
-  constexpr int CW = (LOOP == LOCKSTEP_HALF || LOOP == LOCKSTEP_SPREAD_ILV_HALF) ? (BM / WM) * (BN / WN) / 2 : 0;
+  constexpr bool ILV = LOOP == LOCKSTEP_ILV || LOOP == PERSIST || SPREAD;
+  constexpr int CW = (LOOP == LOCKSTEP_HALF || LOOP == LOCKSTEP_SPREAD_ILV_HALF || LOOP == PERSIST)
+                         ? (BM / WM) * (BN / WN) / 2 : 0;
   if constexpr (LOOP == PINGPONG) {
     fn = reinterpret_cast<const void*>(&gemm_pp_kernel<DT, EP, BM, BN, WM, WN, BK, ST>);
   } else {
@@ -69,6 +78,12 @@ hipError_t launch_dtl(const Args& a, int grid, hipStream_t s) {
       if (a.dp_tiles < grid) {
         fn = reinterpret_cast<const void*>(&gemm_sk_kernel<DT, EP, BM, BN, WM, WN, BK, ST, SPREAD, ILV, CW>);
         grid = a.dp_tiles + a.sk_wgs;
+      }
+    }
+    if constexpr (LOOP == PERSIST) {
+      if (a.dp_tiles == grid && a.persist_grid > 0) {
+        fn = reinterpret_cast<const void*>(&gemm_persist_kernel<DT, EP, BM, BN, WM, WN, BK, ST, CW, kPersistPre>);
+        grid = a.persist_grid;
       }
     }
   }
@@ -87,7 +102,8 @@ LaunchFn pick_cfg(int cfg) {
   }
   if constexpr (DT != F32) {
     switch (cfg) {
-      case CFG_L: return &launch_dtl<DT, EP, 256, 256, 128, 64, 64, 2, LOCKSTEP_HALF>;
+      case CFG_L: return &launch_dtl<DT, EP, 256, 256, 128, 64, 64, 2, PERSIST>;
+      case CFG_LH: return &launch_dtl<DT, EP, 256, 256, 128, 64, 64, 2, LOCKSTEP_HALF>;
       case CFG_LA: return &launch_dtl<DT, EP, 256, 256, 128, 64, 64, 2, LOCKSTEP>;
       case CFG_LI: return &launch_dtl<DT, EP, 256, 256, 128, 64, 64, 2, LOCKSTEP_ILV>;
       case CFG_LS: return &launch_dtl<DT, EP, 256, 256, 128, 64, 32, 4, LOCKSTEP_SPREAD_ILV>;

@@ -113,9 +113,10 @@ typedef enum {
  *   out     : receives the handle; untouched on error.
  * Allocates the workspace on the current device: the per-tile bias-gradient
  * partial sums for DRELU_BGRAD, T1 and T2 for RELU_BIAS_UNFUSED, nothing otherwise.
- * Environment (tuning experiments): GE_TILE=S|M|L|LA|LI|LS|LSH|W4|W4S|P forces a tile configuration;
+ * Environment (tuning experiments): GE_TILE=S|M|L|LH|LA|LI|LS|LSH|W4|W4S|P forces a tile configuration;
  * GE_GROUP_M=g (1..1024) sets how many m-tiles share one group of the tile order;
- * GE_STREAMK=0 keeps a sparse last round of tiles whole instead of splitting its k loop.
+ * GE_STREAMK=0 keeps a sparse last round of tiles whole instead of splitting its k loop;
+ * GE_PERSIST=0 launches one workgroup per tile instead of the persistent kernel.
  */
 ge_status_t gemm_epilog_plan(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt, ge_epilog_t ep,
                              ge_handle_t* out);

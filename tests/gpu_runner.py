@@ -32,6 +32,21 @@ def tile_env(tile):
                 os.environ[k] = v
 
 
+@contextmanager
+def env(values):
+    """Set environment variables for the plans made inside."""
+    saved = {k: os.environ.get(k) for k in values}
+    os.environ.update(values)
+    try:
+        yield
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+
+
 def guarded(numel, dtype, fill):
     buf = torch.full((numel + 2 * GUARD,), fill, dtype=dtype, device="cuda")
     return buf, buf[GUARD:GUARD + numel]

@@ -19,7 +19,8 @@ from tests.helpers import assert_bgrad, assert_close, assert_mask, tight_ratio, 
 pytestmark = pytest.mark.gpu
 
 DTS = ["f32", "f16", "bf16"]
-TILES = {"f32": ["S", "M"], "f16": ["S", "M", "L", "L-nosk", "LA", "LI", "LS", "LSH", "W4", "W4S", "P"], "bf16": ["S", "M", "L", "L-nosk", "LA", "LI", "LS", "LSH", "W4", "W4S", "P"]}
+TILES16 = ["S", "M", "L", "L-nosk", "LH", "LA", "LI", "LS", "LSH", "W4", "W4S", "P"]
+TILES = {"f32": ["S", "M"], "f16": TILES16, "bf16": TILES16}
 INT_SHAPES = [(1, 8, 8), (33, 136, 72), (200, 264, 200), (300, 520, 136)]
 
 
@@ -183,10 +184,74 @@ def test_split_tail_plan_and_determinism(gpu):
     assert "split" in g1["desc"]
     g2 = R.run(gpu, "RELU_AUX_BIAS", "f16", A, B, bias)
     assert torch.equal(g1["D_dev"], g2["D_dev"]) and torch.equal(g1["mask_dev"], g2["mask_dev"])
-    g0 = R.run(gpu, "RELU_AUX_BIAS", "f16", A, B, bias, tile="L-nosk")
+    g0 = R.run(gpu, "RELU_AUX_BIAS", "f16", A, B, bias, tile="LH-nosk")
     assert "split" not in g0["desc"]
     assert_close(g1["D"], g0["D"], "f16", "split vs unsplit")
     rows = np.r_[0:32, 4096:4352]   # the first row group and the split tiles' rows
     o = oracle.gemm_epilog(to_np(A)[rows], to_np(B), "RELU_AUX_BIAS", bias=to_np(bias)[rows], want_pre=True)
     assert_close(g1["D"][rows], o["D"], "f16", "split vs oracle")
 
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_persistent_tiles_integer_exact(gpu, dt):
+    """The persistent kernel (one workgroup per compute unit walking the tile order,
+    k loop running on from one tile into the next): 528 tiles of a ragged 4000 x 8200
+    output on 256 workgroups, so most workgroups finish three tiles and every tile
+    after a workgroup's first starts from operands fetched during the previous one.
+    Integer inputs make every epilogue bit-exact against the oracle."""
+    m, n, k = 4000, 8200, 256
+    print(f"[case] persistent integer {dt} m={m} n={n} k={k}", flush=True)
+    A, B, bias, A2, B2 = inputs.integer_case(m, n, k, dt)
+    a, b, c = to_np(A), to_np(B), to_np(bias)
+    for ep in ("NONE", "BIAS", "RELU_BIAS"):
+        g = R.run(gpu, ep, dt, A, B, bias, tile="L-nosk")
+        assert "persistent workgroups" in g["desc"], g["desc"]
+        o = oracle.gemm_epilog(a, b, ep, bias=c, ab=dt)
+        assert np.array_equal(g["D"].view(np.uint8), o["D"].view(np.uint8)), f"{ep} {g['desc']}"
+    g = R.run(gpu, "RELU_AUX_BIAS", dt, A, B, bias, tile="L-nosk")
+    o = oracle.gemm_epilog(a, b, "RELU_AUX_BIAS", bias=c, ab=dt)
+    assert np.array_equal(g["D"].view(np.uint8), o["D"].view(np.uint8)), g["desc"]
+    assert np.array_equal(g["mask"].view(np.uint32), o["mask"]), g["desc"]
+    mask = torch.from_numpy(o["mask"].view(np.int32).copy())
+    gb = R.run(gpu, "DRELU_BGRAD", dt, A2, B2, mask=mask, tile="L-nosk")
+    assert "persistent workgroups" in gb["desc"], gb["desc"]
+    ob = oracle.gemm_epilog(to_np(A2), to_np(B2), "DRELU_BGRAD", mask=o["mask"], ab=dt)
+    assert np.array_equal(gb["D"].view(np.uint8), ob["D"].view(np.uint8)), gb["desc"]
+    assert np.array_equal(gb["bgrad"].view(np.uint8), ob["bgrad"].view(np.uint8)), gb["desc"]
+
+
+def test_persistent_plan_conditions(gpu):
+    """The persistent kernel runs only when k is a multiple of 64 spanning an even
+    number (at least 4) of k-tiles and the tile grid is not split; otherwise the same
+    configuration launches one workgroup per tile."""
+    ge = gpu
+    cases = [((4096, 11008, 4096), True), ((4096, 11008, 4160), False), ((4096, 11008, 4040), False),
+             ((4096, 11008, 128), False), ((4352, 4096, 1024), False)]
+    with R.tile_env("L"):
+        for (m, n, k), want in cases:
+            h = ge.gemm_epilog_plan(m, n, k, ("f16", "f16", "f16"), "RELU_BIAS")
+            try:
+                d = ge.gemm_epilog_describe(h)
+                assert ("persistent workgroups" in d) == want, (m, n, k, d)
+            finally:
+                ge.gemm_epilog_free(h)
+
+
+def test_persistent_random_matches_one_tile_per_workgroup(gpu):
+    """Normal inputs at 2048 x 11008 x 512 (344 tiles): the persistent kernel and the
+    one-workgroup-per-tile kernel of the same loop agree bit for bit (same k order per
+    tile), repeat bit for bit, and match the oracle on sampled rows."""
+    m, n, k = 2048, 11008, 512
+    A, B, bias, _, _ = inputs.small_case(m, n, k, "f16", std=k ** -0.5, std_bias=0.02)
+    gp = R.run(gpu, "RELU_AUX_BIAS", "f16", A, B, bias, tile="L-nosk", repeat=2)
+    assert "persistent workgroups" in gp["desc"], gp["desc"]
+    gq = R.run(gpu, "RELU_AUX_BIAS", "f16", A, B, bias, tile="L-nosk")
+    assert torch.equal(gp["D_dev"], gq["D_dev"]) and torch.equal(gp["mask_dev"], gq["mask_dev"])
+    with R.env({"GE_PERSIST": "0"}):
+        g1 = R.run(gpu, "RELU_AUX_BIAS", "f16", A, B, bias, tile="L-nosk")
+    assert "persistent workgroups" not in g1["desc"], g1["desc"]
+    assert torch.equal(gp["D_dev"], g1["D_dev"]) and torch.equal(gp["mask_dev"], g1["mask_dev"])
+    rows = np.r_[0:32, 992:1056, 2016:2048]
+    o = oracle.gemm_epilog(to_np(A)[rows], to_np(B), "RELU_AUX_BIAS", bias=to_np(bias)[rows], want_pre=True)
+    assert_close(gp["D"][rows], o["D"], "f16", "persistent vs oracle")
