@@ -213,15 +213,26 @@ __device__ __forceinline__ void epilogue_lds(const Args& p, f32x16 (&acc)[NB][MB
   const __amdgpu_buffer_rsrc_t rd = rsrc(Dw);
   const int c = lane % L::LPR;
   const bool cok = n0w + 8 * c < N;
+  // read-backs in groups of four ahead of their stores: the compiler does not move an
+  // LDS read past a buffer store, so one read per store would serialise the round trips
+  constexpr int G = 4;
+  static_assert((WM / L::RPI) % G == 0, "read-back groups");
 #pragma unroll
-  for (int i = 0; i < WM / L::RPI; ++i) {
-    const int row = i * L::RPI + lane / L::LPR;
-    const int s = L::swz(row);
-    const i32x4 raw = *reinterpret_cast<const i32x4*>(scratch + row * L::RB + ((c ^ (s >> 1)) << 4));
-    const i32x4 v = (s & 1) ? i32x4{raw[2], raw[3], raw[0], raw[1]} : raw;
-    const bool ok = cok && (m0w + row < M);
-    const uint32_t off = ok ? (uint32_t)(((int64_t)row * N + 8 * c) * 2) : kOOB;
-    __builtin_amdgcn_raw_buffer_store_b128(v, rd, off, 0, 0);
+  for (int i0 = 0; i0 < WM / L::RPI; i0 += G) {
+    i32x4 raw[G];
+#pragma unroll
+    for (int e = 0; e < G; ++e) {
+      const int row = (i0 + e) * L::RPI + lane / L::LPR;
+      raw[e] = *reinterpret_cast<const i32x4*>(scratch + row * L::RB + ((c ^ (L::swz(row) >> 1)) << 4));
+    }
+#pragma unroll
+    for (int e = 0; e < G; ++e) {
+      const int row = (i0 + e) * L::RPI + lane / L::LPR;
+      const i32x4 v = (L::swz(row) & 1) ? i32x4{raw[e][2], raw[e][3], raw[e][0], raw[e][1]} : raw[e];
+      const bool ok = cok && (m0w + row < M);
+      const uint32_t off = ok ? (uint32_t)(((int64_t)row * N + 8 * c) * 2) : kOOB;
+      __builtin_amdgcn_raw_buffer_store_b128(v, rd, off, 0, 0);
+    }
   }
 }
 
@@ -302,16 +313,23 @@ __device__ __forceinline__ void epilogue_block(const Args& p, const f32x16 (&acc
     }
   }
 
+  // all read-backs first, then the stores: the compiler does not move an LDS read
+  // past a buffer store, so interleaving them would serialise the LDS round trips
   char* Dw = static_cast<char*>(p.D) + ((m0w + 32 * b) * (int64_t)N + n0w) * 2;
   const __amdgpu_buffer_rsrc_t rd = rsrc(Dw);
   const int c = lane % L::LPR;
   const bool cok = n0w + 8 * c < N;
+  constexpr int NR = 32 / L::RPI;
+  i32x4 raw[NR];
 #pragma unroll
-  for (int i = 0; i < 32 / L::RPI; ++i) {
+  for (int i = 0; i < NR; ++i) {
     const int row = i * L::RPI + lane / L::LPR;
-    const int sw = L::swz(row);
-    const i32x4 raw = *reinterpret_cast<const i32x4*>(scratch + row * L::RB + ((c ^ (sw >> 1)) << 4));
-    const i32x4 v = (sw & 1) ? i32x4{raw[2], raw[3], raw[0], raw[1]} : raw;
+    raw[i] = *reinterpret_cast<const i32x4*>(scratch + row * L::RB + ((c ^ (L::swz(row) >> 1)) << 4));
+  }
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    const int row = i * L::RPI + lane / L::LPR;
+    const i32x4 v = (L::swz(row) & 1) ? i32x4{raw[i][2], raw[i][3], raw[i][0], raw[i][1]} : raw[i];
     const bool ok = cok && (m0w + 32 * b + row < M);
     const uint32_t off = ok ? (uint32_t)(((int64_t)row * N + 8 * c) * 2) : kOOB;
     __builtin_amdgcn_raw_buffer_store_b128(v, rd, off, 0, 0);

@@ -215,9 +215,9 @@ __device__ __forceinline__ uint32_t load_vec_bits(const void* p, int vec_dt, int
   return static_cast<const uint16_t*>(p)[i];
 }
 __device__ __forceinline__ float vec_value(uint32_t bits, int vec_dt) {
-  if (vec_dt == F32) return __uint_as_float(bits);
-  if (vec_dt == F16) return Tr<F16>::widen((uint16_t)bits);
-  return Tr<BF16>::widen((uint16_t)bits);
+  // selects, not branches: this sits between the blocks of an epilogue
+  const float f = __uint_as_float(bits), h = Tr<F16>::widen((uint16_t)bits), g = Tr<BF16>::widen((uint16_t)bits);
+  return vec_dt == F32 ? f : vec_dt == F16 ? h : g;
 }
 
 __device__ __forceinline__ float load_vec(const void* p, int vec_dt, int64_t i) {
