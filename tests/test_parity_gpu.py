@@ -21,7 +21,8 @@ pytestmark = pytest.mark.gpu
 DTS = ["f32", "f16", "bf16"]
 TILES16 = ["S", "M", "L", "L-nosk", "LH", "LA", "LI", "LS", "LSH", "W4", "W4S", "P"]
 TILES = {"f32": ["S", "M"], "f16": TILES16, "bf16": TILES16}
-INT_SHAPES = [(1, 8, 8), (33, 136, 72), (200, 264, 200), (300, 520, 136)]
+# the last shape (k a multiple of 64 over 4 k-tiles) runs the persistent kernel in "L"
+INT_SHAPES = [(1, 8, 8), (33, 136, 72), (200, 264, 200), (300, 520, 136), (300, 520, 256)]
 
 
 def cases_int():
@@ -53,9 +54,10 @@ def test_integer_exact_all_epilogues(gpu, dt, tile, shape):
 
 
 @pytest.mark.parametrize("dt", DTS)
-def test_integer_exact_fp32_vectors(gpu, dt):
+@pytest.mark.parametrize("shape", [(96, 72, 40), (300, 264, 256)])
+def test_integer_exact_fp32_vectors(gpu, dt, shape):
     # bias and bgrad in fp32 with 16-bit matrices (and fp32 with fp32)
-    m, n, k = 96, 72, 40
+    m, n, k = shape
     A, B, bias, A2, B2 = inputs.integer_case(m, n, k, dt, vec="f32")
     o = oracle.gemm_epilog(to_np(A), to_np(B), "RELU_AUX_BIAS", bias=to_np(bias), ab=dt, vec="f32")
     g = R.run(gpu, "RELU_AUX_BIAS", dt, A, B, bias, vec="f32")
