@@ -7,8 +7,8 @@ metric is 2mnk / time in TFLOP/s and its fraction of the dense fp16 MFMA peak.
 Also measured (reported under "variants", not in "value"): the unfused three-kernel
 chain on the same inputs, bf16 GELU_BIAS, RELU_AUX_BIAS, the bf16 8192^3
 RELU_AUX_BIAS + DRELU_BGRAD pair and the large (65536,16384)x(16384,8192) fp16 shape
-with and without the mask. The CPU oracle is timed on a bounded sample of rows of
-the headline workload on the host cores.
+with and without the mask. The CPU oracle is timed on the headline workload on the
+host cores, in whole passes for a bounded time (about 12 s).
 
 Prints one JSON line (the last line of stdout).
 """
