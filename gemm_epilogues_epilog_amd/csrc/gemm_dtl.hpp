@@ -1,7 +1,8 @@
 // Fused kernel for fp16 / bf16 with direct-to-LDS operand copies (gfx950).
 //
-// Operands. Per k-tile (BK values of k) every wave issues buffer loads that write
-// straight into LDS (no register staging, no VALU work on the copy path):
+// Operands. Per k-tile (BK values of k) the copying waves (all, or one per SIMD)
+// issue buffer loads that write straight into LDS (no register staging, no VALU work
+// on the copy path):
 //   A tile: BM rows of 2 BK bytes (row = m, k contiguous), the 16-byte chunks of
 //           each row XOR-swizzled by swz_a(row).
 //   B tile: BK rows of 2 BN bytes (row = k, n contiguous, as B is stored), the
@@ -14,15 +15,17 @@
 // layout (k contiguous per lane) produced from the n-contiguous tile.
 //
 // Pipeline. STAGES LDS stages form a ring. The copies are inline assembly, ordered
-// by hand with vmcnt / lgkmcnt waits and workgroup barriers (the two main loops
-// below describe their schedules): the compiler would otherwise make every LDS read
-// wait for every copy still in flight.
+// by hand with vmcnt / lgkmcnt waits and workgroup barriers (the lockstep, persistent
+// and ping-pong loops below describe their schedules): the compiler would otherwise
+// make every LDS read wait for every copy still in flight.
 //
-// Epilogue. After the last k-tile the stage memory becomes per-wave scratch: each
-// wave writes its finished (activated, rounded) WM x WN tile there with a swizzle
-// that keeps the 8-byte writes conflict-free, reads it back as 16-byte row pieces
-// and stores whole 2 WN-byte row segments of D, so every store instruction covers
-// full cache lines instead of 32 rows x 16 bytes.
+// Epilogue. Each wave writes its finished (activated, rounded) accumulators to LDS
+// scratch with a swizzle that keeps the 8-byte writes conflict-free, reads them back
+// as 16-byte row pieces and stores whole 2 WN-byte row segments of D, so every store
+// instruction covers full cache lines instead of 32 rows x 16 bytes. One-tile kernels
+// use the freed stage memory for the whole WM x WN tile (epilogue_lds); the
+// persistent kernel keeps 32 rows per wave of its own, block by block
+// (epilogue_block), since the stages then hold the next tile's operands.
 #pragma once
 
 #include <type_traits>
@@ -336,7 +339,7 @@ __device__ __forceinline__ void epilogue_block(const Args& p, const f32x16 (&acc
   }
 }
 
-// ---- operand copies and fragment reads shared by both main loops ---------------
+// ---- operand copies and fragment reads shared by the main loops -----------------
 template <int DT, int BM, int BN, int WM, int WN, int BK, int STAGES, int CW = 0>
 struct Operands {
   using C = DtlCfg<BM, BN, WM, WN, BK, STAGES, CW>;
