@@ -151,10 +151,7 @@ __device__ __forceinline__ void epilogue_lds(const Args& p, f32x16 (&acc)[NB][MB
         float dz[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int idx = 8 * (r >> 2) + (r & 3);
-          const uint32_t wl = __builtin_amdgcn_readlane(word, idx);
-          const uint32_t wh = __builtin_amdgcn_readlane(word, idx + 4);
-          const uint32_t wr = lhi ? wh : wl;
+          const uint32_t wr = mask_word_of_reg(word, r, lane);
           dz[r] = (wr & mybit) ? acc[a][b][r] : 0.0f;
           rowsum += dz[r];
         }
@@ -194,15 +191,7 @@ __device__ __forceinline__ void epilogue_lds(const Args& p, f32x16 (&acc)[NB][MB
           *reinterpret_cast<i32x2*>(scratch + row * L::RB + unit * 8) = v;
         }
         if constexpr (EP == RELU_AUX_BIAS) {
-          // ballot r: bits 0-31 = rows of column 8(r/4) + r%4, bits 32-63 = column +4
-          uint32_t word = 0;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const uint64_t bal = __ballot(mok && pre[r] > 0.0f);
-            const int cl = 8 * (r >> 2) + (r & 3);
-            if (lane == cl) word = (uint32_t)bal;
-            if (lane == cl + 4) word = (uint32_t)(bal >> 32);
-          }
+          const uint32_t word = relu_mask_words(pre, mok);
           const int64_t grp = (m0w + 32 * b) >> 5;
           const int ncol = n0w + 32 * a + lane;
           if (lane < 32 && grp * 32 < M && ncol < N) p.aux[grp * N + ncol] = word;
@@ -270,10 +259,7 @@ __device__ __forceinline__ void epilogue_block(const Args& p, const f32x16 (&acc
       float dz[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int idx = 8 * (r >> 2) + (r & 3);
-        const uint32_t wl = __builtin_amdgcn_readlane(word, idx);
-        const uint32_t wh = __builtin_amdgcn_readlane(word, idx + 4);
-        const uint32_t wr = lhi ? wh : wl;
+        const uint32_t wr = mask_word_of_reg(word, r, lane);
         dz[r] = (wr & mybit) ? acc[a][b][r] : 0.0f;
         rowsum += dz[r];
       }
@@ -302,14 +288,7 @@ __device__ __forceinline__ void epilogue_block(const Args& p, const f32x16 (&acc
         *reinterpret_cast<i32x2*>(scratch + lrow * L::RB + unit * 8) = v;
       }
       if constexpr (EP == RELU_AUX_BIAS) {
-        uint32_t word = 0;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const uint64_t bal = __ballot(mok && pre[r] > 0.0f);
-          const int cl = 8 * (r >> 2) + (r & 3);
-          if (lane == cl) word = (uint32_t)bal;
-          if (lane == cl + 4) word = (uint32_t)(bal >> 32);
-        }
+        const uint32_t word = relu_mask_words(pre, mok);
         const int ncol = n0w + 32 * a + lane;
         if (lane < 32 && grp * 32 < M && ncol < N) p.aux[grp * N + ncol] = word;
       }

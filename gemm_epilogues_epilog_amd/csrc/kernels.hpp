@@ -129,7 +129,8 @@ __device__ __forceinline__ i32x4 make_srd(const void* base, uint32_t range = 0x7
 // must be uniform; readfirstlane keeps it in an SGPR where the compiler cannot prove
 // that by itself.
 __device__ __forceinline__ void copy_to_lds_b128(const i32x4& srd, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+  // one wait state between the M0 write and the LDS-DMA load that reads it (gfx9)
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :
                : "v"(voff), "s"(srd), "s"(__builtin_amdgcn_readfirstlane(lds))
                : "memory", "m0");
@@ -220,6 +221,44 @@ __device__ __forceinline__ float vec_value(uint32_t bits, int vec_dt) {
   return vec_dt == F32 ? f : vec_dt == F16 ? h : g;
 }
 
+// ReLU mask words of one 32 x 32 accumulator block: lane c < 32 returns the word of
+// block column c (bit i = pre of row i > 0; rows past m count as 0). Register r of
+// lane l holds row l % 32 and column 8 (r / 4) + 4 (l / 32) + r % 4, so the ballot of
+// register r holds column 8 (r / 4) + r % 4 in its low half and that column + 4 in
+// its high half; each half is written straight into its column's lane.
+// The mask word that register r of this lane needs: `word` holds in lane c (and
+// c + 32) the mask word of block column c, and register r of lane l is row l % 32,
+// column 8 (r / 4) + 4 (l / 32) + r % 4 of the block. Bit l % 32 of the result is the
+// register's mask bit.
+__device__ __forceinline__ uint32_t mask_word_of_reg(uint32_t word, int r, int lane) {
+  const int col = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+  return (uint32_t)__builtin_amdgcn_ds_bpermute(col << 2, (int)word);
+}
+
+// Lane L of v = s (v_writelane_b32, immediate lane select). The compiler does not
+// see into the asm, so it cannot space the instruction from a vector-ALU write of s
+// (the ballot's compare): with WAIT, five wait states come first.
+template <int L, bool WAIT>
+__device__ __forceinline__ void write_lane(uint32_t& v, uint32_t s) {
+  if constexpr (WAIT) asm("s_nop 4\n\tv_writelane_b32 %0, %1, %2" : "+v"(v) : "s"(s), "i"(L));
+  else asm("v_writelane_b32 %0, %1, %2" : "+v"(v) : "s"(s), "i"(L));
+}
+template <int R = 0>
+__device__ __forceinline__ void relu_mask_step(const float (&pre)[16], bool row_ok, uint32_t& word) {
+  if constexpr (R < 16) {
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(row_ok && pre[R] > 0.0f);
+    constexpr int cl = 8 * (R >> 2) + (R & 3);
+    write_lane<cl, true>(word, (uint32_t)bal);
+    write_lane<cl + 4, false>(word, (uint32_t)(bal >> 32));   // same producer, already spaced
+    relu_mask_step<R + 1>(pre, row_ok, word);
+  }
+}
+__device__ __forceinline__ uint32_t relu_mask_words(const float (&pre)[16], bool row_ok) {
+  uint32_t word = 0;
+  relu_mask_step(pre, row_ok, word);
+  return word;
+}
+
 __device__ __forceinline__ float load_vec(const void* p, int vec_dt, int64_t i) {
   if (vec_dt == F32) return static_cast<const float*>(p)[i];
   const uint16_t v = static_cast<const uint16_t*>(p)[i];
@@ -284,10 +323,7 @@ __device__ __forceinline__ void epilogue(const Args& p, f32x16 (&acc)[NB][MB], i
         float dz[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int idx = 8 * (r >> 2) + (r & 3);
-          const uint32_t wl = __builtin_amdgcn_readlane(word, idx);
-          const uint32_t wh = __builtin_amdgcn_readlane(word, idx + 4);
-          const uint32_t wr = lhi ? wh : wl;
+          const uint32_t wr = mask_word_of_reg(word, r, lane);
           dz[r] = (wr & mybit) ? acc[a][b][r] : 0.0f;
           rowsum += dz[r];
         }
@@ -340,15 +376,7 @@ __device__ __forceinline__ void epilogue(const Args& p, f32x16 (&acc)[NB][MB], i
           }
         }
         if constexpr (EP == RELU_AUX_BIAS) {
-          // ballot r: bits 0-31 = rows of column 8(r/4) + r%4, bits 32-63 = column +4
-          uint32_t word = 0;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const uint64_t bal = __ballot(mok && pre[r] > 0.0f);
-            const int cl = 8 * (r >> 2) + (r & 3);
-            if (lane == cl) word = (uint32_t)bal;
-            if (lane == cl + 4) word = (uint32_t)(bal >> 32);
-          }
+          const uint32_t word = relu_mask_words(pre, mok);
           const int64_t grp = (m0w + 32 * b) >> 5;
           const int ncol = n0w + 32 * a + lane;
           if (lane < 32 && grp * 32 < M && ncol < N) p.aux[grp * N + ncol] = word;
