@@ -326,14 +326,36 @@ const char* gemm_epilog_describe(ge_handle_t h) { return h ? h->desc.c_str() : "
 
 namespace gek {
 
-// ---- second pass of DRELU_BGRAD: bgrad[i] = sum over t ascending of partial[t][i] ----
-__global__ __launch_bounds__(256) void bgrad_reduce_kernel(const float* __restrict__ partial, int T, int64_t M,
-                                                           void* bgrad, int vec_dt) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= M) return;
+// ---- second pass of DRELU_BGRAD: bgrad[i] = sum over t of partial[t][i] ----
+// A workgroup of 4 waves takes 64 rows, one per lane; wave w sums the t-range
+// [w T/4, (w+1) T/4) in ascending order with 16 loads in flight, and wave 0 adds the
+// four range sums in order w = 0 .. 3. The order is fixed, so results repeat bit for
+// bit; there are no atomics.
+constexpr int kReduceWaves = 4, kReduceBatch = 16;
+__global__ __launch_bounds__(64 * kReduceWaves) void bgrad_reduce_kernel(const float* __restrict__ partial, int T,
+                                                                       int64_t M, void* bgrad, int vec_dt) {
+  __shared__ float sums[kReduceWaves][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t i = (int64_t)blockIdx.x * 64 + lane;
+  const int t0 = (int)((int64_t)T * w / kReduceWaves), t1 = (int)((int64_t)T * (w + 1) / kReduceWaves);
   float s = 0.0f;
-  for (int t = 0; t < T; ++t) s += partial[(int64_t)t * M + i];
-  store_vec(bgrad, vec_dt, i, s);
+  if (i < M) {
+    for (int t = t0; t < t1; t += kReduceBatch) {
+      float v[kReduceBatch];
+#pragma unroll
+      for (int j = 0; j < kReduceBatch; ++j) v[j] = t + j < t1 ? partial[(int64_t)(t + j) * M + i] : 0.0f;
+#pragma unroll
+      for (int j = 0; j < kReduceBatch; ++j) s += v[j];
+    }
+  }
+  sums[w][lane] = s;
+  __syncthreads();
+  if (w == 0 && i < M) {
+    float r = sums[0][lane];
+#pragma unroll
+    for (int q = 1; q < kReduceWaves; ++q) r += sums[q][lane];
+    store_vec(bgrad, vec_dt, i, r);
+  }
 }
 
 hipError_t launch_bias_add(int dt, const void* in, const void* bias, int vec_dt, void* out, int64_t m, int n,
@@ -360,9 +382,10 @@ hipError_t launch_relu(int dt, const void* in, void* out, int64_t m, int n, hipS
 }
 
 hipError_t launch_bgrad_reduce(const float* partial, int t, int64_t m, void* bgrad, int vec_dt, hipStream_t s) {
-  const dim3 grid((unsigned)cdiv(m, 256));
+  const dim3 grid((unsigned)cdiv(m, 64));
   void* params[] = {&partial, &t, &m, &bgrad, &vec_dt};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&bgrad_reduce_kernel), grid, dim3(256), params, 0, s);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&bgrad_reduce_kernel), grid, dim3(64 * kReduceWaves), params,
+                         0, s);
 }
 
 }  // namespace gek
