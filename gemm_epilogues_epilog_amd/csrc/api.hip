@@ -85,8 +85,10 @@ bool env_off(const char* name) {
   return v && v[0] == '0' && v[1] == 0;
 }
 
-// Pick the largest tile that still gives every compute unit at least one tile;
-// fall back to the smaller register-staged tiles for small problems.
+// 16-bit types: the 256 x 256 tile when it gives every compute unit at least one
+// tile, else the 128 x 128 direct-to-LDS tile (two workgroups per compute unit; a
+// sparse grid splits its k loop). fp32: the register-staged tiles, the largest that
+// still gives every compute unit a tile.
 int choose_cfg(int64_t m, int n, ge_dtype_t ab, int cus) {
   const char* env = std::getenv("GE_TILE");
   if (env && env[0]) {
@@ -94,7 +96,7 @@ int choose_cfg(int64_t m, int n, ge_dtype_t ab, int cus) {
       if (std::strcmp(env, gek::kTiles[c].name) == 0 && (ab != GE_F32 || !gek::cfg_is_dtl(c))) return c;
   }
   auto tiles = [&](int c) { return cdiv(m, gek::kTiles[c].bm) * cdiv(n, gek::kTiles[c].bn); };
-  if (ab != GE_F32 && tiles(gek::CFG_L) >= cus) return gek::CFG_L;
+  if (ab != GE_F32) return tiles(gek::CFG_L) >= cus ? gek::CFG_L : gek::CFG_LM;
   if (tiles(gek::CFG_M) >= cus) return gek::CFG_M;
   return gek::CFG_S;
 }

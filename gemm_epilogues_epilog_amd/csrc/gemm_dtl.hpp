@@ -378,8 +378,9 @@ struct Operands {
     }
   }
 
-  // Copies of part `part` (of KSTEPS) of k-tile kt into LDS stage `stage`.
-  __device__ __forceinline__ void issue_part(int kt, int stage, int part) const {
+  // Copies A[a0, a1) and B[b0, b1) (instruction indices) of k-tile kt into LDS stage
+  // `stage`.
+  __device__ __forceinline__ void issue_range(int kt, int stage, int a0, int a1, int b0, int b1) const {
     const int k0 = kt * BK;
     const i32x4 ra = make_srd(Abase + (int64_t)k0 * 2);
     const i32x4 rb = make_srd(Bbase + (int64_t)k0 * N * 2);
@@ -387,14 +388,14 @@ struct Operands {
     const uint32_t sB = sA + C::A_BYTES;
     const bool tail = k0 + BK > K;
 #pragma unroll
-    for (int q = 0; q < A_PART; ++q) {
-      const int j = part * A_PART + q;
+    for (int j = 0; j < C::A_INST; ++j) {
+      if (j < a0 || j >= a1) continue;
       const uint32_t off = (tail && k0 + a_chunk[j] * 8 >= K) ? kOOB : a_src[j];
       copy_to_lds_b128(ra, off, sA + (w * C::A_INST + j) * 1024);
     }
 #pragma unroll
-    for (int q = 0; q < B_PART; ++q) {
-      const int j = part * B_PART + q;
+    for (int j = 0; j < C::B_INST; ++j) {
+      if (j < b0 || j >= b1) continue;
       const uint32_t off = (tail && k0 + b_row[j] >= K) ? kOOB : b_src[j];
       copy_to_lds_b128(rb, off, sB + (w * C::B_INST + j) * 1024);
     }
@@ -413,9 +414,16 @@ struct Operands {
       copy_to_lds_b128(make_srd(Bbase + (int64_t)k0 * N * 2), off, sA + C::A_BYTES + (w * C::B_INST + jb) * 1024);
     }
   }
+  // All copies of k-tile kt: in KSTEPS parts (A then B of each) when the counts divide,
+  // else all A then all B.
   __device__ __forceinline__ void issue_tile(int kt, int stage) const {
+    if constexpr (C::A_INST % C::KSTEPS == 0 && C::B_INST % C::KSTEPS == 0) {
 #pragma unroll
-    for (int part = 0; part < C::KSTEPS; ++part) issue_part(kt, stage, part);
+      for (int part = 0; part < C::KSTEPS; ++part)
+        issue_range(kt, stage, part * A_PART, (part + 1) * A_PART, part * B_PART, (part + 1) * B_PART);
+    } else {
+      issue_range(kt, stage, 0, C::A_INST, 0, C::B_INST);
+    }
   }
 
   // Fragments of k-step s from the stage at `base`.
@@ -977,7 +985,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_sk_kernel(
       }
       const __amdgpu_buffer_rsrc_t slot = rsrc(reinterpret_cast<char*>(p.sk_partial) + (size_t)o * slot_bytes);
       // sixteen loads in flight at a time, then the adds
-      constexpr int BATCH = 16;
+      constexpr int BATCH = PL::QUADS < 16 ? PL::QUADS : 16;
       static_assert(PL::QUADS % BATCH == 0, "load batches");
 #pragma unroll
       for (int q0 = 0; q0 < PL::QUADS; q0 += BATCH) {

@@ -18,7 +18,7 @@ struct TileCfg {
   const char* loop;   // main loop of the direct-to-LDS kernels
 };
 
-enum CfgId { CFG_S = 0, CFG_M, CFG_L, CFG_LH, CFG_LA, CFG_LI, CFG_LS, CFG_LSH, CFG_W4, CFG_W4S, CFG_P, CFG_COUNT };
+enum CfgId { CFG_S = 0, CFG_M, CFG_L, CFG_LH, CFG_LA, CFG_LI, CFG_LS, CFG_LSH, CFG_LM, CFG_W4, CFG_W4S, CFG_P, CFG_COUNT };
 
 constexpr TileCfg kTiles[CFG_COUNT] = {
     {64, 64, 32, 32, 0, 2, "S", ""},
@@ -29,6 +29,7 @@ constexpr TileCfg kTiles[CFG_COUNT] = {
     {256, 256, 128, 64, 64, 2, "LI", "lockstep interleaved"},
     {256, 256, 128, 64, 32, 4, "LS", "lockstep spread interleaved"},
     {256, 256, 128, 64, 32, 4, "LSH", "lockstep spread interleaved, copies on waves 0-3"},
+    {128, 128, 32, 64, 64, 2, "LM", "lockstep"},                        // 8 waves of 32 x 64, two per CU
     {256, 256, 128, 128, 64, 2, "W4", "lockstep"},                      // 4 waves of 128 x 128
     {256, 256, 128, 128, 32, 4, "W4S", "lockstep spread interleaved"},
     {256, 256, 128, 64, 32, 4, "P", "ping-pong"},                       // 8 waves in two groups
@@ -37,7 +38,7 @@ constexpr TileCfg kTiles[CFG_COUNT] = {
 inline bool cfg_is_dtl(int c) { return c >= CFG_L; }
 // Configurations whose kernel can split the last round's K loop (8-wave lockstep
 // loops; the 4-wave tile has no registers left for the partial sums).
-inline bool cfg_can_split(int c) { return c >= CFG_L && c <= CFG_LSH; }
+inline bool cfg_can_split(int c) { return c >= CFG_L && c <= CFG_LM; }
 
 // Configurations with a persistent kernel, used when the tile grid is not split and
 // k spans a whole number of stage rings, at least two.
@@ -108,6 +109,7 @@ LaunchFn pick_cfg(int cfg) {
       case CFG_LI: return &launch_dtl<DT, EP, 256, 256, 128, 64, 64, 2, LOCKSTEP_ILV>;
       case CFG_LS: return &launch_dtl<DT, EP, 256, 256, 128, 64, 32, 4, LOCKSTEP_SPREAD_ILV>;
       case CFG_LSH: return &launch_dtl<DT, EP, 256, 256, 128, 64, 32, 4, LOCKSTEP_SPREAD_ILV_HALF>;
+      case CFG_LM: return &launch_dtl<DT, EP, 128, 128, 32, 64, 64, 2, LOCKSTEP>;
       case CFG_W4: return &launch_dtl<DT, EP, 256, 256, 128, 128, 64, 2, LOCKSTEP>;
       case CFG_W4S: return &launch_dtl<DT, EP, 256, 256, 128, 128, 32, 4, LOCKSTEP_SPREAD_ILV>;
       case CFG_P: return &launch_dtl<DT, EP, 256, 256, 128, 64, 32, 4, PINGPONG>;

@@ -113,7 +113,7 @@ typedef enum {
  *   out     : receives the handle; untouched on error.
  * Allocates the workspace on the current device: the per-tile bias-gradient
  * partial sums for DRELU_BGRAD, T1 and T2 for RELU_BIAS_UNFUSED, nothing otherwise.
- * Environment (tuning experiments): GE_TILE=S|M|L|LH|LA|LI|LS|LSH|W4|W4S|P forces a tile configuration;
+ * Environment (tuning experiments): GE_TILE=S|M|L|LH|LA|LI|LS|LSH|LM|W4|W4S|P forces a tile configuration;
  * GE_GROUP_M=g (1..1024) sets how many m-tiles share one group of the tile order;
  * GE_STREAMK=0 keeps a sparse last round of tiles whole instead of splitting its k loop;
  * GE_PERSIST=0 launches one workgroup per tile instead of the persistent kernel.
