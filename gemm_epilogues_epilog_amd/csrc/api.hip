@@ -171,7 +171,7 @@ ge_status_t gemm_epilog_plan(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt, ge
   // panels come back from HBM each round, and groups of 4 (4 A and 8 B panels) read
   // 3-4% faster (measured at 16384x16384x8192, 32768x8192x8192 and 65536x8192x16384).
   const double a_bytes = (double)m * (double)k * (double)elem_size(dt.ab);
-  h->group_m = a_bytes > 256.0 * 1024 * 1024 ? 4 : 8;
+  h->group_m = a_bytes >= 256.0 * 1024 * 1024 ? 4 : 8;
   if (const char* g = std::getenv("GE_GROUP_M")) {
     const int v = std::atoi(g);
     if (v >= 1 && v <= 1024) h->group_m = v;
