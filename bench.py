@@ -28,6 +28,20 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_ffn_f16_4096x11008x40
 COPY_PROBE_BYTES = 1 << 30
 
 
+# Other measurements, reported under "variants": name -> (workload, epilogue, dtype,
+# inputs drawn on the device). None stands for the headline workload.
+VARIANTS = {
+    "ffn_unfused_f16": (None, "RELU_BIAS_UNFUSED", "f16", False),
+    "ffn_aux_f16": (None, "RELU_AUX_BIAS", "f16", False),
+    "ffn_gelu_bf16": ("ffn_gelu_bf16_4096x11008x4096", "GELU_BIAS", "bf16", False),
+    "mlp8192_fwd_aux_bf16": ("mlp_bf16_8192", "RELU_AUX_BIAS", "bf16", True),
+    "mlp8192_bwd_drelu_bgrad_bf16": ("mlp_bf16_8192", "DRELU_BGRAD", "bf16", True),
+    "large_relu_bias_f16": ("large_f16_65536x8192x16384", "RELU_BIAS", "f16", True),
+    "large_aux_f16": ("large_f16_65536x8192x16384", "RELU_AUX_BIAS", "f16", True),
+    "small_relu_bias_f16": ("relu_bias_f16_1024x512x2048", "RELU_BIAS", "f16", False),
+}
+
+
 def kernel_source_hash() -> str:
     """SHA-256 over the HIP sources: HBM-traffic counters taken for one version of the
     kernels are reported only while the sources are unchanged."""
@@ -195,6 +209,9 @@ def main():
     ap.add_argument("--skip-cpu", action="store_true", help="leave out the cpu_baseline leg (profiling runs)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run the 1 GiB copy that calibrates the HBM byte counters")
+    ap.add_argument("--only", choices=sorted(VARIANTS),
+                    help="time one variant alone (--steps executes after --warmup) and print its line; "
+                         "for profiling runs")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -209,6 +226,12 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_probe:
         copy_probe()
+        return
+    if args.only:
+        wname, ep, dt, dev_rng = VARIANTS[args.only]
+        Wv = inputs.WORKLOADS[inputs.HEADLINE if wname is None else wname]
+        r = run_variant(ge, Wv, ep, dt, args.steps, args.warmup, dev_rng)
+        print(json.dumps({"variant": args.only, **r}), flush=True)
         return
     prop = torch.cuda.get_device_properties(0)
     W = inputs.WORKLOADS[inputs.HEADLINE]
@@ -233,17 +256,10 @@ def main():
     variants = {}
     if not args.no_variants:
         vsteps, vwarm = max(5, args.steps // 4), 5
-        plan = [
-            ("ffn_unfused_f16", inputs.HEADLINE, "RELU_BIAS_UNFUSED", "f16", False),
-            ("ffn_aux_f16", inputs.HEADLINE, "RELU_AUX_BIAS", "f16", False),
-            ("ffn_gelu_bf16", "ffn_gelu_bf16_4096x11008x4096", "GELU_BIAS", "bf16", False),
-            ("mlp8192_fwd_aux_bf16", "mlp_bf16_8192", "RELU_AUX_BIAS", "bf16", True),
-            ("mlp8192_bwd_drelu_bgrad_bf16", "mlp_bf16_8192", "DRELU_BGRAD", "bf16", True),
-            ("large_relu_bias_f16", "large_f16_65536x8192x16384", "RELU_BIAS", "f16", True),
-            ("large_aux_f16", "large_f16_65536x8192x16384", "RELU_AUX_BIAS", "f16", True),
-        ]
-        for name, wname, ep, dt, dev_rng in plan:
-            Wv = inputs.WORKLOADS[wname]
+        for name, (wname, ep, dt, dev_rng) in VARIANTS.items():
+            if name == "small_relu_bias_f16":
+                continue   # latency-bound: a profiling case (--only), not a bench line
+            Wv = inputs.WORKLOADS[inputs.HEADLINE if wname is None else wname]
             steps = vsteps if Wv.flops() < 5e12 else max(3, vsteps // 5)
             log(f"[bench] variant {name}")
             variants[name] = run_variant(ge, Wv, ep, dt, steps, vwarm, dev_rng)

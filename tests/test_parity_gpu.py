@@ -173,7 +173,7 @@ def test_stream_argument(gpu):
 def test_split_tail_plan_and_determinism(gpu):
     """4352 x 4096 (272 tiles on 256 compute units) splits its last round of 16 tiles;
     the split result matches the unsplit one within rounding and repeats bit for bit,
-    and the 7B-FFN shape (last round 69% full) is not split."""
+    and the 7B-FFN shape (its last pass over the CUs 69% full) is not split."""
     ge = gpu
     h = ge.gemm_epilog_plan(4096, 11008, 4096, ("f16", "f16", "f16"), "RELU_BIAS")
     try:

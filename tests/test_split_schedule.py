@@ -79,7 +79,7 @@ def test_sparse_last_round_splits():
 
 def test_full_or_mostly_full_rounds_do_not_split():
     assert plan(1024, 128) is None and plan(8192, 256) is None and plan(512, 64) is None
-    assert plan(688, 64) is None   # 4096 x 11008: last round 69% full
+    assert plan(688, 64) is None   # 4096 x 11008: the last pass over the CUs is 69% full
     assert plan(255, 64) is None
 
 

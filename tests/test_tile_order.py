@@ -66,5 +66,5 @@ def test_concurrent_tiles_of_an_xcd_share_panels():
 def test_group_size_rule():
     assert group_m_for(4096, 4096, 2) == 8          # headline: A is 32 MiB
     assert group_m_for(8192, 8192, 2) == 8          # 8192 x 8192 x 8192: A is 128 MiB
-    assert group_m_for(65536, 16384, 2) == 4        # 65536 x 11008 x 16384: A is 2 GiB
+    assert group_m_for(65536, 16384, 2) == 4        # 65536 x 8192 x 16384: A is 2 GiB
     assert group_m_for(16383, 8192, 2) == 8 and group_m_for(16384, 8192, 2) == 4   # A of 256 MiB
