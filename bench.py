@@ -29,7 +29,8 @@ COPY_PROBE_BYTES = 1 << 30
 
 
 # Other measurements, reported under "variants": name -> (workload, epilogue, dtype,
-# inputs drawn on the device). None stands for the headline workload.
+# inputs drawn on the device[, operand storage "TN" | "NT": A passed as its (k, m)
+# transpose | B passed as its (n, k) transpose]). None stands for the headline workload.
 VARIANTS = {
     "ffn_unfused_f16": (None, "RELU_BIAS_UNFUSED", "f16", False),
     "ffn_aux_f16": (None, "RELU_AUX_BIAS", "f16", False),
@@ -39,7 +40,12 @@ VARIANTS = {
     "large_relu_bias_f16": ("large_f16_65536x8192x16384", "RELU_BIAS", "f16", True),
     "large_aux_f16": ("large_f16_65536x8192x16384", "RELU_AUX_BIAS", "f16", True),
     "small_relu_bias_f16": ("relu_bias_f16_1024x512x2048", "RELU_BIAS", "f16", False),
+    # the rest of the 8192 MLP layer's backward with the weights as stored: dX = W^T . dY
+    # (DRELU_BGRAD on the W^T of the (k, m) weight) and dW = dZ . X^T (B as stored X)
+    "mlp8192_bwd_wt_drelu_bgrad_bf16": ("mlp_bf16_8192", "DRELU_BGRAD", "bf16", True, "TN"),
+    "mlp8192_dw_bf16": ("mlp_bf16_8192", "NONE", "bf16", True, "NT"),
 }
+LAYOUTS = {"NN": (False, False), "TN": (True, False), "NT": (False, True)}
 
 
 def kernel_source_hash() -> str:
@@ -143,12 +149,16 @@ def time_execute(ge, handle, args, steps, warmup, warm_s=0.0):
             "event_ms_p90": per[min(len(per) - 1, (len(per) * 9) // 10)]}
 
 
-def run_variant(ge, W, epilog, dtype, steps, warmup, device_rng, backward=False):
+def run_variant(ge, W, epilog, dtype, steps, warmup, device_rng, layout="NN"):
     import torch
     A, B, bias = device_inputs(W, device_rng)
     m, n, k = W.m, W.n, W.k
+    ta, tb = LAYOUTS[layout]
     t0 = time.perf_counter()
-    h = ge.gemm_epilog_plan(m, n, k, (dtype, dtype, dtype), epilog)
+    if ta or tb:
+        h = ge.gemm_epilog_plan_ex(m, n, k, (dtype, dtype, dtype), epilog, int(ta), int(tb))
+    else:
+        h = ge.gemm_epilog_plan(m, n, k, (dtype, dtype, dtype), epilog)
     plan_ms = (time.perf_counter() - t0) * 1e3
     D = torch.empty(m, n, dtype=A.dtype, device="cuda")
     aux = bg = None
@@ -162,11 +172,15 @@ def run_variant(ge, W, epilog, dtype, steps, warmup, device_rng, backward=False)
         torch.cuda.synchronize()
         ge.gemm_epilog_free(hf)
         bias = None
+    if ta:   # the same operands in the storage order the plan takes
+        A = A.t().contiguous()
+    if tb:
+        B = B.t().contiguous()
     r = time_execute(ge, h, (A, B, bias, D, aux, bg), steps, warmup, warm_s=0.3)
     desc = ge.gemm_epilog_describe(h)
     ge.gemm_epilog_free(h)
     t = r["event_ms_median"] * 1e-3
-    out = {"epilog": epilog, "dtype": dtype, "m": m, "n": n, "k": k, "plan_ms": round(plan_ms, 3),
+    out = {"epilog": epilog, "dtype": dtype, "m": m, "n": n, "k": k, "layout": layout, "plan_ms": round(plan_ms, 3),
            "kernel": desc, "median_ms": round(r["event_ms_median"], 4), "p10_ms": round(r["event_ms_p10"], 4),
            "p90_ms": round(r["event_ms_p90"], 4), "tflops": round(2 * m * n * k / t / 1e12, 1)}
     del A, B, D, aux, bg
@@ -228,9 +242,9 @@ def main():
         copy_probe()
         return
     if args.only:
-        wname, ep, dt, dev_rng = VARIANTS[args.only]
+        wname, ep, dt, dev_rng, *lay = VARIANTS[args.only]
         Wv = inputs.WORKLOADS[inputs.HEADLINE if wname is None else wname]
-        r = run_variant(ge, Wv, ep, dt, args.steps, args.warmup, dev_rng)
+        r = run_variant(ge, Wv, ep, dt, args.steps, args.warmup, dev_rng, *lay)
         print(json.dumps({"variant": args.only, **r}), flush=True)
         return
     prop = torch.cuda.get_device_properties(0)
@@ -256,13 +270,13 @@ def main():
     variants = {}
     if not args.no_variants:
         vsteps, vwarm = max(5, args.steps // 4), 5
-        for name, (wname, ep, dt, dev_rng) in VARIANTS.items():
+        for name, (wname, ep, dt, dev_rng, *lay) in VARIANTS.items():
             if name == "small_relu_bias_f16":
                 continue   # latency-bound: a profiling case (--only), not a bench line
             Wv = inputs.WORKLOADS[inputs.HEADLINE if wname is None else wname]
             steps = vsteps if Wv.flops() < 5e12 else max(3, vsteps // 5)
             log(f"[bench] variant {name}")
-            variants[name] = run_variant(ge, Wv, ep, dt, steps, vwarm, dev_rng)
+            variants[name] = run_variant(ge, Wv, ep, dt, steps, vwarm, dev_rng, *lay)
             log(f"[bench]   {variants[name]}")
         fused_ms = r["event_ms_median"]
         unf = variants["ffn_unfused_f16"]["median_ms"]

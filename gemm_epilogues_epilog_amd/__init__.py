@@ -5,8 +5,9 @@ libgemm_epilog.so (built by gemm_epilogues_epilog_amd/build.py). There is no CPU
 fallback; if the library is missing every call raises.
 
 Low-level functions carry the names of the C ABI in include/gemm_epilog.h:
-gemm_epilog_plan, gemm_epilog_execute, gemm_epilog_free, gemm_epilog_aux_bytes,
-gemm_epilog_workspace_bytes, gemm_epilog_describe, gemm_epilog_status_string.
+gemm_epilog_plan, gemm_epilog_plan_ex, gemm_epilog_execute, gemm_epilog_free,
+gemm_epilog_aux_bytes, gemm_epilog_workspace_bytes, gemm_epilog_describe,
+gemm_epilog_status_string.
 Pointers may be given as torch tensors (device memory), integers or None.
 
 `Matmul` wraps them in the stateful plan / execute / free object with a context
@@ -31,8 +32,10 @@ EPILOG = {"NONE": 0, "RELU_BIAS": 1, "GELU_BIAS": 2, "RELU_AUX_BIAS": 3, "DRELU_
           "RELU_BIAS_UNFUSED": 100}
 STATUS = {0: "GE_OK", 1: "GE_ERR_INVALID_VALUE", 2: "GE_ERR_NOT_SUPPORTED", 3: "GE_ERR_NULL_POINTER",
           4: "GE_ERR_MISALIGNED", 5: "GE_ERR_ALLOC", 6: "GE_ERR_HIP"}
-EXPORTS = ("gemm_epilog_plan", "gemm_epilog_execute", "gemm_epilog_free", "gemm_epilog_aux_bytes",
-           "gemm_epilog_workspace_bytes", "gemm_epilog_describe", "gemm_epilog_status_string")
+EXPORTS = ("gemm_epilog_plan", "gemm_epilog_plan_ex", "gemm_epilog_execute", "gemm_epilog_free",
+           "gemm_epilog_aux_bytes", "gemm_epilog_workspace_bytes", "gemm_epilog_describe",
+           "gemm_epilog_status_string")
+OP_N, OP_T = 0, 1
 
 
 class ge_dtypes_t(ctypes.Structure):
@@ -60,6 +63,8 @@ def load() -> ctypes.CDLL:
     vp, i64, c_int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     L.gemm_epilog_plan.argtypes = [i64, i64, i64, ge_dtypes_t, c_int, ctypes.POINTER(vp)]
     L.gemm_epilog_plan.restype = c_int
+    L.gemm_epilog_plan_ex.argtypes = [i64, i64, i64, ge_dtypes_t, c_int, c_int, c_int, ctypes.POINTER(vp)]
+    L.gemm_epilog_plan_ex.restype = c_int
     L.gemm_epilog_execute.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
     L.gemm_epilog_execute.restype = c_int
     L.gemm_epilog_free.argtypes = [vp]
@@ -113,6 +118,21 @@ def gemm_epilog_plan(m: int, n: int, k: int, dtypes, epilog, check: bool = True)
     return h.value
 
 
+def gemm_epilog_plan_ex(m: int, n: int, k: int, dtypes, epilog, op_a: int = OP_N, op_b: int = OP_N,
+                        check: bool = True):
+    """gemm_epilog_plan with operand storage orders: op_a = OP_T takes A as its (k, m)
+    transpose, op_b = OP_T takes B as its (n, k) transpose."""
+    ab, d, vec = (_dt(x) for x in dtypes)
+    h = ctypes.c_void_p()
+    st = load().gemm_epilog_plan_ex(int(m), int(n), int(k), ge_dtypes_t(ab, d, vec), _ep(epilog), int(op_a),
+                                    int(op_b), ctypes.byref(h))
+    if not check:
+        return st, h.value
+    if st != 0:
+        raise GemmEpilogError(st, "gemm_epilog_plan_ex")
+    return h.value
+
+
 def gemm_epilog_execute(handle, A, B, bias=None, D=None, aux=None, bgrad=None, stream=None, check: bool = True):
     """Enqueue one execute. stream: hipStream_t as int, a torch stream, or None for
     torch's current stream on the current device."""
@@ -147,18 +167,25 @@ class Matmul:
 
     mm = Matmul(m, n, k, "f16", "RELU_BIAS"); mm.plan(); D = mm.execute(A, B, bias); mm.free()
     or `with Matmul(...) as mm:` which plans on entry and frees on exit.
+    trans_a=True takes A as its (k, m) transpose, trans_b=True B as its (n, k) transpose.
     """
 
-    def __init__(self, m: int, n: int, k: int, dtype: str, epilog: str, vec_dtype: Optional[str] = None):
+    def __init__(self, m: int, n: int, k: int, dtype: str, epilog: str, vec_dtype: Optional[str] = None,
+                 trans_a: bool = False, trans_b: bool = False):
         self.m, self.n, self.k = int(m), int(n), int(k)
         self.dtype, self.epilog = dtype, epilog
         self.vec_dtype = vec_dtype or dtype
+        self.trans_a, self.trans_b = bool(trans_a), bool(trans_b)
         self.handle = None
 
     def plan(self):
         if self.handle is None:
-            self.handle = gemm_epilog_plan(self.m, self.n, self.k, (self.dtype, self.dtype, self.vec_dtype),
-                                           self.epilog)
+            dts = (self.dtype, self.dtype, self.vec_dtype)
+            if self.trans_a or self.trans_b:
+                self.handle = gemm_epilog_plan_ex(self.m, self.n, self.k, dts, self.epilog,
+                                                  OP_T if self.trans_a else OP_N, OP_T if self.trans_b else OP_N)
+            else:
+                self.handle = gemm_epilog_plan(self.m, self.n, self.k, dts, self.epilog)
         return self
 
     def describe(self) -> str:
@@ -171,7 +198,9 @@ class Matmul:
         for name, t in (("A", A), ("B", B)):
             if not (t.is_cuda and t.is_contiguous() and _TORCH_NAME.get(str(t.dtype)) == self.dtype):
                 raise ValueError(f"{name} must be a contiguous {self.dtype} device tensor")
-        if tuple(A.shape) != (self.m, self.k) or tuple(B.shape) != (self.k, self.n):
+        a_shape = (self.k, self.m) if self.trans_a else (self.m, self.k)
+        b_shape = (self.n, self.k) if self.trans_b else (self.k, self.n)
+        if tuple(A.shape) != a_shape or tuple(B.shape) != b_shape:
             raise ValueError("operand shapes do not match the plan")
         if out is None:
             out = torch.empty((self.m, self.n), dtype=A.dtype, device=A.device)

@@ -16,7 +16,9 @@ OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libgemm_epilog.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.hip", "inst_f32.hip", "inst_f16.hip", "inst_bf16.hip"]
+SOURCES = ["api.hip", "inst_f32.hip", "inst_f16.hip", "inst_bf16.hip",
+           "inst_f16_lay1.hip", "inst_f16_lay2.hip", "inst_f16_lay3.hip",
+           "inst_bf16_lay1.hip", "inst_bf16_lay2.hip", "inst_bf16_lay3.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -37,7 +39,7 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False, jobs: int = 4) -> str:
+def build(verbose: bool = False, jobs: int = 8) -> str:
     os.makedirs(OBJ, exist_ok=True)
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))

@@ -25,6 +25,7 @@ struct ge_plan {
   ge_dtypes_t dt;
   ge_epilog_t ep;
   int cfg;                 // gek::CfgId
+  int lay;                 // operand storage: bit 0 A as (k,m), bit 1 B as (n,k)
   int device;
   int tiles_m, tiles_n, group_m;
   gek::LaunchFn gemm;      // main kernel (the NONE instance for the unfused chain)
@@ -89,23 +90,45 @@ bool env_off(const char* name) {
 // tile, else the 128 x 128 direct-to-LDS tile (two workgroups per compute unit; a
 // sparse grid splits its k loop). fp32: the register-staged tiles, the largest that
 // still gives every compute unit a tile.
-int choose_cfg(int64_t m, int n, ge_dtype_t ab, int cus) {
+// With an operand stored transposed (lay != 0) the 256 x 256 tile runs one workgroup
+// per tile (LH) instead of the persistent kernel.
+int choose_cfg(int64_t m, int n, ge_dtype_t ab, int cus, int lay) {
   const char* env = std::getenv("GE_TILE");
   if (env && env[0]) {
     for (int c = 0; c < gek::CFG_COUNT; ++c)
-      if (std::strcmp(env, gek::kTiles[c].name) == 0 && (ab != GE_F32 || !gek::cfg_is_dtl(c))) return c;
+      if (std::strcmp(env, gek::kTiles[c].name) == 0 && (ab != GE_F32 || !gek::cfg_is_dtl(c)) &&
+          (lay == 0 || gek::cfg_has_layouts(c)))
+        return c;
   }
   auto tiles = [&](int c) { return cdiv(m, gek::kTiles[c].bm) * cdiv(n, gek::kTiles[c].bn); };
-  if (ab != GE_F32) return tiles(gek::CFG_L) >= cus ? gek::CFG_L : gek::CFG_LM;
+  if (ab != GE_F32) {
+    if (tiles(gek::CFG_L) >= cus) return lay ? gek::CFG_LH : gek::CFG_L;
+    return gek::CFG_LM;
+  }
   if (tiles(gek::CFG_M) >= cus) return gek::CFG_M;
   return gek::CFG_S;
 }
 
-gek::LaunchFn lookup(ge_dtype_t ab, int ep, int cfg) {
+gek::LaunchFn lookup(ge_dtype_t ab, int ep, int cfg, int lay) {
+  if (lay != 0 && !gek::cfg_has_layouts(cfg)) return nullptr;
   switch (ab) {
-    case GE_F32: return gek::get_launch_f32(ep, cfg);
-    case GE_F16: return gek::get_launch_f16(ep, cfg);
-    case GE_BF16: return gek::get_launch_bf16(ep, cfg);
+    case GE_F32: return lay == 0 ? gek::get_launch_f32(ep, cfg) : nullptr;
+    case GE_F16:
+      switch (lay) {
+        case 0: return gek::get_launch_f16(ep, cfg);
+        case 1: return gek::get_launch_f16_lay1(ep, cfg);
+        case 2: return gek::get_launch_f16_lay2(ep, cfg);
+        case 3: return gek::get_launch_f16_lay3(ep, cfg);
+      }
+      break;
+    case GE_BF16:
+      switch (lay) {
+        case 0: return gek::get_launch_bf16(ep, cfg);
+        case 1: return gek::get_launch_bf16_lay1(ep, cfg);
+        case 2: return gek::get_launch_bf16_lay2(ep, cfg);
+        case 3: return gek::get_launch_bf16_lay3(ep, cfg);
+      }
+      break;
   }
   return nullptr;
 }
@@ -133,16 +156,26 @@ size_t gemm_epilog_aux_bytes(int64_t m, int64_t n) {
 }
 
 ge_status_t gemm_epilog_plan(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt, ge_epilog_t ep, ge_handle_t* out) {
+  return gemm_epilog_plan_ex(m, n, k, dt, ep, GE_OP_N, GE_OP_N, out);
+}
+
+ge_status_t gemm_epilog_plan_ex(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt, ge_epilog_t ep, ge_op_t op_a,
+                                ge_op_t op_b, ge_handle_t* out) {
   // ---- host-only validation (no HIP call before this block passes) ----
   if (!out) return GE_ERR_NULL_POINTER;
   if (m < 1 || m > 0x7fffffffLL || n < 1 || n > (1LL << 20) || k < 1 || k > (1LL << 20))
     return GE_ERR_INVALID_VALUE;
   if (!known_dtype(dt.ab) || !known_dtype(dt.d) || !known_dtype(dt.vec) || !known_epilog(ep))
     return GE_ERR_INVALID_VALUE;
+  if ((op_a != GE_OP_N && op_a != GE_OP_T) || (op_b != GE_OP_N && op_b != GE_OP_T)) return GE_ERR_INVALID_VALUE;
   if (dt.d != dt.ab) return GE_ERR_NOT_SUPPORTED;
   if (dt.vec != dt.d && dt.vec != GE_F32) return GE_ERR_NOT_SUPPORTED;
   const int64_t mult = dt.ab == GE_F32 ? 4 : 8;   // 16-byte rows
   if (n % mult != 0 || k % mult != 0) return GE_ERR_NOT_SUPPORTED;
+  const int lay = (op_a == GE_OP_T ? 1 : 0) | (op_b == GE_OP_T ? 2 : 0);
+  if (lay != 0 && dt.ab == GE_F32) return GE_ERR_NOT_SUPPORTED;
+  // A stored as (k, m): its rows hold m values, so m follows the row rules of n
+  if (op_a == GE_OP_T && (m > (1LL << 20) || m % mult != 0)) return GE_ERR_NOT_SUPPORTED;
   const int64_t tiles_bound = cdiv(m, 64) * cdiv(n, 64);
   if (tiles_bound > 0x7fffffffLL) return GE_ERR_NOT_SUPPORTED;   // grid size
 
@@ -162,7 +195,8 @@ ge_status_t gemm_epilog_plan(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt, ge
   h->dt = dt;
   h->ep = ep;
   h->device = dev;
-  h->cfg = choose_cfg(m, (int)n, dt.ab, cus);
+  h->lay = lay;
+  h->cfg = choose_cfg(m, (int)n, dt.ab, cus, lay);
   const gek::TileCfg& tc = gek::kTiles[h->cfg];
   h->tiles_m = (int)cdiv(m, tc.bm);
   h->tiles_n = (int)cdiv(n, tc.bn);
@@ -177,7 +211,7 @@ ge_status_t gemm_epilog_plan(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt, ge
     if (v >= 1 && v <= 1024) h->group_m = v;
   }
   const int kernel_ep = ep == GE_EPILOG_RELU_BIAS_UNFUSED ? (int)gek::NONE : (int)ep;
-  h->gemm = lookup(dt.ab, kernel_ep, h->cfg);
+  h->gemm = lookup(dt.ab, kernel_ep, h->cfg, lay);
   if (!h->gemm) {
     delete h;
     return GE_ERR_NOT_SUPPORTED;
@@ -189,7 +223,7 @@ ge_status_t gemm_epilog_plan(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt, ge
   // than that, i.e. when the last round is at most half full)
   const int tiles = h->tiles_m * h->tiles_n;
   h->dp_tiles = tiles;
-  if (gek::cfg_can_split(h->cfg) && !env_off("GE_STREAMK")) {
+  if (gek::cfg_can_split(h->cfg) && lay == 0 && !env_off("GE_STREAMK")) {
     const int kt = (int)cdiv(k, tc.bk);
     const int rem = tiles % cus;
     if (rem != 0 && (int64_t)rem * 2 <= (int64_t)cus && kt >= 2) {
@@ -205,7 +239,7 @@ ge_status_t gemm_epilog_plan(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt, ge
   }
 
   // ---- persistent kernel: one workgroup per compute unit walks the tiles ----
-  if (gek::cfg_can_persist(h->cfg) && h->dp_tiles == tiles && !env_off("GE_PERSIST")) {
+  if (gek::cfg_can_persist(h->cfg) && lay == 0 && h->dp_tiles == tiles && !env_off("GE_PERSIST")) {
     const int kt = (int)cdiv(k, tc.bk);
     if (k % tc.bk == 0 && kt % tc.stages == 0 && kt >= 2 * tc.stages) h->persist_grid = std::min(tiles, cus);
   }
@@ -246,7 +280,9 @@ ge_status_t gemm_epilog_plan(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt, ge
       }
     }
   }
-  h->desc = std::string(dt_name(dt.ab)) + " " + ep_name(ep) + " tile " + std::to_string(tc.bm) + "x" +
+  h->desc = std::string(dt_name(dt.ab)) + " " + ep_name(ep) +
+            (lay ? std::string(" op_a ") + (lay & 1 ? "T" : "N") + " op_b " + (lay & 2 ? "T" : "N") : std::string()) +
+            " tile " + std::to_string(tc.bm) + "x" +
             std::to_string(tc.bn) + " waves " + std::to_string(tc.bm / tc.wm) + "x" +
             std::to_string(tc.bn / tc.wn) + (gek::cfg_is_dtl(h->cfg) ? " bk " + std::to_string(tc.bk) + " stages " +
                                                  std::to_string(tc.stages) + " " + tc.loop : std::string()) +

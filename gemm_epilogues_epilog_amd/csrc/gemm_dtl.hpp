@@ -471,6 +471,152 @@ __device__ __forceinline__ void mma_step(f32x16 (&acc)[NB][MB], const i32x4 (&fa
     for (int b = 0; b < MB; ++b) acc[a][b] = Tr<DT>::mma(fb[a], fa[b], acc[a][b]);
 }
 
+// ---- operands in either storage order ----------------------------------------------
+// LAY bit 0: A is stored as A^T, a row-major (k, m) matrix; bit 1: B is stored as
+// B^T, a row-major (n, k) matrix. An operand tile then sits in LDS in the order it
+// has in memory:
+//   k-major (A as stored normally, B given as B^T): MN rows of 2 BK bytes, 16-byte
+//     chunks swizzled by swz_a, one ds_read_b128 per 32-row fragment (8 k values);
+//   mn-major (B as stored normally, A given as A^T): BK rows of 2 MN bytes, chunks
+//     swizzled by swz_b, two ds_read_b64_tr_b16 per fragment.
+// Both give the MFMA operand layout (lane l: index l % 32 of the fragment's 32 rows or
+// columns, k values 8 (l / 32) .. +7 of the k-step), so the main loop and epilogue
+// do not depend on the layout.
+template <int MN, int BK, bool KMAJ>
+struct TileGeom {
+  static constexpr int ROWB = KMAJ ? 2 * BK : 2 * MN;   // bytes per LDS row
+  static constexpr int CHUNKS = ROWB / 16;
+  static constexpr int RPI = 1024 / ROWB;               // rows per 1 KB copy instruction
+  static_assert(KMAJ || MN >= 128, "mn-major rows hold at least 16 chunks");
+  __device__ static __forceinline__ int swz(int row) {
+    if constexpr (KMAJ) return swz_a<ROWB>(row);
+    else return swz_b(row);
+  }
+};
+
+// Copies of one operand's tile: INST 1 KB instructions per copying wave. The tile
+// starts at row (k-major) or column (mn-major) mn0 of the stored matrix, whose
+// extent along m or n is MNDIM; k runs over [0, K). Elements past MNDIM or K read
+// as zero (out-of-range offsets).
+template <int MN, int BK, bool KMAJ, int INST>
+struct OperandCopy {
+  using G = TileGeom<MN, BK, KMAJ>;
+  const char* base;
+  int64_t ldb;            // bytes between stored rows
+  uint32_t src[INST];
+  int kpos[INST];         // k offset inside the k-tile that decides the k tail
+
+  __device__ __forceinline__ void init(const void* X, int64_t mn0, int64_t mndim, int K, int w, int lane) {
+    if constexpr (KMAJ) {
+      base = static_cast<const char*>(X) + mn0 * (int64_t)K * 2;
+      ldb = (int64_t)K * 2;
+    } else {
+      base = static_cast<const char*>(X) + mn0 * 2;
+      ldb = mndim * 2;
+    }
+#pragma unroll
+    for (int j = 0; j < INST; ++j) {
+      const int row = (w * INST + j) * G::RPI + lane / G::CHUNKS;
+      const int c = (lane % G::CHUNKS) ^ G::swz(row);
+      if constexpr (KMAJ) {
+        kpos[j] = 8 * c;
+        src[j] = (mn0 + row < mndim) ? (uint32_t)(row * ldb + c * 16) : kOOB;
+      } else {
+        kpos[j] = row;
+        src[j] = (mn0 + 8 * c < mndim) ? (uint32_t)(row * ldb + c * 16) : kOOB;
+      }
+    }
+  }
+  // k-tile starting at k0 into the LDS region at `dst`.
+  __device__ __forceinline__ void issue(int k0, int K, int w, uint32_t dst) const {
+    const i32x4 srd = make_srd(base + (KMAJ ? (int64_t)k0 * 2 : (int64_t)k0 * ldb));
+    const bool tail = k0 + BK > K;
+#pragma unroll
+    for (int j = 0; j < INST; ++j) {
+      const uint32_t off = (tail && k0 + kpos[j] >= K) ? kOOB : src[j];
+      copy_to_lds_b128(srd, off, dst + (w * INST + j) * 1024);
+    }
+  }
+};
+
+// Fragment reads of one operand for a wave whose fragments start at index wpos * W
+// of the tile (NBLK fragments of 32, KS k-steps per k-tile), from the LDS region at
+// byte `region` of a stage.
+template <int MN, int BK, bool KMAJ, int W, int NBLK, int KS>
+struct FragRead {
+  using G = TileGeom<MN, BK, KMAJ>;
+  int rd[KMAJ ? KS : NBLK];
+
+  __device__ __forceinline__ void init(int wpos, int lane, int region) {
+    const int lrow = lane & 31, lhi = lane >> 5;
+    if constexpr (KMAJ) {
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        rd[s] = region + (wpos * W + lrow) * G::ROWB + (((2 * s + lhi) ^ G::swz(lrow)) << 4);
+    } else {
+      const int g = lane >> 4, i = lane & 15;
+      const int row = 8 * lhi + (i >> 2);   // + 16 s, + 4 for the second read
+#pragma unroll
+      for (int blk = 0; blk < NBLK; ++blk) {
+        const int x = wpos * W + blk * 32 + 16 * (g & 1) + 4 * (i & 3);
+        rd[blk] = region + row * G::ROWB + (((x >> 3) ^ G::swz(row)) << 4) + ((x & 7) << 1);
+      }
+    }
+  }
+  __device__ __forceinline__ i32x4 read(const char* stage, int s, int blk) const {
+    if constexpr (KMAJ) {
+      return *reinterpret_cast<const i32x4*>(stage + rd[s] + blk * 32 * G::ROWB);
+    } else {
+      const char* q = stage + rd[blk] + 16 * s * G::ROWB;
+      const i32x2 lo = ds_read_tr(q);
+      const i32x2 hi = ds_read_tr(q + 4 * G::ROWB);
+      return i32x4{lo[0], lo[1], hi[0], hi[1]};
+    }
+  }
+};
+
+// Copies and fragment reads of both operands for LAY != 0 (the lockstep loop without
+// interleaved reads or spread copies).
+template <int DT, int BM, int BN, int WM, int WN, int BK, int STAGES, int CW, int LAY>
+struct OperandsT {
+  using C = DtlCfg<BM, BN, WM, WN, BK, STAGES, CW>;
+  static constexpr bool TA = (LAY & 1) != 0, TB = (LAY & 2) != 0;
+  static constexpr int MB = C::MB, NB = C::NB;
+  OperandCopy<BM, BK, !TA, C::A_INST> ca;
+  OperandCopy<BN, BK, TB, C::B_INST> cb;
+  FragRead<BM, BK, !TA, WM, MB, C::KSTEPS> fa;
+  FragRead<BN, BK, TB, WN, NB, C::KSTEPS> fb;
+  int K, w;
+  uint32_t lds_base;
+
+  __device__ __forceinline__ OperandsT(const Args& p, int64_t m0, int n0, int w_, int wm, int wn, int lane,
+                                       uint32_t lds) {
+    K = p.k;
+    w = w_;
+    lds_base = lds;
+    ca.init(p.A, m0, p.m, K, w, lane);
+    cb.init(p.B, n0, p.n, K, w, lane);
+    fa.init(wm, lane, 0);
+    fb.init(wn, lane, C::A_BYTES);
+  }
+  __device__ __forceinline__ void issue_tile(int kt, int stage) const {
+    const uint32_t sA = lds_base + stage * C::STAGE;
+    ca.issue(kt * BK, K, w, sA);
+    cb.issue(kt * BK, K, w, sA + C::A_BYTES);
+  }
+  // Every fragment of k-step s from the stage at `base`.
+  __device__ __forceinline__ void read_step(const char* base, int s, Frags<MB, NB>& f) const {
+#pragma unroll
+    for (int b = 0; b < MB; ++b) f.a[b] = fa.read(base, s, b);
+#pragma unroll
+    for (int a = 0; a < NB; ++a) {
+      const i32x4 v = fb.read(base, s, a);
+      f.b[a][0] = i32x2{v[0], v[1]};
+      f.b[a][1] = i32x2{v[2], v[3]};
+    }
+  }
+};
+
 // ---- lockstep main loop --------------------------------------------------------
 // All waves run the same schedule. At the end of k-tile t every wave waits until
 // its own copies of tile t+1 have landed and its reads of tile t are done, and one
@@ -485,13 +631,15 @@ __device__ __forceinline__ void mma_step(f32x16 (&acc)[NB][MB], const i32x4 (&fa
 // lockstep_tile accumulates the k-tiles [kb, kb + nt) of one output tile into acc.
 // It expects no copy of its own in flight and every wave done with the LDS; on
 // return every copy has landed, but reads of the last stage may still be in flight.
-template <int DT, int BM, int BN, int WM, int WN, int BK, int STAGES, bool SPREAD, bool ILV, int CW>
+template <int DT, int BM, int BN, int WM, int WN, int BK, int STAGES, bool SPREAD, bool ILV, int CW, int LAY = 0>
 __device__ __forceinline__ void lockstep_tile(const Args& p, char* smem, int64_t m0, int n0, int kb, int nt,
                                               f32x16 (&acc)[WN / 32][WM / 32]) {
   using C = DtlCfg<BM, BN, WM, WN, BK, STAGES, CW>;
-  using O = Operands<DT, BM, BN, WM, WN, BK, STAGES, CW>;
+  using O = std::conditional_t<LAY == 0, Operands<DT, BM, BN, WM, WN, BK, STAGES, CW>,
+                               OperandsT<DT, BM, BN, WM, WN, BK, STAGES, CW, LAY>>;
   using F = Frags<C::MB, C::NB>;
   static_assert(DT == F16 || DT == BF16, "16-bit types only");
+  static_assert(LAY == 0 || (!SPREAD && !ILV), "transposed operands use the plain lockstep loop");
   static_assert(C::KSTEPS % 2 == 0, "every tile starts on fragment buffer 0");
   static_assert(!SPREAD || STAGES >= 3, "spread copies run STAGES - 2 tiles ahead");
   constexpr int MB = C::MB, NB = C::NB, KS = C::KSTEPS;
@@ -518,8 +666,12 @@ __device__ __forceinline__ void lockstep_tile(const Args& p, char* smem, int64_t
   F fr[2];
 
   auto read_all = [&](const char* base, int s, F& f) {
+    if constexpr (LAY == 0) {
 #pragma unroll
-    for (int q = 0; q < F::PIECES; ++q) read_piece(op, base, s, q, f);
+      for (int q = 0; q < F::PIECES; ++q) read_piece(op, base, s, q, f);
+    } else {
+      op.read_step(base, s, f);
+    }
   };
 
   // prologue: tile 0 complete, the next tiles in flight
@@ -581,9 +733,11 @@ __device__ __forceinline__ void lockstep_tile(const Args& p, char* smem, int64_t
         const int a = i / MB, b = i % MB;
         acc[a][b] = Tr<DT>::mma(fr[buf].bfrag(a), fr[buf].a[b], acc[a][b]);
         if constexpr (ILV) {
-          if (i < F::PIECES && reads) read_piece(op, rbase, rs, i, fr[buf ^ 1]);
+          if constexpr (LAY == 0) {
+            if (i < F::PIECES && reads) read_piece(op, rbase, rs, i, fr[buf ^ 1]);
+          }
         }
-        if constexpr (SPREAD) {
+        if constexpr (SPREAD && LAY == 0) {
           if (i % EVERY == 0 && copy && copier) op.issue_one(kb + kc, uc, (i / EVERY) * KS + s);
         }
         if constexpr (ILV || SPREAD) __builtin_amdgcn_sched_barrier(0);
@@ -606,8 +760,9 @@ __device__ __forceinline__ void lockstep_tile(const Args& p, char* smem, int64_t
   }
 }
 
-// One workgroup per output tile.
-template <int DT, int EP, int BM, int BN, int WM, int WN, int BK, int STAGES, bool SPREAD, bool ILV, int CW>
+// One workgroup per output tile. LAY: storage order of the operands (OperandsT).
+template <int DT, int EP, int BM, int BN, int WM, int WN, int BK, int STAGES, bool SPREAD, bool ILV, int CW,
+          int LAY = 0>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_dtl_kernel(Args p) {
   using C = DtlCfg<BM, BN, WM, WN, BK, STAGES>;
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
@@ -620,7 +775,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_dtl_kernel
   const int wm = w % C::WAVES_M, wn = w / C::WAVES_M;
 
   f32x16 acc[C::NB][C::MB];
-  lockstep_tile<DT, BM, BN, WM, WN, BK, STAGES, SPREAD, ILV, CW>(p, smem, m0, n0, 0, (p.k + BK - 1) / BK, acc);
+  lockstep_tile<DT, BM, BN, WM, WN, BK, STAGES, SPREAD, ILV, CW, LAY>(p, smem, m0, n0, 0, (p.k + BK - 1) / BK, acc);
 
   // every wave is done with the stages: reuse them as per-wave epilogue scratch
   wait_lgkmcnt<0>();

@@ -62,7 +62,8 @@ enum Loop { LOCKSTEP = 0, LOCKSTEP_ILV = 1, LOCKSTEP_SPREAD_ILV = 2, PINGPONG = 
 // MFMAs of a k-tile's last step that the persistent loop issues before its barrier.
 constexpr int kPersistPre = 4;
 
-template <int DT, int EP, int BM, int BN, int WM, int WN, int BK, int ST, int LOOP>
+// LAY != 0 (an operand stored transposed): one workgroup per tile, plain lockstep loop.
+template <int DT, int EP, int BM, int BN, int WM, int WN, int BK, int ST, int LOOP, int LAY = 0>
 hipError_t launch_dtl(const Args& a, int grid, hipStream_t s) {
   Args copy = a;
   void* params[] = {&copy};
@@ -71,7 +72,10 @@ hipError_t launch_dtl(const Args& a, int grid, hipStream_t s) {
   constexpr bool ILV = LOOP == LOCKSTEP_ILV || LOOP == PERSIST || SPREAD;
   constexpr int CW = (LOOP == LOCKSTEP_HALF || LOOP == LOCKSTEP_SPREAD_ILV_HALF || LOOP == PERSIST)
                          ? (BM / WM) * (BN / WN) / 2 : 0;
-  if constexpr (LOOP == PINGPONG) {
+  if constexpr (LAY != 0) {
+    static_assert(LOOP == LOCKSTEP || LOOP == LOCKSTEP_HALF, "transposed operands: plain lockstep loop");
+    fn = reinterpret_cast<const void*>(&gemm_dtl_kernel<DT, EP, BM, BN, WM, WN, BK, ST, false, false, CW, LAY>);
+  } else if constexpr (LOOP == PINGPONG) {
     fn = reinterpret_cast<const void*>(&gemm_pp_kernel<DT, EP, BM, BN, WM, WN, BK, ST>);
   } else {
     fn = reinterpret_cast<const void*>(&gemm_dtl_kernel<DT, EP, BM, BN, WM, WN, BK, ST, SPREAD, ILV, CW>);
@@ -132,10 +136,44 @@ LaunchFn pick(int ep, int cfg) {
   }
 }
 
-// Defined one per storage type, each in its own translation unit.
+// Operands stored transposed (LAY bit 0: A as (k,m), bit 1: B as (n,k)), 16-bit
+// types, in the 256 x 256 tile with copies on waves 0-3 (LH) or the 128 x 128 tile
+// (LM).
+inline bool cfg_has_layouts(int c) { return c == CFG_LH || c == CFG_LM; }
+
+template <int DT, int EP, int LAY>
+LaunchFn pick_cfg_t(int cfg) {
+  switch (cfg) {
+    case CFG_LH: return &launch_dtl<DT, EP, 256, 256, 128, 64, 64, 2, LOCKSTEP_HALF, LAY>;
+    case CFG_LM: return &launch_dtl<DT, EP, 128, 128, 32, 64, 64, 2, LOCKSTEP, LAY>;
+    default: return nullptr;
+  }
+}
+
+template <int DT, int LAY>
+LaunchFn pick_t(int ep, int cfg) {
+  switch (ep) {
+    case NONE: return pick_cfg_t<DT, NONE, LAY>(cfg);
+    case RELU_BIAS: return pick_cfg_t<DT, RELU_BIAS, LAY>(cfg);
+    case GELU_BIAS: return pick_cfg_t<DT, GELU_BIAS, LAY>(cfg);
+    case RELU_AUX_BIAS: return pick_cfg_t<DT, RELU_AUX_BIAS, LAY>(cfg);
+    case DRELU_BGRAD: return pick_cfg_t<DT, DRELU_BGRAD, LAY>(cfg);
+    case BIAS: return pick_cfg_t<DT, BIAS, LAY>(cfg);
+    default: return nullptr;
+  }
+}
+
+// Defined one per storage type (and, for the transposed layouts, per layout), each in
+// its own translation unit.
 LaunchFn get_launch_f32(int ep, int cfg);
 LaunchFn get_launch_f16(int ep, int cfg);
 LaunchFn get_launch_bf16(int ep, int cfg);
+LaunchFn get_launch_f16_lay1(int ep, int cfg);
+LaunchFn get_launch_f16_lay2(int ep, int cfg);
+LaunchFn get_launch_f16_lay3(int ep, int cfg);
+LaunchFn get_launch_bf16_lay1(int ep, int cfg);
+LaunchFn get_launch_bf16_lay2(int ep, int cfg);
+LaunchFn get_launch_bf16_lay3(int ep, int cfg);
 
 // Elementwise kernels of the unfused chain and the bgrad second pass.
 hipError_t launch_bias_add(int dt, const void* in, const void* bias, int vec_dt, void* out, int64_t m, int n,

@@ -121,9 +121,34 @@ typedef enum {
 ge_status_t gemm_epilog_plan(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt, ge_epilog_t ep,
                              ge_handle_t* out);
 
+/* Storage order of an operand ([P3] section "The DRELU_BGRAD path in the backward
+ * pass", second paragraph: the backward's weight transpose and gradient layout must
+ * match the matmul call; its FAQ: the rest of the backward pass, such as the weight
+ * gradient, is outside DRELU_BGRAD). The product always uses A as (m, k) and B as
+ * (k, n); GE_OP_T says the operand is passed as its transpose:
+ *   op_a = GE_OP_T: the A pointer holds a row-major (k, m) matrix At, A[i][kk] = At[kk][i]
+ *                   (e.g. dX = W^T . dY with W passed as stored);
+ *   op_b = GE_OP_T: the B pointer holds a row-major (n, k) matrix Bt, B[kk][j] = Bt[j][kk]
+ *                   (e.g. dW = dZ . X^T with X passed as stored). */
+typedef enum { GE_OP_N = 0, GE_OP_T = 1 } ge_op_t;
+
+/*
+ * gemm_epilog_plan_ex - gemm_epilog_plan with the storage order of A and B.
+ *   op_a, op_b : GE_OP_N or GE_OP_T (anything else: GE_ERR_INVALID_VALUE).
+ * GE_OP_T needs fp16 or bf16 operands (fp32: GE_ERR_NOT_SUPPORTED). With op_a =
+ * GE_OP_T, m follows the rules of n: a multiple of 8 and at most 2^20, else
+ * GE_ERR_NOT_SUPPORTED. Every other argument, rule and error is that of
+ * gemm_epilog_plan, which equals gemm_epilog_plan_ex(..., GE_OP_N, GE_OP_N, out).
+ * Plans with a transposed operand run the 256 x 256 tile one workgroup per tile
+ * (or the 128 x 128 tile below one tile per compute unit); GE_TILE may pick LH or LM.
+ */
+ge_status_t gemm_epilog_plan_ex(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt, ge_epilog_t ep, ge_op_t op_a,
+                                ge_op_t op_b, ge_handle_t* out);
+
 /*
  * gemm_epilog_execute - enqueue the planned computation on `stream` and return.
- *   A, B   : device inputs (m,k) and (k,n), type dt.ab, 16-byte aligned.
+ *   A, B   : device inputs (m,k) and (k,n), type dt.ab, 16-byte aligned; (k,m) for A
+ *            and (n,k) for B when the plan was made with op_a / op_b = GE_OP_T.
  *   bias   : device, m values of type dt.vec, aligned to its element size.
  *            Read by BIAS, RELU_BIAS, GELU_BIAS, RELU_AUX_BIAS, RELU_BIAS_UNFUSED;
  *            ignored (may be NULL) otherwise.

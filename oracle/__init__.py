@@ -34,6 +34,9 @@ def lib():
         L.oracle_gemm_epilog.argtypes = [i64, i64, i64, c_int, c_int, c_int, c_int,
                                          vp, vp, vp, vp, vp, vp, vp, vp, c_int]
         L.oracle_gemm_epilog.restype = c_int
+        L.oracle_gemm_epilog_t.argtypes = [i64, i64, i64, c_int, c_int, c_int, c_int, c_int, c_int,
+                                           vp, vp, vp, vp, vp, vp, vp, vp, c_int]
+        L.oracle_gemm_epilog_t.restype = c_int
         L.oracle_f16_to_f32.argtypes = [ctypes.c_uint16]
         L.oracle_f16_to_f32.restype = ctypes.c_float
         L.oracle_f32_to_f16.argtypes = [ctypes.c_float]
@@ -102,11 +105,12 @@ def to_f32(a: np.ndarray, dt: str) -> np.ndarray:
 
 
 def gemm_epilog(A, B, epilog, bias=None, mask=None, ab="f16", d=None, vec=None,
-                want_pre=False, nthreads=0):
+                want_pre=False, nthreads=0, trans_a=False, trans_b=False):
     """Compute one epilogue on the CPU.
 
-    A: (m,k), B: (k,n) arrays in dtype `ab`; bias: (m,) in `vec` (forward epilogs);
-    mask: uint32 (ceil(m/32), n) words, read by DRELU_BGRAD.
+    A: (m,k), B: (k,n) arrays in dtype `ab` (A given as its (k,m) transpose with
+    trans_a, B as its (n,k) transpose with trans_b); bias: (m,) in `vec` (forward
+    epilogs); mask: uint32 (ceil(m/32), n) words, read by DRELU_BGRAD.
     Returns a dict with "D" (m,n) in `d`, and as applicable "mask", "bgrad",
     "pre" (fp32 pre-activation, or dz for DRELU_BGRAD) and "absum" (sum_j |dz|).
     """
@@ -115,8 +119,8 @@ def gemm_epilog(A, B, epilog, bias=None, mask=None, ab="f16", d=None, vec=None,
     ep = EPILOG[epilog]
     A = np.ascontiguousarray(A, dtype=_NP[ab])
     B = np.ascontiguousarray(B, dtype=_NP[ab])
-    m, k = A.shape
-    k2, n = B.shape
+    m, k = A.shape[::-1] if trans_a else A.shape
+    k2, n = B.shape[::-1] if trans_b else B.shape
     assert k == k2, "inner dimensions differ"
     D = np.empty((m, n), _NP[d])
     out = {"D": D}
@@ -142,8 +146,9 @@ def gemm_epilog(A, B, epilog, bias=None, mask=None, ab="f16", d=None, vec=None,
     pre = np.empty((m, n), np.float32) if want_pre else None
     if want_pre:
         out["pre"] = pre
-    rc = lib().oracle_gemm_epilog(m, n, k, DT[ab], DT[d], DT[vec], ep, _ptr(A), _ptr(B), _ptr(bias),
-                                  _ptr(D), _ptr(aux), _ptr(bgrad), _ptr(pre), _ptr(absum), int(nthreads))
+    rc = lib().oracle_gemm_epilog_t(m, n, k, DT[ab], DT[d], DT[vec], ep, int(bool(trans_a)), int(bool(trans_b)),
+                                    _ptr(A), _ptr(B), _ptr(bias), _ptr(D), _ptr(aux), _ptr(bgrad), _ptr(pre),
+                                    _ptr(absum), int(nthreads))
     if rc != 0:
         raise ValueError("oracle rejected the arguments")
     return out

@@ -40,6 +40,12 @@
 //    dz[i,j]) with the sum taken in double over ascending j.
 //  * unfused chain: T1 = round_d(acc); T2 = round_d(T1 + bias); D = max(T2, 0).
 //
+// Operand storage order ("Fusing epilogs with matrix multiplication using
+// nvmath-python", section on the DRELU_BGRAD path, second paragraph: the backward's
+// weight transpose must match the matmul call): with trans_a the A argument holds the
+// row-major (k, m) matrix At and a[i,kk] = At[kk,i]; with trans_b the B argument holds
+// the row-major (n, k) matrix Bt and b[kk,j] = Bt[j,kk]. The product is the same sum.
+//
 // Parity unpinned: NaN / Inf propagation and the sign of zero; inputs never hold them.
 //
 // Build: g++ -O3 -march=x86-64-v3 -ffp-contract=off -fno-fast-math -shared -fPIC -pthread
@@ -277,13 +283,13 @@ void oracle_f16_to_f32_n(const uint16_t* x, float* y, int64_t n) { for (int64_t 
 void oracle_f32_to_bf16_n(const float* x, uint16_t* y, int64_t n) { for (int64_t i = 0; i < n; ++i) y[i] = f32_to_bf16(x[i]); }
 void oracle_bf16_to_f32_n(const uint16_t* x, float* y, int64_t n) { for (int64_t i = 0; i < n; ++i) y[i] = bf16_to_f32(x[i]); }
 
-// Full computation on host memory. A (m,k), B (k,n), D (m,n) row-major; bias and
-// bgrad hold m values; aux holds ceil(m/32)*n words. Returns 0 on success, -1 on
-// an invalid argument. nthreads <= 0 picks min(hardware threads, 16) or
-// $ORACLE_THREADS.
-int oracle_gemm_epilog(int64_t m, int64_t n, int64_t k, int ab_dt, int d_dt, int vec_dt, int epilog,
-                       const void* A, const void* B, const void* bias, void* D, uint32_t* aux,
-                       void* bgrad, float* pre_out, double* absum_out, int nthreads) {
+// Full computation on host memory. A (m,k) (or (k,m) with trans_a), B (k,n) (or
+// (n,k) with trans_b), D (m,n), all row-major; bias and bgrad hold m values; aux
+// holds ceil(m/32)*n words. Returns 0 on success, -1 on an invalid argument.
+// nthreads <= 0 picks min(hardware threads, 16) or $ORACLE_THREADS.
+int oracle_gemm_epilog_t(int64_t m, int64_t n, int64_t k, int ab_dt, int d_dt, int vec_dt, int epilog,
+                         int trans_a, int trans_b, const void* A, const void* B, const void* bias, void* D,
+                         uint32_t* aux, void* bgrad, float* pre_out, double* absum_out, int nthreads) {
   if (m < 1 || n < 1 || k < 1) return -1;
   if (ab_dt < 0 || ab_dt > 2 || d_dt < 0 || d_dt > 2 || vec_dt < 0 || vec_dt > 2) return -1;
   const bool uses_bias = epilog == OEP_BIAS || epilog == OEP_RELU_BIAS || epilog == OEP_GELU_BIAS ||
@@ -294,10 +300,14 @@ int oracle_gemm_epilog(int64_t m, int64_t n, int64_t k, int ab_dt, int d_dt, int
   if ((epilog == OEP_RELU_AUX_BIAS || epilog == OEP_DRELU_BGRAD) && !aux) return -1;
   if (epilog == OEP_DRELU_BGRAD && !bgrad) return -1;
 
-  // O0: widen the operands exactly
+  // O0: widen the operands exactly, into a (m,k) and b (k,n)
   std::vector<float> Aw((size_t)(m * k)), Bw((size_t)(k * n));
-  for (int64_t i = 0; i < m * k; ++i) Aw[(size_t)i] = load_elem(A, ab_dt, i);
-  for (int64_t i = 0; i < k * n; ++i) Bw[(size_t)i] = load_elem(B, ab_dt, i);
+  for (int64_t i = 0; i < m; ++i)
+    for (int64_t kk = 0; kk < k; ++kk)
+      Aw[(size_t)(i * k + kk)] = load_elem(A, ab_dt, trans_a ? kk * m + i : i * k + kk);
+  for (int64_t kk = 0; kk < k; ++kk)
+    for (int64_t j = 0; j < n; ++j)
+      Bw[(size_t)(kk * n + j)] = load_elem(B, ab_dt, trans_b ? j * k + kk : kk * n + j);
 
   Problem P{m, n, k, ab_dt, d_dt, vec_dt, epilog, Aw.data(), Bw.data(), bias, D, aux, bgrad, pre_out, absum_out};
   if (epilog == OEP_RELU_AUX_BIAS && (m % 32) != 0) {
@@ -317,6 +327,14 @@ int oracle_gemm_epilog(int64_t m, int64_t n, int64_t k, int ab_dt, int d_dt, int
   }
   for (auto& th : pool) th.join();
   return 0;
+}
+
+// Both operands stored as in the product: A (m,k), B (k,n).
+int oracle_gemm_epilog(int64_t m, int64_t n, int64_t k, int ab_dt, int d_dt, int vec_dt, int epilog,
+                       const void* A, const void* B, const void* bias, void* D, uint32_t* aux,
+                       void* bgrad, float* pre_out, double* absum_out, int nthreads) {
+  return oracle_gemm_epilog_t(m, n, k, ab_dt, d_dt, vec_dt, epilog, 0, 0, A, B, bias, D, aux, bgrad, pre_out,
+                              absum_out, nthreads);
 }
 
 }  // extern "C"

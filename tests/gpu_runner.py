@@ -61,13 +61,18 @@ def check_guard(buf, fill, what):
     assert ok, f"{what}: a write landed outside the output extent"
 
 
-def run(ge, epilog, dt, A, B, bias=None, mask=None, vec=None, tile=None, stream=None, repeat=1):
-    """A, B, bias, mask: CPU or device tensors. Returns numpy outputs + plan description."""
+def run(ge, epilog, dt, A, B, bias=None, mask=None, vec=None, tile=None, stream=None, repeat=1,
+        trans_a=False, trans_b=False):
+    """A, B, bias, mask: CPU or device tensors; A is (k, m) with trans_a and B is (n, k)
+    with trans_b. Returns numpy outputs + plan description."""
     vec = vec or dt
-    m, k = A.shape
-    n = B.shape[1]
+    m, k = A.shape[::-1] if trans_a else A.shape
+    n = B.shape[0] if trans_b else B.shape[1]
     with tile_env(tile):
-        h = ge.gemm_epilog_plan(m, n, k, (dt, dt, vec), epilog)
+        if trans_a or trans_b:
+            h = ge.gemm_epilog_plan_ex(m, n, k, (dt, dt, vec), epilog, int(trans_a), int(trans_b))
+        else:
+            h = ge.gemm_epilog_plan(m, n, k, (dt, dt, vec), epilog)
     try:
         Ad = A.to("cuda").contiguous()
         Bd = B.to("cuda").contiguous()

@@ -72,6 +72,33 @@ def test_plan_rejects_invalid_arguments(args, status):
     assert h is None
 
 
+@pytest.mark.parametrize("args,status", [
+    ((64, 64, 64, F16, "RELU_BIAS", 2, 0), 1),                   # op_a neither N nor T
+    ((64, 64, 64, F16, "RELU_BIAS", 0, -1), 1),                  # op_b neither N nor T
+    ((64, 64, 64, ("f32", "f32", "f32"), "RELU_BIAS", 1, 0), 2),  # transposed fp32 operand
+    ((64, 64, 64, ("f32", "f32", "f32"), "NONE", 0, 1), 2),
+    ((60, 64, 64, F16, "RELU_BIAS", 1, 0), 2),                   # A as (k, m): m not a multiple of 8
+    (((1 << 20) + 8, 64, 64, F16, "RELU_BIAS", 1, 0), 2),        # A as (k, m): m above 2^20
+    ((64, 12, 64, F16, "RELU_BIAS", 0, 1), 2),                   # n not a multiple of 8
+    ((0, 64, 64, F16, "RELU_BIAS", 1, 1), 1),                    # the plain rules still apply
+])
+def test_plan_ex_rejects_invalid_arguments(args, status):
+    st, h = ge.gemm_epilog_plan_ex(*args, check=False)
+    assert st == status
+    assert h is None
+
+
+def test_plan_ex_without_gpu_reports_hip_error():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible: plan succeeds here")
+    # a ragged m is fine when only B is transposed
+    st, h = ge.gemm_epilog_plan_ex(61, 64, 64, F16, "DRELU_BGRAD", 0, 1, check=False)
+    assert st == 6 and h is None
+    st, h = ge.gemm_epilog_plan_ex(64, 64, 64, F16, "DRELU_BGRAD", 1, 0, check=False)
+    assert st == 6 and h is None
+
+
 def test_plan_null_out():
     lib = ge.load()
     st = lib.gemm_epilog_plan(8, 8, 8, ge.ge_dtypes_t(1, 1, 1), 1, None)

@@ -1,0 +1,126 @@
+"""GPU parity of the transposed-operand plans (gemm_epilog_plan_ex) against the CPU
+oracle, through the C ABI: A handed over as its (k, m) transpose (the backward's
+dX = W^T . dY with W as stored), B as its (n, k) transpose (the weight gradient
+dW = dZ . X^T with X as stored), or both.
+
+* integer-valued inputs: D, the mask and bgrad equal the oracle bit for bit, for every
+  epilogue but GELU, both 16-bit types, both tiles with layouts (256 x 256 "LH" and
+  128 x 128 "LM"), ragged n, several k-tiles and a ragged k tail (and a ragged m where
+  A is not transposed);
+* random normal inputs: the fused-epilogue tolerances and the rounding-model ratio;
+* the same tile on the same data gives the same bits whatever the operands' order.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gemm_epilogues_epilog_amd import inputs
+from tests import gpu_runner as R
+from tests.helpers import assert_bgrad, assert_close, assert_mask, tight_ratio, to_np
+
+pytestmark = pytest.mark.gpu
+
+LAYOUTS = {"TN": (True, False), "NT": (False, True), "TT": (True, True)}
+TILES = [None, "LH", "LM"]
+INT_SHAPES = [(8, 8, 8), (40, 136, 72), (200, 264, 200), (304, 520, 136), (512, 520, 256)]
+RAGGED_M = [(33, 136, 72), (300, 520, 256)]   # A not transposed: m need not be a multiple of 8
+
+
+def stored(t: torch.Tensor, trans: bool) -> torch.Tensor:
+    """The operand in the storage order the plan expects."""
+    return t.t().contiguous() if trans else t
+
+
+def cases_int():
+    for dt in ("f16", "bf16"):
+        for lay, (ta, tb) in LAYOUTS.items():
+            for tile in TILES:
+                for shape in INT_SHAPES + (RAGGED_M if not ta else []):
+                    yield dt, lay, tile, shape
+
+
+@pytest.mark.parametrize("dt,lay,tile,shape", list(cases_int()))
+def test_integer_exact_layouts(gpu, dt, lay, tile, shape):
+    ta, tb = LAYOUTS[lay]
+    m, n, k = shape
+    print(f"[case] integer {dt} {lay} tile {tile} m={m} n={n} k={k}", flush=True)
+    A, B, bias, A2, B2 = inputs.integer_case(m, n, k, dt)
+    As, Bs = stored(A, ta), stored(B, tb)
+    a, b, c = to_np(As), to_np(Bs), to_np(bias)
+    kw = dict(trans_a=ta, trans_b=tb)
+    for ep in ("NONE", "BIAS", "RELU_BIAS", "RELU_BIAS_UNFUSED"):
+        g = R.run(gpu, ep, dt, As, Bs, bias, tile=tile, **kw)
+        o = oracle.gemm_epilog(a, b, ep, bias=c, ab=dt, **kw)
+        assert np.array_equal(g["D"].view(np.uint8), o["D"].view(np.uint8)), f"{ep} {g['desc']}"
+    g = R.run(gpu, "RELU_AUX_BIAS", dt, As, Bs, bias, tile=tile, **kw)
+    o = oracle.gemm_epilog(a, b, "RELU_AUX_BIAS", bias=c, ab=dt, **kw)
+    assert np.array_equal(g["D"].view(np.uint8), o["D"].view(np.uint8)), g["desc"]
+    assert np.array_equal(g["mask"].view(np.uint32), o["mask"]), g["desc"]
+    mask = torch.from_numpy(o["mask"].view(np.int32).copy())
+    A2s, B2s = stored(A2, ta), stored(B2, tb)
+    gb = R.run(gpu, "DRELU_BGRAD", dt, A2s, B2s, mask=mask, tile=tile, **kw)
+    ob = oracle.gemm_epilog(to_np(A2s), to_np(B2s), "DRELU_BGRAD", mask=o["mask"], ab=dt, **kw)
+    assert np.array_equal(gb["D"].view(np.uint8), ob["D"].view(np.uint8)), gb["desc"]
+    assert np.array_equal(gb["bgrad"].view(np.uint8), ob["bgrad"].view(np.uint8)), gb["desc"]
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("lay", list(LAYOUTS))
+@pytest.mark.parametrize("shape", [(64, 48, 32), (136, 200, 264), (256, 392, 520), (1024, 512, 2048)])
+def test_random_parity_layouts(gpu, dt, lay, shape):
+    ta, tb = LAYOUTS[lay]
+    m, n, k = shape
+    print(f"[case] random {dt} {lay} m={m} n={n} k={k}", flush=True)
+    A, B, bias, A2, B2 = inputs.small_case(m, n, k, dt, std=1.0, std_bias=1.0)
+    As, Bs = stored(A, ta), stored(B, tb)
+    a, b, c = to_np(As), to_np(Bs), to_np(bias)
+    wa, wb = oracle.to_f32(to_np(A), dt), oracle.to_f32(to_np(B), dt)
+    kw = dict(trans_a=ta, trans_b=tb)
+    for ep in ("RELU_BIAS", "GELU_BIAS", "BIAS"):
+        g = R.run(gpu, ep, dt, As, Bs, bias, **kw)
+        o = oracle.gemm_epilog(a, b, ep, bias=c, ab=dt, **kw)
+        assert_close(g["D"], o["D"], dt, f"{ep} {g['desc']}")
+        r = tight_ratio(g["D"], o["D"], dt, wa, wb, 1.13 if ep == "GELU_BIAS" else 1.0)
+        assert r <= 4.0, f"{ep} {g['desc']}: rounding-model ratio {r}"
+    g = R.run(gpu, "RELU_AUX_BIAS", dt, As, Bs, bias, **kw)
+    o = oracle.gemm_epilog(a, b, "RELU_AUX_BIAS", bias=c, ab=dt, want_pre=True, **kw)
+    assert_close(g["D"], o["D"], dt, g["desc"])
+    assert_mask(g["mask"], o["mask"], o["pre"], m)
+    mask = torch.from_numpy(g["mask"].view(np.int32).copy())   # the GPU forward's mask
+    A2s, B2s = stored(A2, ta), stored(B2, tb)
+    gb = R.run(gpu, "DRELU_BGRAD", dt, A2s, B2s, mask=mask, **kw)
+    ob = oracle.gemm_epilog(to_np(A2s), to_np(B2s), "DRELU_BGRAD", mask=g["mask"].view(np.uint32), ab=dt, **kw)
+    assert_close(gb["D"], ob["D"], dt, gb["desc"])
+    assert_bgrad(gb["bgrad"], ob["bgrad"], ob["absum"], dt)
+
+
+@pytest.mark.parametrize("tile", ["LH", "LM"])
+def test_layout_does_not_change_bits(gpu, tile):
+    # one tile configuration, one k order: the storage order of the operands only changes
+    # how they reach LDS, so the random-input results agree bit for bit (the reference
+    # keeps whole tiles, as the transposed plans always do: a split k loop adds its
+    # partial sums in another order)
+    m, n, k = 512, 520, 1032
+    A, B, bias, A2, B2 = inputs.small_case(m, n, k, "bf16")
+    ref = R.run(gpu, "RELU_AUX_BIAS", "bf16", A, B, bias, tile=tile + "-nosk")
+    for lay, (ta, tb) in LAYOUTS.items():
+        g = R.run(gpu, "RELU_AUX_BIAS", "bf16", stored(A, ta), stored(B, tb), bias, tile=tile,
+                  trans_a=ta, trans_b=tb)
+        assert np.array_equal(g["D"], ref["D"]) and np.array_equal(g["mask"], ref["mask"]), f"{lay} {g['desc']}"
+
+
+def test_plan_describes_layout(gpu):
+    ge = gpu
+    h = ge.gemm_epilog_plan_ex(4096, 4096, 512, ("bf16", "bf16", "bf16"), "DRELU_BGRAD", 1, 0)
+    try:
+        d = ge.gemm_epilog_describe(h)
+        assert "op_a T op_b N" in d and "tile 256x256" in d and "persistent" not in d, d
+    finally:
+        ge.gemm_epilog_free(h)
+    h = ge.gemm_epilog_plan_ex(256, 256, 512, ("f16", "f16", "f16"), "NONE", 0, 1)
+    try:
+        d = ge.gemm_epilog_describe(h)
+        assert "op_a N op_b T" in d and "tile 128x128" in d, d
+    finally:
+        ge.gemm_epilog_free(h)

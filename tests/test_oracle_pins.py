@@ -201,6 +201,43 @@ def test_integer_exact_backward(dt, shape):
     assert np.array_equal(o["absum"], np.abs(dz).sum(axis=1))
 
 
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("ta,tb", [(True, False), (False, True), (True, True)])
+def test_integer_exact_transposed_operands(dt, shape, ta, tb):
+    # operands handed over in the other storage order: A as its (k, m) transpose, B as
+    # its (n, k) transpose; the exact float64 product of the untransposed integers decides
+    m, n, k = shape
+    A, B, bias, A2, B2 = inputs.integer_case(m, n, k, dt)
+    a64, b64 = A.double().numpy(), B.double().numpy()
+    pre = a64 @ b64 + bias.double().numpy()[:, None]
+    An = np.ascontiguousarray(np_of(A, dt).T) if ta else np_of(A, dt)
+    Bn = np.ascontiguousarray(np_of(B, dt).T) if tb else np_of(B, dt)
+    w = lambda a: oracle.to_f32(a, dt).astype(np.float64)
+    o = oracle.gemm_epilog(An, Bn, "RELU_AUX_BIAS", bias=np_of(bias, dt), ab=dt, trans_a=ta, trans_b=tb)
+    assert o["D"].shape == (m, n)
+    assert np.array_equal(w(o["D"]), np.maximum(pre, 0))
+    assert np.array_equal(o["mask"], pack_mask_np(pre > 0))
+    o = oracle.gemm_epilog(An, Bn, "NONE", ab=dt, trans_a=ta, trans_b=tb)
+    assert np.array_equal(w(o["D"]), a64 @ b64)
+    prod = A2.double().numpy() @ B2.double().numpy()
+    dz = np.where(pre > 0, prod, 0.0)
+    A2n = np.ascontiguousarray(np_of(A2, dt).T) if ta else np_of(A2, dt)
+    B2n = np.ascontiguousarray(np_of(B2, dt).T) if tb else np_of(B2, dt)
+    o = oracle.gemm_epilog(A2n, B2n, "DRELU_BGRAD", mask=pack_mask_np(pre > 0), ab=dt, trans_a=ta, trans_b=tb)
+    assert np.array_equal(w(o["D"]), dz)
+    assert np.array_equal(w(o["bgrad"]), dz.sum(axis=1))
+
+
+def test_transposed_operand_shapes_rejected():
+    # a (k, m) array without trans_a is a different problem; mismatched inner sizes raise
+    A = np.ones((16, 40), np.float32)
+    B = np.ones((24, 16), np.float32)
+    with pytest.raises(AssertionError):
+        oracle.gemm_epilog(A, B, "NONE", ab="f32")
+    assert oracle.gemm_epilog(A, B, "NONE", ab="f32", trans_a=True, trans_b=True)["D"].shape == (40, 24)
+
+
 def test_integer_gelu_plumbing():
     # bias indexing and output rounding of GELU_BIAS on exact pre-activations
     m, n, k = 40, 24, 16
