@@ -6,8 +6,9 @@ metric is 2mnk / time in TFLOP/s and its fraction of the dense fp16 MFMA peak.
 
 Also measured (reported under "variants", not in "value"): the unfused three-kernel
 chain on the same inputs, bf16 GELU_BIAS, RELU_AUX_BIAS, the bf16 8192^3
-RELU_AUX_BIAS + DRELU_BGRAD pair and the large (65536,16384)x(16384,8192) fp16 shape
-with and without the mask. The CPU oracle is timed on the headline workload on the
+RELU_AUX_BIAS + DRELU_BGRAD pair, the rest of that layer's backward with transposed
+operands, a whole two-layer training step at 8192, the square 4096^3 fused/unfused
+pair, and the large (65536,16384)x(16384,8192) fp16 shape with and without the mask. The CPU oracle is timed on the headline workload on the
 host cores, in whole passes for a bounded time (about 12 s).
 
 Prints one JSON line (the last line of stdout).
@@ -44,6 +45,10 @@ VARIANTS = {
     # (DRELU_BGRAD on the W^T of the (k, m) weight) and dW = dZ . X^T (B as stored X)
     "mlp8192_bwd_wt_drelu_bgrad_bf16": ("mlp_bf16_8192", "DRELU_BGRAD", "bf16", True, "TN"),
     "mlp8192_dw_bf16": ("mlp_bf16_8192", "NONE", "bf16", True, "NT"),
+    # the square size the epilog-configuration page recommends for comparing fused and
+    # unfused latency
+    "square4096_relu_bias_f16": ("square_f16_4096", "RELU_BIAS", "f16", False),
+    "square4096_unfused_f16": ("square_f16_4096", "RELU_BIAS_UNFUSED", "f16", False),
 }
 LAYOUTS = {"NN": (False, False), "TN": (True, False), "NT": (False, True)}
 
@@ -188,6 +193,54 @@ def run_variant(ge, W, epilog, dtype, steps, warmup, device_rng, layout="NN"):
     return out
 
 
+def run_mlp_step(steps: int, warmup: int, size: int = 8192, dtype: str = "bf16"):
+    """One training step of the two-layer perceptron (batch, input, hidden and output
+    all `size`): RELU_AUX_BIAS and NONE forward, then dW2 = dY H^T, the DRELU_BGRAD
+    product W2^T dY with db1, and dW1 = dZ1 X^T, five executes per step. Inputs drawn
+    on the device with the distributions of gemm_epilogues_epilog_amd.inputs.mlp_case."""
+    import torch
+    from gemm_epilogues_epilog_amd import inputs
+    from gemm_epilogues_epilog_amd.mlp import MLP2Step
+    t = inputs.TORCH_DT[dtype]
+    g = torch.Generator(device="cuda").manual_seed(0)
+    n = size
+    X = torch.randn(n, n, device="cuda", generator=g).to(t)
+    W1 = (torch.randn(n, n, device="cuda", generator=g) * n ** -0.5).to(t)
+    b1 = (torch.randn(n, device="cuda", generator=g) * 0.02).to(t)
+    W2 = (torch.randn(n, n, device="cuda", generator=g) * n ** -0.5).to(t)
+    dY = torch.randn(n, n, device="cuda", generator=g).to(t)
+    t0 = time.perf_counter()
+    st = MLP2Step(n, n, n, n, dtype)
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    for _ in range(warmup):
+        st.step(X, W1, b1, W2, dY)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        st.step(X, W1, b1, W2, dY)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        st.step(X, W1, b1, W2, dY)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    per = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    kernels = [p.describe() for p in st.plans]
+    flops = st.flops()
+    st.free()
+    del X, W1, b1, W2, dY, st
+    torch.cuda.empty_cache()
+    med = per[len(per) // 2]
+    return {"what": f"2-layer MLP training step, batch = input = hidden = output = {n}, {dtype}: "
+                    "RELU_AUX_BIAS, NONE; dW2 (B^T), DRELU_BGRAD + db1 (A^T), dW1 (B^T)",
+            "plan_ms": round(plan_ms, 3), "wall_ms_per_step": round(wall_ms, 4), "median_ms": round(med, 4),
+            "p10_ms": round(per[len(per) // 10], 4), "p90_ms": round(per[(len(per) * 9) // 10], 4),
+            "tflops": round(flops / (wall_ms * 1e-3) / 1e12, 1), "kernels": kernels}
+
+
 def cpu_baseline(W, budget_s: float):
     """The CPU oracle on the whole headline workload, repeated until about budget_s
     seconds have passed (at least one full pass); inputs are drawn before timing."""
@@ -223,7 +276,7 @@ def main():
     ap.add_argument("--skip-cpu", action="store_true", help="leave out the cpu_baseline leg (profiling runs)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run the 1 GiB copy that calibrates the HBM byte counters")
-    ap.add_argument("--only", choices=sorted(VARIANTS),
+    ap.add_argument("--only", choices=sorted(VARIANTS) + ["mlp8192_train_step_bf16"],
                     help="time one variant alone (--steps executes after --warmup) and print its line; "
                          "for profiling runs")
     args = ap.parse_args()
@@ -240,6 +293,9 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_probe:
         copy_probe()
+        return
+    if args.only == "mlp8192_train_step_bf16":
+        print(json.dumps({"variant": args.only, **run_mlp_step(args.steps, args.warmup)}), flush=True)
         return
     if args.only:
         wname, ep, dt, dev_rng, *lay = VARIANTS[args.only]
@@ -282,6 +338,12 @@ def main():
         unf = variants["ffn_unfused_f16"]["median_ms"]
         variants["ffn_fusion_saving"] = {"fused_ms": round(fused_ms, 4), "unfused_ms": unf,
                                          "saving_frac": round(1 - fused_ms / unf, 4)}
+        sq_f, sq_u = variants["square4096_relu_bias_f16"]["median_ms"], variants["square4096_unfused_f16"]["median_ms"]
+        variants["square4096_fusion_saving"] = {"fused_ms": sq_f, "unfused_ms": sq_u,
+                                                "saving_frac": round(1 - sq_f / sq_u, 4)}
+        log("[bench] variant mlp8192_train_step_bf16")
+        variants["mlp8192_train_step_bf16"] = run_mlp_step(max(3, vsteps // 5), 3)
+        log(f"[bench]   {variants['mlp8192_train_step_bf16']}")
 
     del A, B, D
     torch.cuda.empty_cache()

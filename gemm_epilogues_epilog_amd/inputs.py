@@ -25,6 +25,7 @@ TORCH_DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
 # tensor tags (part of the seed)
 TAG_A, TAG_B, TAG_BIAS, TAG_A2, TAG_B2 = 1, 2, 3, 4, 5
+TAG_X, TAG_W1, TAG_B1, TAG_W2, TAG_DY = 6, 7, 8, 9, 10
 
 
 def _mix(seed: int, tag: int, block: int) -> int:
@@ -121,6 +122,10 @@ WORKLOADS: Dict[str, Workload] = {w.name: w for w in [
     # 2-layer MLP training pair, batch 8192, hidden 8192
     _w(name="mlp_bf16_8192", m=8192, n=8192, k=8192, dtype="bf16", epilog="RELU_AUX_BIAS",
        std_a=8192 ** -0.5, std_b=1.0, std_bias=0.02, std_a2=8192 ** -0.5, std_b2=1.0),
+    # the square benchmark size the epilog-configuration page recommends for comparing
+    # fused and unfused latency (distributions as for the FFN layer)
+    _w(name="square_f16_4096", m=4096, n=4096, k=4096, dtype="f16", epilog="RELU_BIAS",
+       std_a=1.0 / 64, std_b=1.0 / 64, std_bias=0.02),
     # the H200 comparison shape, RELU_BIAS and (same inputs) RELU_AUX_BIAS
     _w(name="large_f16_65536x8192x16384", m=65536, n=8192, k=16384, dtype="f16", epilog="RELU_BIAS",
        std_a=1.0 / 128, std_b=1.0 / 128, std_bias=0.02),
@@ -136,6 +141,15 @@ def small_case(m: int, n: int, k: int, dtype: str, std: float = 1.0, std_bias: f
     return (normal(m, k, std, dtype, seed, TAG_A), normal(k, n, std, dtype, seed, TAG_B),
             vector(m, std_bias, v, seed, TAG_BIAS), normal(m, k, std, dtype, seed, TAG_A2),
             normal(k, n, std, dtype, seed, TAG_B2))
+
+
+def mlp_case(d: int, h: int, o: int, batch: int, dtype: str, seed: int = 0) -> Tuple[torch.Tensor, ...]:
+    """X (d, batch) ~ N(0,1), W1 (h, d) ~ N(0, 1/sqrt(d)), b1 (h) ~ N(0, 0.02),
+    W2 (o, h) ~ N(0, 1/sqrt(h)) and the output gradient dY (o, batch) ~ N(0,1) of a
+    two-layer perceptron step (features along rows, the batch along columns)."""
+    return (normal(d, batch, 1.0, dtype, seed, TAG_X), normal(h, d, d ** -0.5, dtype, seed, TAG_W1),
+            vector(h, 0.02, dtype, seed, TAG_B1), normal(o, h, h ** -0.5, dtype, seed, TAG_W2),
+            normal(o, batch, 1.0, dtype, seed, TAG_DY))
 
 
 def integer_case(m: int, n: int, k: int, dtype: str, seed: int = 0, vec: Optional[str] = None):
