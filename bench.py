@@ -193,6 +193,30 @@ def run_variant(ge, W, epilog, dtype, steps, warmup, device_rng, layout="NN"):
     return out
 
 
+def run_autotune(ge, W, steps: int, warmup: int, repeats: int = 20):
+    """The plan's table choice against gemm_epilog_autotune's measured choice on the
+    same inputs: both timed like a variant, plus the wall time of the search."""
+    import torch
+    A, B, bias = device_inputs(W, device_rng=False)
+    D = torch.empty(W.m, W.n, dtype=A.dtype, device="cuda")
+    h = ge.gemm_epilog_plan(W.m, W.n, W.k, (W.dtype, W.dtype, W.dtype), W.epilog)
+    args = (A, B, bias, D, None, None)
+    before = ge.gemm_epilog_describe(h)
+    r0 = time_execute(ge, h, args, steps, warmup, warm_s=0.3)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    best = ge.gemm_epilog_autotune(h, *args, repeats=repeats)
+    search_ms = (time.perf_counter() - t0) * 1e3
+    after = ge.gemm_epilog_describe(h)
+    r1 = time_execute(ge, h, args, steps, warmup, warm_s=0.3)
+    ge.gemm_epilog_free(h)
+    del A, B, D
+    torch.cuda.empty_cache()
+    return {"workload": W.name, "epilog": W.epilog, "table_kernel": before, "table_median_ms": round(r0["event_ms_median"], 4),
+            "tuned_kernel": after, "tuned_median_ms": round(r1["event_ms_median"], 4),
+            "search_best_ms": round(best, 4), "search_wall_ms": round(search_ms, 1), "repeats": repeats}
+
+
 def run_mlp_step(steps: int, warmup: int, size: int = 8192, dtype: str = "bf16"):
     """One training step of the two-layer perceptron (batch, input, hidden and output
     all `size`): RELU_AUX_BIAS and NONE forward, then dW2 = dY H^T, the DRELU_BGRAD
@@ -276,7 +300,7 @@ def main():
     ap.add_argument("--skip-cpu", action="store_true", help="leave out the cpu_baseline leg (profiling runs)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run the 1 GiB copy that calibrates the HBM byte counters")
-    ap.add_argument("--only", choices=sorted(VARIANTS) + ["mlp8192_train_step_bf16"],
+    ap.add_argument("--only", choices=sorted(VARIANTS) + ["mlp8192_train_step_bf16", "autotune_small", "autotune_headline"],
                     help="time one variant alone (--steps executes after --warmup) and print its line; "
                          "for profiling runs")
     args = ap.parse_args()
@@ -293,6 +317,11 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_probe:
         copy_probe()
+        return
+    if args.only in ("autotune_small", "autotune_headline"):
+        wname = "relu_bias_f16_1024x512x2048" if args.only == "autotune_small" else inputs.HEADLINE
+        print(json.dumps({"variant": args.only, **run_autotune(ge, inputs.WORKLOADS[wname], args.steps, args.warmup)}),
+              flush=True)
         return
     if args.only == "mlp8192_train_step_bf16":
         print(json.dumps({"variant": args.only, **run_mlp_step(args.steps, args.warmup)}), flush=True)
@@ -341,6 +370,10 @@ def main():
         sq_f, sq_u = variants["square4096_relu_bias_f16"]["median_ms"], variants["square4096_unfused_f16"]["median_ms"]
         variants["square4096_fusion_saving"] = {"fused_ms": sq_f, "unfused_ms": sq_u,
                                                 "saving_frac": round(1 - sq_f / sq_u, 4)}
+        for wname in ("relu_bias_f16_1024x512x2048", inputs.HEADLINE):
+            log(f"[bench] autotune {wname}")
+            variants[f"autotune_{wname}"] = run_autotune(ge, inputs.WORKLOADS[wname], vsteps, vwarm)
+            log(f"[bench]   {variants[f'autotune_{wname}']}")
         log("[bench] variant mlp8192_train_step_bf16")
         variants["mlp8192_train_step_bf16"] = run_mlp_step(max(3, vsteps // 5), 3)
         log(f"[bench]   {variants['mlp8192_train_step_bf16']}")

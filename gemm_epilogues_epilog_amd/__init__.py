@@ -5,9 +5,9 @@ libgemm_epilog.so (built by gemm_epilogues_epilog_amd/build.py). There is no CPU
 fallback; if the library is missing every call raises.
 
 Low-level functions carry the names of the C ABI in include/gemm_epilog.h:
-gemm_epilog_plan, gemm_epilog_plan_ex, gemm_epilog_execute, gemm_epilog_free,
-gemm_epilog_aux_bytes, gemm_epilog_workspace_bytes, gemm_epilog_describe,
-gemm_epilog_status_string.
+gemm_epilog_plan, gemm_epilog_plan_ex, gemm_epilog_execute, gemm_epilog_autotune,
+gemm_epilog_free, gemm_epilog_aux_bytes, gemm_epilog_workspace_bytes,
+gemm_epilog_describe, gemm_epilog_status_string.
 Pointers may be given as torch tensors (device memory), integers or None.
 
 `Matmul` wraps them in the stateful plan / execute / free object with a context
@@ -32,7 +32,8 @@ EPILOG = {"NONE": 0, "RELU_BIAS": 1, "GELU_BIAS": 2, "RELU_AUX_BIAS": 3, "DRELU_
           "RELU_BIAS_UNFUSED": 100}
 STATUS = {0: "GE_OK", 1: "GE_ERR_INVALID_VALUE", 2: "GE_ERR_NOT_SUPPORTED", 3: "GE_ERR_NULL_POINTER",
           4: "GE_ERR_MISALIGNED", 5: "GE_ERR_ALLOC", 6: "GE_ERR_HIP"}
-EXPORTS = ("gemm_epilog_plan", "gemm_epilog_plan_ex", "gemm_epilog_execute", "gemm_epilog_free",
+EXPORTS = ("gemm_epilog_plan", "gemm_epilog_plan_ex", "gemm_epilog_execute", "gemm_epilog_autotune",
+           "gemm_epilog_free",
            "gemm_epilog_aux_bytes", "gemm_epilog_workspace_bytes", "gemm_epilog_describe",
            "gemm_epilog_status_string")
 OP_N, OP_T = 0, 1
@@ -67,6 +68,8 @@ def load() -> ctypes.CDLL:
     L.gemm_epilog_plan_ex.restype = c_int
     L.gemm_epilog_execute.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
     L.gemm_epilog_execute.restype = c_int
+    L.gemm_epilog_autotune.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, c_int, ctypes.POINTER(ctypes.c_float)]
+    L.gemm_epilog_autotune.restype = c_int
     L.gemm_epilog_free.argtypes = [vp]
     L.gemm_epilog_free.restype = c_int
     L.gemm_epilog_aux_bytes.argtypes = [i64, i64]
@@ -147,6 +150,26 @@ def gemm_epilog_execute(handle, A, B, bias=None, D=None, aux=None, bgrad=None, s
     return st
 
 
+def gemm_epilog_autotune(handle, A, B, bias=None, D=None, aux=None, bgrad=None, stream=None, repeats: int = 10,
+                         check: bool = True):
+    """Time the plan's candidate configurations on these operands and keep the fastest.
+    Returns the chosen configuration's mean ms per execute (or (status, ms) with
+    check=False). Synchronises the stream."""
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream().cuda_stream
+    elif not isinstance(stream, int):
+        stream = stream.cuda_stream
+    ms = ctypes.c_float(0.0)
+    st = load().gemm_epilog_autotune(handle, _ptr(A), _ptr(B), _ptr(bias), _ptr(D), _ptr(aux), _ptr(bgrad), stream,
+                                     int(repeats), ctypes.byref(ms))
+    if not check:
+        return st, ms.value
+    if st != 0:
+        raise GemmEpilogError(st, "gemm_epilog_autotune")
+    return ms.value
+
+
 def gemm_epilog_free(handle) -> int:
     return int(load().gemm_epilog_free(handle))
 
@@ -191,7 +214,8 @@ class Matmul:
     def describe(self) -> str:
         return gemm_epilog_describe(self.handle) if self.handle is not None else ""
 
-    def execute(self, A, B, bias=None, relu_aux=None, out=None, bgrad=None, stream=None):
+    def _outputs(self, A, B, relu_aux, out, bgrad):
+        """Check the operands against the plan and allocate the outputs not given."""
         import torch
         if self.handle is None:
             self.plan()
@@ -213,12 +237,27 @@ class Matmul:
             if bgrad is None:
                 vt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[self.vec_dtype]
                 bgrad = torch.empty(self.m, dtype=vt, device=A.device)
-        gemm_epilog_execute(self.handle, A, B, bias, out, relu_aux, bgrad, stream)
+        return relu_aux, out, bgrad
+
+    def _result(self, out, relu_aux, bgrad):
         if self.epilog == "RELU_AUX_BIAS":
             return out, {"relu_aux": relu_aux}
         if self.epilog == "DRELU_BGRAD":
             return out, {"drelu_bgrad": bgrad}
         return out
+
+    def execute(self, A, B, bias=None, relu_aux=None, out=None, bgrad=None, stream=None):
+        relu_aux, out, bgrad = self._outputs(A, B, relu_aux, out, bgrad)
+        gemm_epilog_execute(self.handle, A, B, bias, out, relu_aux, bgrad, stream)
+        return self._result(out, relu_aux, bgrad)
+
+    def autotune(self, A, B, bias=None, relu_aux=None, out=None, bgrad=None, stream=None, repeats: int = 10):
+        """Time the candidate configurations on these operands and keep the fastest in
+        the plan (gemm_epilog_autotune). Returns (ms per execute, the result as
+        execute returns it)."""
+        relu_aux, out, bgrad = self._outputs(A, B, relu_aux, out, bgrad)
+        ms = gemm_epilog_autotune(self.handle, A, B, bias, out, relu_aux, bgrad, stream, repeats)
+        return ms, self._result(out, relu_aux, bgrad)
 
     def free(self):
         if self.handle is not None:

@@ -15,6 +15,8 @@
 #include <cstring>
 #include <new>
 #include <string>
+#include <utility>
+#include <vector>
 
 #include "gemm_epilog.h"
 #include "launch.hpp"
@@ -40,6 +42,8 @@ struct ge_plan {
   float* sk_partial;       // split tail: one fp32 tile per split workgroup
   uint32_t* sk_flag;       // split tail: epoch of each published partial
   int persist_grid = 0;    // persistent workgroups (0: one workgroup per tile)
+  int cus;                 // compute units of the device
+  bool allow_split, allow_persist;
   uint32_t epoch;          // execute counter, 1 .. 2^31 - 1
   std::string desc;
 };
@@ -133,60 +137,10 @@ gek::LaunchFn lookup(ge_dtype_t ab, int ep, int cfg, int lay) {
   return nullptr;
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* gemm_epilog_status_string(ge_status_t s) {
-  switch (s) {
-    case GE_OK: return "GE_OK";
-    case GE_ERR_INVALID_VALUE: return "GE_ERR_INVALID_VALUE: a size or enum value is out of range";
-    case GE_ERR_NOT_SUPPORTED: return "GE_ERR_NOT_SUPPORTED: dtype combination or shape not supported";
-    case GE_ERR_NULL_POINTER: return "GE_ERR_NULL_POINTER: a required pointer is NULL";
-    case GE_ERR_MISALIGNED: return "GE_ERR_MISALIGNED: a pointer violates its alignment rule";
-    case GE_ERR_ALLOC: return "GE_ERR_ALLOC: allocation failed";
-    case GE_ERR_HIP: return "GE_ERR_HIP: a HIP runtime call failed";
-  }
-  return "unknown status";
-}
-
-size_t gemm_epilog_aux_bytes(int64_t m, int64_t n) {
-  if (m < 1 || n < 1) return 0;
-  return (size_t)4 * (size_t)cdiv(m, 32) * (size_t)n;
-}
-
-ge_status_t gemm_epilog_plan(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt, ge_epilog_t ep, ge_handle_t* out) {
-  return gemm_epilog_plan_ex(m, n, k, dt, ep, GE_OP_N, GE_OP_N, out);
-}
-
-ge_status_t gemm_epilog_plan_ex(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt, ge_epilog_t ep, ge_op_t op_a,
-                                ge_op_t op_b, ge_handle_t* out) {
-  // ---- host-only validation (no HIP call before this block passes) ----
-  if (!out) return GE_ERR_NULL_POINTER;
-  if (m < 1 || m > 0x7fffffffLL || n < 1 || n > (1LL << 20) || k < 1 || k > (1LL << 20))
-    return GE_ERR_INVALID_VALUE;
-  if (!known_dtype(dt.ab) || !known_dtype(dt.d) || !known_dtype(dt.vec) || !known_epilog(ep))
-    return GE_ERR_INVALID_VALUE;
-  if ((op_a != GE_OP_N && op_a != GE_OP_T) || (op_b != GE_OP_N && op_b != GE_OP_T)) return GE_ERR_INVALID_VALUE;
-  if (dt.d != dt.ab) return GE_ERR_NOT_SUPPORTED;
-  if (dt.vec != dt.d && dt.vec != GE_F32) return GE_ERR_NOT_SUPPORTED;
-  const int64_t mult = dt.ab == GE_F32 ? 4 : 8;   // 16-byte rows
-  if (n % mult != 0 || k % mult != 0) return GE_ERR_NOT_SUPPORTED;
-  const int lay = (op_a == GE_OP_T ? 1 : 0) | (op_b == GE_OP_T ? 2 : 0);
-  if (lay != 0 && dt.ab == GE_F32) return GE_ERR_NOT_SUPPORTED;
-  // A stored as (k, m): its rows hold m values, so m follows the row rules of n
-  if (op_a == GE_OP_T && (m > (1LL << 20) || m % mult != 0)) return GE_ERR_NOT_SUPPORTED;
-  const int64_t tiles_bound = cdiv(m, 64) * cdiv(n, 64);
-  if (tiles_bound > 0x7fffffffLL) return GE_ERR_NOT_SUPPORTED;   // grid size
-
-  // ---- device query ----
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return GE_ERR_HIP;
-  hipDeviceProp_t prop;
-  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GE_ERR_HIP;
-  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return GE_ERR_NOT_SUPPORTED;
-  const int cus = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
-
+// A plan for a validated problem with a given tile configuration; allow_split and
+// allow_persist permit the split tail and the persistent kernel where they apply.
+ge_status_t build_plan(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt, ge_epilog_t ep, int lay, int dev, int cus,
+                       int cfg, bool allow_split, bool allow_persist, ge_handle_t* out) {
   ge_plan* h = new (std::nothrow) ge_plan();
   if (!h) return GE_ERR_ALLOC;
   h->m = m;
@@ -196,7 +150,10 @@ ge_status_t gemm_epilog_plan_ex(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt,
   h->ep = ep;
   h->device = dev;
   h->lay = lay;
-  h->cfg = choose_cfg(m, (int)n, dt.ab, cus, lay);
+  h->cus = cus;
+  h->cfg = cfg;
+  h->allow_split = allow_split;
+  h->allow_persist = allow_persist;
   const gek::TileCfg& tc = gek::kTiles[h->cfg];
   h->tiles_m = (int)cdiv(m, tc.bm);
   h->tiles_n = (int)cdiv(n, tc.bn);
@@ -223,7 +180,7 @@ ge_status_t gemm_epilog_plan_ex(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt,
   // than that, i.e. when the last round is at most half full)
   const int tiles = h->tiles_m * h->tiles_n;
   h->dp_tiles = tiles;
-  if (gek::cfg_can_split(h->cfg) && lay == 0 && !env_off("GE_STREAMK")) {
+  if (gek::cfg_can_split(h->cfg) && lay == 0 && allow_split) {
     const int kt = (int)cdiv(k, tc.bk);
     const int rem = tiles % cus;
     if (rem != 0 && (int64_t)rem * 2 <= (int64_t)cus && kt >= 2) {
@@ -239,7 +196,7 @@ ge_status_t gemm_epilog_plan_ex(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt,
   }
 
   // ---- persistent kernel: one workgroup per compute unit walks the tiles ----
-  if (gek::cfg_can_persist(h->cfg) && lay == 0 && h->dp_tiles == tiles && !env_off("GE_PERSIST")) {
+  if (gek::cfg_can_persist(h->cfg) && lay == 0 && h->dp_tiles == tiles && allow_persist) {
     const int kt = (int)cdiv(k, tc.bk);
     if (k % tc.bk == 0 && kt % tc.stages == 0 && kt >= 2 * tc.stages) h->persist_grid = std::min(tiles, cus);
   }
@@ -296,6 +253,64 @@ ge_status_t gemm_epilog_plan_ex(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt,
   return GE_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+const char* gemm_epilog_status_string(ge_status_t s) {
+  switch (s) {
+    case GE_OK: return "GE_OK";
+    case GE_ERR_INVALID_VALUE: return "GE_ERR_INVALID_VALUE: a size or enum value is out of range";
+    case GE_ERR_NOT_SUPPORTED: return "GE_ERR_NOT_SUPPORTED: dtype combination or shape not supported";
+    case GE_ERR_NULL_POINTER: return "GE_ERR_NULL_POINTER: a required pointer is NULL";
+    case GE_ERR_MISALIGNED: return "GE_ERR_MISALIGNED: a pointer violates its alignment rule";
+    case GE_ERR_ALLOC: return "GE_ERR_ALLOC: allocation failed";
+    case GE_ERR_HIP: return "GE_ERR_HIP: a HIP runtime call failed";
+  }
+  return "unknown status";
+}
+
+size_t gemm_epilog_aux_bytes(int64_t m, int64_t n) {
+  if (m < 1 || n < 1) return 0;
+  return (size_t)4 * (size_t)cdiv(m, 32) * (size_t)n;
+}
+
+ge_status_t gemm_epilog_plan(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt, ge_epilog_t ep, ge_handle_t* out) {
+  return gemm_epilog_plan_ex(m, n, k, dt, ep, GE_OP_N, GE_OP_N, out);
+}
+
+ge_status_t gemm_epilog_plan_ex(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt, ge_epilog_t ep, ge_op_t op_a,
+                                ge_op_t op_b, ge_handle_t* out) {
+  // ---- host-only validation (no HIP call before this block passes) ----
+  if (!out) return GE_ERR_NULL_POINTER;
+  if (m < 1 || m > 0x7fffffffLL || n < 1 || n > (1LL << 20) || k < 1 || k > (1LL << 20))
+    return GE_ERR_INVALID_VALUE;
+  if (!known_dtype(dt.ab) || !known_dtype(dt.d) || !known_dtype(dt.vec) || !known_epilog(ep))
+    return GE_ERR_INVALID_VALUE;
+  if ((op_a != GE_OP_N && op_a != GE_OP_T) || (op_b != GE_OP_N && op_b != GE_OP_T)) return GE_ERR_INVALID_VALUE;
+  if (dt.d != dt.ab) return GE_ERR_NOT_SUPPORTED;
+  if (dt.vec != dt.d && dt.vec != GE_F32) return GE_ERR_NOT_SUPPORTED;
+  const int64_t mult = dt.ab == GE_F32 ? 4 : 8;   // 16-byte rows
+  if (n % mult != 0 || k % mult != 0) return GE_ERR_NOT_SUPPORTED;
+  const int lay = (op_a == GE_OP_T ? 1 : 0) | (op_b == GE_OP_T ? 2 : 0);
+  if (lay != 0 && dt.ab == GE_F32) return GE_ERR_NOT_SUPPORTED;
+  // A stored as (k, m): its rows hold m values, so m follows the row rules of n
+  if (op_a == GE_OP_T && (m > (1LL << 20) || m % mult != 0)) return GE_ERR_NOT_SUPPORTED;
+  const int64_t tiles_bound = cdiv(m, 64) * cdiv(n, 64);
+  if (tiles_bound > 0x7fffffffLL) return GE_ERR_NOT_SUPPORTED;   // grid size
+
+  // ---- device query ----
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return GE_ERR_HIP;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GE_ERR_HIP;
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return GE_ERR_NOT_SUPPORTED;
+  const int cus = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
+
+  return build_plan(m, n, k, dt, ep, lay, dev, cus, choose_cfg(m, (int)n, dt.ab, cus, lay), !env_off("GE_STREAMK"),
+                    !env_off("GE_PERSIST"), out);
+}
+
 ge_status_t gemm_epilog_execute(ge_handle_t h, const void* A, const void* B, const void* bias, void* D, void* aux,
                                 void* bgrad, void* stream) {
   // ---- host-only validation ----
@@ -350,6 +365,95 @@ ge_status_t gemm_epilog_execute(ge_handle_t h, const void* A, const void* B, con
       return GE_ERR_HIP;
     if (gek::launch_relu((int)h->dt.d, h->t2, D, h->m, h->n, s) != hipSuccess) return GE_ERR_HIP;
   }
+  return GE_OK;
+}
+
+ge_status_t gemm_epilog_autotune(ge_handle_t h, const void* A, const void* B, const void* bias, void* D, void* aux,
+                                 void* bgrad, void* stream, int repeats, float* best_ms) {
+  if (!h) return GE_ERR_NULL_POINTER;
+  if (repeats < 1 || repeats > 1000) return GE_ERR_INVALID_VALUE;
+  // the argument rules of execute, checked once on the plan itself before any timing
+  if (ge_status_t st = gemm_epilog_execute(h, A, B, bias, D, aux, bgrad, stream); st != GE_OK) return st;
+
+  // Candidates: every configuration the plan's types and operand layout can run, with
+  // and without the split tail; the persistent kernel wherever it applies.
+  struct Cand {
+    int cfg;
+    bool split, persist;
+  };
+  std::vector<Cand> cands;
+  if (h->dt.ab == GE_F32) {
+    cands = {{gek::CFG_S, false, false}, {gek::CFG_M, false, false}};
+  } else if (h->lay != 0) {
+    cands = {{gek::CFG_LH, false, false}, {gek::CFG_LM, false, false}};
+  } else {
+    cands = {{gek::CFG_L, true, true},   {gek::CFG_L, false, true},   {gek::CFG_L, false, false},
+             {gek::CFG_LH, true, false}, {gek::CFG_LH, false, false}, {gek::CFG_LM, true, false},
+             {gek::CFG_LM, false, false}};
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+    if (e0) hipEventDestroy(e0);
+    return GE_ERR_HIP;
+  }
+  // time one plan: one warm-up execute, then `repeats` between two events
+  auto time_plan = [&](ge_plan* c, float* ms) -> ge_status_t {
+    if (ge_status_t st = gemm_epilog_execute(c, A, B, bias, D, aux, bgrad, stream); st != GE_OK) return st;
+    if (hipEventRecord(e0, s) != hipSuccess) return GE_ERR_HIP;
+    for (int r = 0; r < repeats; ++r)
+      if (ge_status_t st = gemm_epilog_execute(c, A, B, bias, D, aux, bgrad, stream); st != GE_OK) return st;
+    if (hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess) return GE_ERR_HIP;
+    return hipEventElapsedTime(ms, e0, e1) == hipSuccess ? GE_OK : GE_ERR_HIP;
+  };
+
+  ge_status_t st = GE_OK;
+  float best = 0.0f;
+  if ((st = time_plan(h, &best)) != GE_OK) {
+    hipEventDestroy(e0);
+    hipEventDestroy(e1);
+    return st;
+  }
+  ge_plan* winner = nullptr;   // a better plan than h, if one is found
+  std::vector<std::string> seen = {h->desc};
+  for (const Cand& c : cands) {
+    ge_handle_t t = nullptr;
+    if (build_plan(h->m, h->n, h->k, h->dt, h->ep, h->lay, h->device, h->cus, c.cfg, c.split, c.persist, &t) !=
+        GE_OK)
+      continue;   // e.g. no workspace for this configuration: not a candidate
+    if (std::find(seen.begin(), seen.end(), t->desc) != seen.end()) {   // the same kernels as one timed already
+      gemm_epilog_free(t);
+      continue;
+    }
+    seen.push_back(t->desc);
+    float ms = 0.0f;
+    if ((st = time_plan(t, &ms)) != GE_OK) {
+      gemm_epilog_free(t);
+      break;
+    }
+    if (ms < best) {
+      best = ms;
+      if (winner) gemm_epilog_free(winner);
+      winner = t;
+    } else {
+      gemm_epilog_free(t);
+    }
+  }
+  hipEventDestroy(e0);
+  hipEventDestroy(e1);
+  if (st != GE_OK) {
+    if (winner) gemm_epilog_free(winner);
+    return st;
+  }
+  if (winner) {
+    // the stream is idle (every timing ended with an event synchronisation): the plan
+    // takes the winner's configuration and workspace, the winner's struct the old ones
+    std::swap(*h, *winner);
+    gemm_epilog_free(winner);
+    // leave the outputs as an execute of the chosen configuration writes them
+    if ((st = gemm_epilog_execute(h, A, B, bias, D, aux, bgrad, stream)) != GE_OK) return st;
+  }
+  if (best_ms) *best_ms = best / (float)repeats;
   return GE_OK;
 }
 

@@ -164,6 +164,32 @@ ge_status_t gemm_epilog_plan_ex(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt,
 ge_status_t gemm_epilog_execute(ge_handle_t h, const void* A, const void* B, const void* bias, void* D,
                                 void* aux, void* bgrad, void* stream);
 
+/*
+ * gemm_epilog_autotune - time the kernel configurations that can run this plan on the
+ * caller's own operands and keep the fastest in the plan. The plan's configuration
+ * comes from a fixed per-shape table; this is the measured search that [P1] (final
+ * paragraph: hand tuning through the algorithm heuristic) and [P2] (body, plan step:
+ * the plan picks the best algorithm for the problem) describe. It runs on the real
+ * data because the matrix cores' clock under the power limit depends on the values.
+ *   h, A, B, bias, D, aux, bgrad, stream : as for gemm_epilog_execute (same rules and
+ *            errors, checked first). D, aux and bgrad are written: on return they hold
+ *            what one execute of the chosen configuration writes.
+ *   repeats : timed executes per candidate, 1..1000 (else GE_ERR_INVALID_VALUE), each
+ *            candidate after one untimed execute.
+ *   best_ms : optional (may be NULL): receives the chosen configuration's mean time per
+ *            execute in milliseconds, from HIP events on `stream`.
+ * Candidates: for fp32 the 64x64 and 128x128 tiles; for fp16/bf16 with transposed
+ * operands the 256x256 and 128x128 lockstep tiles; otherwise the 256x256 tile
+ * (persistent, one workgroup per tile, with copies on all or half of the waves) and
+ * the 128x128 tile, each with and without the split tail where it applies. A candidate
+ * whose workspace cannot be allocated is skipped. The call synchronises `stream`, must
+ * not overlap another execute of this plan, and runs on the device current at plan
+ * time. On an error the plan keeps its configuration (GE_ERR_HIP if a launch or an
+ * event call failed).
+ */
+ge_status_t gemm_epilog_autotune(ge_handle_t h, const void* A, const void* B, const void* bias, void* D, void* aux,
+                                 void* bgrad, void* stream, int repeats, float* best_ms);
+
 /* gemm_epilog_free - release a plan and its workspace. NULL is accepted (GE_OK).
  * Must not be called while an execute on this plan may still be running. */
 ge_status_t gemm_epilog_free(ge_handle_t h);

@@ -105,6 +105,13 @@ def test_plan_null_out():
     assert st == 3
 
 
+def test_autotune_null_handle():
+    lib = ge.load()
+    ms = ctypes.c_float(0.0)
+    assert lib.gemm_epilog_autotune(None, 16, 16, 16, 16, None, None, None, 10, ctypes.byref(ms)) == 3
+    assert lib.gemm_epilog_autotune(None, 16, 16, 16, 16, None, None, None, 0, None) == 3
+
+
 def test_execute_null_handle_and_free_null():
     lib = ge.load()
     assert lib.gemm_epilog_execute(None, 16, 16, 16, 16, None, None, None) == 3
