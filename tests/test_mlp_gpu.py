@@ -46,3 +46,36 @@ def test_mlp_step_rejects_bad_sizes(gpu):
         MLP2Step(72, 130, 40, 264, "bf16")
     with pytest.raises(ValueError):
         MLP2Step(72, 136, 40, 264, "f32")
+
+
+def test_mlp_step_8192_sampled_rows(gpu):
+    # the step as the benchmark times it (all sizes 8192, bf16): every stage's output on
+    # sampled 32-row groups against the oracle on that stage's GPU inputs
+    from gemm_epilogues_epilog_amd.mlp import MLP2Step
+    n = 8192
+    print("[case] mlp step 8192 bf16: generating inputs", flush=True)
+    X, W1, b1, W2, dY = inputs.mlp_case(n, n, n, n, "bf16")
+    with MLP2Step(n, n, n, n, "bf16") as st:
+        print("[case] mlp step 8192 bf16: step", flush=True)
+        g = st.step(X.cuda(), W1.cuda(), b1.cuda(), W2.cuda(), dY.cuda())
+        torch.cuda.synchronize()
+        H, mask, Y = to_np(st.H), to_np(st.mask), to_np(st.Y)
+        dW2, dZ1, db1, dW1 = to_np(g["dW2"]), to_np(g["dZ1"]), to_np(g["db1"]), to_np(g["dW1"])
+    x, w1, bb1, w2, dy = (to_np(t) for t in (X, W1, b1, W2, dY))
+    rng = np.random.default_rng(7)
+    groups = sorted(set(rng.choice(n // 32, size=3, replace=False).tolist()) | {0, n // 32 - 1})
+    w2t = np.ascontiguousarray(w2.T)        # rows of W2^T, the DRELU_BGRAD operand
+    Ht = np.ascontiguousarray(H.T)          # H^T (batch, hidden), the dW2 operand
+    xt = np.ascontiguousarray(x.T)          # X^T, the dW1 operand
+    for grp in groups:
+        r = slice(32 * grp, 32 * grp + 32)
+        print(f"[case] mlp step 8192 rows {r.start}:{r.stop}", flush=True)
+        o1 = oracle.gemm_epilog(w1[r], x, "RELU_AUX_BIAS", bias=bb1[r], ab="bf16", want_pre=True)
+        assert_close(H[r], o1["D"], "bf16", "H")
+        assert_mask(mask[grp:grp + 1], o1["mask"], o1["pre"], 32)
+        assert_close(Y[r], oracle.gemm_epilog(w2[r], H, "NONE", ab="bf16")["D"], "bf16", "Y")
+        assert_close(dW2[r], oracle.gemm_epilog(dy[r], Ht, "NONE", ab="bf16")["D"], "bf16", "dW2")
+        ob = oracle.gemm_epilog(w2t[r], dy, "DRELU_BGRAD", mask=mask[grp:grp + 1].view(np.uint32), ab="bf16")
+        assert_close(dZ1[r], ob["D"], "bf16", "dZ1")
+        assert_bgrad(db1[r], ob["bgrad"], ob["absum"], "bf16")
+        assert_close(dW1[r], oracle.gemm_epilog(dZ1[r], xt, "NONE", ab="bf16")["D"], "bf16", "dW1")

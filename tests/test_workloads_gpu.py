@@ -159,3 +159,45 @@ def test_large_f16_relu_bias_and_aux(gpu):
     assert torch.equal(g["D_dev"], D1), "RELU_AUX_BIAS changed D"
     check_rows(g["D_dev"], W, A, B, bias, groups[:3], "RELU_AUX_BIAS", "f16", want_mask=g["mask_dev"])
     relu_mask_invariants(g["D_dev"], g["mask_dev"], W.m)
+
+
+def test_mlp_bf16_8192_backward_with_weights_as_stored(gpu):
+    # the rest of the 8192 layer's backward as the benchmark times it: dX = W^T dY with
+    # W handed over as stored (A as its (k, m) transpose, DRELU_BGRAD), and the weight
+    # gradient dW = dZ X^T with X as stored (B as its (n, k) transpose, NONE)
+    W = inputs.WORKLOADS["mlp_bf16_8192"]
+    A, B, bias = W.a(), W.b(), W.bias()
+    g = R.run(gpu, "RELU_AUX_BIAS", "bf16", A, B, bias)
+    mask_dev = g["mask_dev"]
+    del g, A, B
+    A2, B2 = W.a2(), W.b2()
+    groups = sample_groups(W.m)
+    a2, b2 = to_np(A2), to_np(B2)
+    mask_np = to_np(mask_dev)
+    print(f"[case] {W.name} DRELU_BGRAD, A as its transpose", flush=True)
+    gb = R.run(gpu, "DRELU_BGRAD", "bf16", A2.t().contiguous(), B2, mask=mask_dev, trans_a=True)
+    assert "op_a T" in gb["desc"]
+    for grp in groups:
+        r0, r1 = 32 * grp, 32 * grp + 32
+        ob = oracle.gemm_epilog(a2[r0:r1], b2, "DRELU_BGRAD", mask=mask_np[grp:grp + 1], ab="bf16")
+        assert_close(to_np(gb["D_dev"][r0:r1]), ob["D"], "bf16", f"dz rows {r0}:{r1}")
+        assert_bgrad(gb["bgrad"][r0:r1], ob["bgrad"], ob["absum"], "bf16")
+    del gb
+    print(f"[case] {W.name} NONE, B as its transpose", flush=True)
+    g = R.run(gpu, "NONE", "bf16", A2, B2.t().contiguous(), trans_b=True)
+    assert "op_b T" in g["desc"]
+    for grp in groups[:4]:
+        r0, r1 = 32 * grp, 32 * grp + 32
+        o = oracle.gemm_epilog(a2[r0:r1], b2, "NONE", ab="bf16")
+        assert_close(to_np(g["D_dev"][r0:r1]), o["D"], "bf16", f"dW rows {r0}:{r1}")
+
+
+def test_square_f16_4096_fused_and_unfused(gpu):
+    W = inputs.WORKLOADS["square_f16_4096"]
+    A, B, bias = W.a(), W.b(), W.bias()
+    print(f"[case] {W.name} RELU_BIAS and RELU_BIAS_UNFUSED", flush=True)
+    gf = R.run(gpu, "RELU_BIAS", "f16", A, B, bias)
+    assert "persistent" in gf["desc"]
+    check_rows(gf["D_dev"], W, A, B, bias, sample_groups(W.m), "RELU_BIAS", "f16")
+    gu = R.run(gpu, "RELU_BIAS_UNFUSED", "f16", A, B, bias)
+    assert_close(gu["D"], gf["D"], "f16", "unfused vs fused")
