@@ -51,6 +51,10 @@ VARIANTS = {
     "square4096_unfused_f16": ("square_f16_4096", "RELU_BIAS_UNFUSED", "f16", False),
 }
 LAYOUTS = {"NN": (False, False), "TN": (True, False), "NT": (False, True)}
+# The HBM-bound rows timed cold as well: each execute follows a 1 GiB scratch write, which
+# evicts the 256 MB MALL and the L2s, so the operands come from HBM.
+COLD_VARIANTS = {"small_relu_bias_f16_cold": "small_relu_bias_f16", "ffn_unfused_f16_cold": "ffn_unfused_f16"}
+FLUSH_BYTES = 1 << 30
 
 
 def kernel_source_hash() -> str:
@@ -154,7 +158,28 @@ def time_execute(ge, handle, args, steps, warmup, warm_s=0.0):
             "event_ms_p90": per[min(len(per) - 1, (len(per) * 9) // 10)]}
 
 
-def run_variant(ge, W, epilog, dtype, steps, warmup, device_rng, layout="NN"):
+def time_execute_cold(ge, handle, args, steps):
+    """`steps` executes, each after a FLUSH_BYTES scratch write and timed alone with a
+    HIP event pair on the launch stream (the flush is outside the pair)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    ge.gemm_epilog_execute(handle, *args, stream=sptr)
+    for i, (e0, e1) in enumerate(ev):
+        flush.fill_(i)
+        e0.record(stream)
+        ge.gemm_epilog_execute(handle, *args, stream=sptr)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    del flush
+    per = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    return {"wall_ms_per_step": None, "event_ms_mean": sum(per) / len(per), "event_ms_median": per[len(per) // 2],
+            "event_ms_p10": per[len(per) // 10], "event_ms_p90": per[min(len(per) - 1, (len(per) * 9) // 10)]}
+
+
+def run_variant(ge, W, epilog, dtype, steps, warmup, device_rng, layout="NN", cold=False):
     import torch
     A, B, bias = device_inputs(W, device_rng)
     m, n, k = W.m, W.n, W.k
@@ -181,13 +206,23 @@ def run_variant(ge, W, epilog, dtype, steps, warmup, device_rng, layout="NN"):
         A = A.t().contiguous()
     if tb:
         B = B.t().contiguous()
-    r = time_execute(ge, h, (A, B, bias, D, aux, bg), steps, warmup, warm_s=0.3)
+    if cold:
+        r = time_execute_cold(ge, h, (A, B, bias, D, aux, bg), steps)
+    else:
+        r = time_execute(ge, h, (A, B, bias, D, aux, bg), steps, warmup, warm_s=0.3)
     desc = ge.gemm_epilog_describe(h)
     ge.gemm_epilog_free(h)
     t = r["event_ms_median"] * 1e-3
     out = {"epilog": epilog, "dtype": dtype, "m": m, "n": n, "k": k, "layout": layout, "plan_ms": round(plan_ms, 3),
            "kernel": desc, "median_ms": round(r["event_ms_median"], 4), "p10_ms": round(r["event_ms_p10"], 4),
            "p90_ms": round(r["event_ms_p90"], 4), "tflops": round(2 * m * n * k / t / 1e12, 1)}
+    if cold:
+        # algorithmic HBM bytes: A, B and D once, the bias; the unfused chain adds its two
+        # elementwise kernels' reads and writes of T1 and T2 (4 m n s)
+        es = 2 if dtype in ("f16", "bf16") else 4
+        byts = es * (m * k + k * n + m * n + m) + (4 * m * n * es if epilog == "RELU_BIAS_UNFUSED" else 0)
+        out.update({"cold": f"each execute after a {FLUSH_BYTES >> 20} MiB scratch write",
+                    "algorithmic_bytes": byts, "hbm_gbs": round(byts / t / 1e9, 1)})
     del A, B, D, aux, bg
     torch.cuda.empty_cache()
     return out
@@ -300,7 +335,8 @@ def main():
     ap.add_argument("--skip-cpu", action="store_true", help="leave out the cpu_baseline leg (profiling runs)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run the 1 GiB copy that calibrates the HBM byte counters")
-    ap.add_argument("--only", choices=sorted(VARIANTS) + ["mlp8192_train_step_bf16", "autotune_small", "autotune_headline"],
+    ap.add_argument("--only", choices=sorted(VARIANTS) + sorted(COLD_VARIANTS) +
+                    ["mlp8192_train_step_bf16", "autotune_small", "autotune_headline"],
                     help="time one variant alone (--steps executes after --warmup) and print its line; "
                          "for profiling runs")
     args = ap.parse_args()
@@ -327,9 +363,10 @@ def main():
         print(json.dumps({"variant": args.only, **run_mlp_step(args.steps, args.warmup)}), flush=True)
         return
     if args.only:
-        wname, ep, dt, dev_rng, *lay = VARIANTS[args.only]
+        cold = args.only in COLD_VARIANTS
+        wname, ep, dt, dev_rng, *lay = VARIANTS[COLD_VARIANTS.get(args.only, args.only)]
         Wv = inputs.WORKLOADS[inputs.HEADLINE if wname is None else wname]
-        r = run_variant(ge, Wv, ep, dt, args.steps, args.warmup, dev_rng, *lay)
+        r = run_variant(ge, Wv, ep, dt, args.steps, args.warmup, dev_rng, *lay, cold=cold)
         print(json.dumps({"variant": args.only, **r}), flush=True)
         return
     prop = torch.cuda.get_device_properties(0)
@@ -370,6 +407,12 @@ def main():
         sq_f, sq_u = variants["square4096_relu_bias_f16"]["median_ms"], variants["square4096_unfused_f16"]["median_ms"]
         variants["square4096_fusion_saving"] = {"fused_ms": sq_f, "unfused_ms": sq_u,
                                                 "saving_frac": round(1 - sq_f / sq_u, 4)}
+        for name, base in COLD_VARIANTS.items():
+            wname, ep, dt, dev_rng, *lay = VARIANTS[base]
+            Wv = inputs.WORKLOADS[inputs.HEADLINE if wname is None else wname]
+            log(f"[bench] variant {name}")
+            variants[name] = run_variant(ge, Wv, ep, dt, vsteps, vwarm, dev_rng, *lay, cold=True)
+            log(f"[bench]   {variants[name]}")
         for wname in ("relu_bias_f16_1024x512x2048", inputs.HEADLINE):
             log(f"[bench] autotune {wname}")
             variants[f"autotune_{wname}"] = run_autotune(ge, inputs.WORKLOADS[wname], vsteps, vwarm)
