@@ -35,6 +35,10 @@ COPY_PROBE_BYTES = 1 << 30
 VARIANTS = {
     "ffn_unfused_f16": (None, "RELU_BIAS_UNFUSED", "f16", False),
     "ffn_aux_f16": (None, "RELU_AUX_BIAS", "f16", False),
+    # the same product with the identity epilogue and with no epilogue: what bias + ReLU
+    # cost inside the fused kernel
+    "ffn_bias_f16": (None, "BIAS", "f16", False),
+    "ffn_none_f16": (None, "NONE", "f16", False),
     "ffn_gelu_bf16": ("ffn_gelu_bf16_4096x11008x4096", "GELU_BIAS", "bf16", False),
     "mlp8192_fwd_aux_bf16": ("mlp_bf16_8192", "RELU_AUX_BIAS", "bf16", True),
     "mlp8192_bwd_drelu_bgrad_bf16": ("mlp_bf16_8192", "DRELU_BGRAD", "bf16", True),
