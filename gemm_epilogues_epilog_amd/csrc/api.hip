@@ -186,7 +186,13 @@ ge_status_t build_plan(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt, ge_epilo
     if (rem != 0 && (int64_t)rem * 2 <= (int64_t)cus && kt >= 2) {
       const int64_t units = (int64_t)rem * kt;
       // runs of at least a quarter tile: an owner then adds at most about four partials
-      const int64_t per = std::max(cdiv(units, cus), cdiv(kt, 4));
+      int64_t per = std::max(cdiv(units, cus), cdiv(kt, 4));
+      // (experiments: GE_SK_RUN sets the run length, never below one run per compute
+      // unit, so every split workgroup is resident at once and every wait ends)
+      if (const char* e = std::getenv("GE_SK_RUN")) {
+        const int64_t v = std::atoll(e);
+        if (v >= 1) per = std::max(v, cdiv(units, cus));
+      }
       if (per < kt) {   // a run of k-tiles then holds at most one tile start
         h->dp_tiles = tiles - rem;
         h->sk_units = (int)per;
