@@ -1168,6 +1168,16 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_sk_kernel(
   // every wave is done with the stages: reuse them as per-wave epilogue scratch
   wait_lgkmcnt<0>();
   barrier_only();
+  if (split && threadIdx.x == 0) {
+    // Every wave has passed its waits: clear the flags this owner consumed (no other
+    // workgroup reads them). A flag then holds the epoch only between its run's publish
+    // and its owner's wait, so a later execute that repeats this epoch (a replay of a
+    // captured graph, whose arguments are frozen) waits for its own partials.
+    const int t = pos - p.dp_tiles;
+    const int last = min(((t + 1) * KT - 1) / p.sk_units, p.sk_wgs - 1);
+    for (int o = r + 1; o <= last; ++o)
+      __hip_atomic_store(p.sk_flag + o, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   epilogue_lds<DT, EP, MB, NB, WN>(p, acc, (int64_t)tm * BM + wm * WM, tn * BN + wn * WN, lane,
                                    smem + w * C::SCRATCH);
 }

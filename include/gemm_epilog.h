@@ -161,6 +161,9 @@ ge_status_t gemm_epilog_plan_ex(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt,
  *   stream : a hipStream_t; NULL means the null stream.
  * Every output element in range is written; nothing outside the stated extents is.
  * Returns GE_ERR_HIP if a launch fails.
+ * An execute enqueues kernel launches only (no memset, no host synchronisation), so it
+ * may be captured into a HIP graph and replayed; replays of one plan must not overlap,
+ * as for any two executes of a plan.
  */
 ge_status_t gemm_epilog_execute(ge_handle_t h, const void* A, const void* B, const void* bias, void* D,
                                 void* aux, void* bgrad, void* stream);
