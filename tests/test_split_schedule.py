@@ -7,16 +7,21 @@ plan's choice and the kernel's piece arithmetic and checks the invariants the ke
 relies on: every (tile, k-tile) is computed exactly once, each tile has exactly one
 owner piece starting at k = 0, each run publishes at most one partial (which never
 starts at k = 0), and the runs an owner waits for are exactly the runs that hold the
-rest of its tile, each of which publishes before it waits for anything."""
+rest of its tile, each of which publishes before it waits for anything. Every
+published flag has exactly one owner that waits for it, which is what lets that owner
+clear it afterwards. The run length may also be forced (GE_SK_RUN), never below one
+run per compute unit, so every split workgroup is resident at once."""
 import pytest
 
 
-def plan(tiles, kt, cus=256):
+def plan(tiles, kt, cus=256, run=None):
     rem = tiles % cus
     if not (rem != 0 and rem * 2 <= cus and kt >= 2):
         return None
     units = rem * kt
     per = max(-(-units // cus), -(-kt // 4))
+    if run is not None and run >= 1:
+        per = max(run, -(-units // cus))
     if per >= kt:
         return None
     return tiles - rem, per, -(-units // per)
@@ -27,9 +32,9 @@ def xcd_remap(i, g):
     return (x * (per + 1) if x < rem else rem * (per + 1) + (x - rem) * per) + local
 
 
-def pieces(tiles, kt, cus=256):
+def pieces(tiles, kt, cus=256, run=None):
     """(run, kind, tile, kb, nt) in the order one run's workgroup computes them."""
-    dp, u, wgs = plan(tiles, kt, cus)
+    dp, u, wgs = plan(tiles, kt, cus, run)
     total = (tiles - dp) * kt
     for wid in range(wgs):
         r = xcd_remap(wid, wgs)
@@ -43,14 +48,15 @@ def pieces(tiles, kt, cus=256):
             yield r, "owner", ts // kt, 0, u1 - ts
 
 
-def check(tiles, kt, cus=256):
-    dp, u, wgs = plan(tiles, kt, cus)
+def check(tiles, kt, cus=256, run=None):
+    dp, u, wgs = plan(tiles, kt, cus, run)
     total = (tiles - dp) * kt
+    assert wgs <= cus   # every split workgroup resident at once
     assert sorted(xcd_remap(i, wgs) for i in range(wgs)) == list(range(wgs))
     assert wgs * u >= total > (wgs - 1) * u
     cover, owners, partial_of = set(), {}, {}
     last_kind = {}
-    for r, kind, t, kb, nt in pieces(tiles, kt, cus):
+    for r, kind, t, kb, nt in pieces(tiles, kt, cus, run):
         assert kb + nt <= kt
         for kk in range(kb, kb + nt):
             assert (t, kk) not in cover
@@ -63,11 +69,15 @@ def check(tiles, kt, cus=256):
             partial_of[r] = t
         last_kind[r] = kind
     assert len(cover) == total
+    waited = []
     for t in range(tiles - dp):
         r = owners[t]
         last = min(((t + 1) * kt - 1) // u, wgs - 1)
         partners = list(range(r + 1, last + 1))
         assert sorted(o for o, tt in partial_of.items() if tt == t) == partners
+        waited += partners
+    # each published flag is waited for by exactly one owner (who then clears it)
+    assert sorted(waited) == sorted(partial_of)
 
 
 def test_sparse_last_round_splits():
@@ -88,3 +98,12 @@ def test_full_or_mostly_full_rounds_do_not_split():
 def test_schedule_invariants(tiles, kt):
     if plan(tiles, kt) is not None:
         check(tiles, kt)
+
+
+@pytest.mark.parametrize("tiles", [1, 8, 32, 100, 272])
+@pytest.mark.parametrize("kt", [2, 8, 32, 64])
+@pytest.mark.parametrize("run", [1, 2, 4, 16, 63])
+def test_forced_run_lengths(tiles, kt, run):
+    p = plan(tiles, kt, run=run)
+    if p is not None:
+        check(tiles, kt, run=run)
