@@ -90,13 +90,21 @@ bool env_off(const char* name) {
   return v && v[0] == '0' && v[1] == 0;
 }
 
-// 16-bit types: the 256 x 256 tile when it gives every compute unit at least one
-// tile, else the 128 x 128 direct-to-LDS tile (two workgroups per compute unit; a
-// sparse grid splits its k loop). fp32: the register-staged tiles, the largest that
-// still gives every compute unit a tile.
-// With an operand stored transposed (lay != 0) the 256 x 256 tile runs one workgroup
-// per tile (LH) instead of the persistent kernel.
-int choose_cfg(int64_t m, int n, ge_dtype_t ab, int cus, int lay) {
+// 16-bit types, by the number T of 256 x 256 tiles and of 64-wide k-tiles KT
+// (measured at 4096x2752x4096, 4096x3200x4096, 8192x1024x8192, 2048x2048x8192,
+// 2048x1024x16384, 3072x2560x4096, 4096x1376x4096, 2048^3 and 1024x1024x4096):
+//   T >= CUs:      the 256 x 256 tile;
+//   T > CUs / 2:   still the 256 x 256 tile, one partly filled round (15-18% faster
+//                  than 128 x 128 tiles, which would need more than one round of two
+//                  workgroups per CU);
+//   KT >= 128:     the 256 x 256 tile with its k loop split across the idle CUs (3-9%
+//                  faster: long runs amortise the partial sums); not for transposed
+//                  operands, whose plans do not split;
+//   otherwise:     the 128 x 128 tile (two workgroups per compute unit).
+// fp32: the register-staged tiles, the largest that still gives every compute unit a
+// tile. With an operand stored transposed (lay != 0) the 256 x 256 tile runs one
+// workgroup per tile (LH) instead of the persistent kernel.
+int choose_cfg(int64_t m, int n, int64_t k, ge_dtype_t ab, int cus, int lay) {
   const char* env = std::getenv("GE_TILE");
   if (env && env[0]) {
     for (int c = 0; c < gek::CFG_COUNT; ++c)
@@ -106,7 +114,9 @@ int choose_cfg(int64_t m, int n, ge_dtype_t ab, int cus, int lay) {
   }
   auto tiles = [&](int c) { return cdiv(m, gek::kTiles[c].bm) * cdiv(n, gek::kTiles[c].bn); };
   if (ab != GE_F32) {
-    if (tiles(gek::CFG_L) >= cus) return lay ? gek::CFG_LH : gek::CFG_L;
+    const int64_t t = tiles(gek::CFG_L);
+    const int64_t kt = cdiv(k, gek::kTiles[gek::CFG_L].bk);
+    if (t >= cus || 2 * t > cus || (kt >= 128 && lay == 0)) return lay ? gek::CFG_LH : gek::CFG_L;
     return gek::CFG_LM;
   }
   if (tiles(gek::CFG_M) >= cus) return gek::CFG_M;
@@ -182,7 +192,10 @@ ge_status_t build_plan(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt, ge_epilo
   h->dp_tiles = tiles;
   if (gek::cfg_can_split(h->cfg) && lay == 0 && allow_split) {
     const int kt = (int)cdiv(k, tc.bk);
-    const int rem = tiles % cus;
+    // a round holds one workgroup per CU, two for the 128 x 128 tile (64 KB of LDS): a
+    // grid of up to 2 CUs tiles of that size runs in one round and has no sparse tail
+    const int slots = h->cfg == gek::CFG_LM ? 2 * cus : cus;
+    const int rem = tiles % slots;
     if (rem != 0 && (int64_t)rem * 2 <= (int64_t)cus && kt >= 2) {
       const int64_t units = (int64_t)rem * kt;
       // runs of at least a quarter tile: an owner then adds at most about four partials
@@ -313,7 +326,7 @@ ge_status_t gemm_epilog_plan_ex(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt,
   if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return GE_ERR_NOT_SUPPORTED;
   const int cus = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
 
-  return build_plan(m, n, k, dt, ep, lay, dev, cus, choose_cfg(m, (int)n, dt.ab, cus, lay), !env_off("GE_STREAMK"),
+  return build_plan(m, n, k, dt, ep, lay, dev, cus, choose_cfg(m, (int)n, k, dt.ab, cus, lay), !env_off("GE_STREAMK"),
                     !env_off("GE_PERSIST"), out);
 }
 

@@ -257,3 +257,26 @@ def test_persistent_random_matches_one_tile_per_workgroup(gpu):
     rows = np.r_[0:32, 992:1056, 2016:2048]
     o = oracle.gemm_epilog(to_np(A)[rows], to_np(B), "RELU_AUX_BIAS", bias=to_np(bias)[rows], want_pre=True)
     assert_close(gp["D"][rows], o["D"], "f16", "persistent vs oracle")
+
+
+@pytest.mark.parametrize("shape,lay,tile,split", [
+    ((4096, 2752, 4096), "NN", "256x256", False),    # 176 tiles of 256 x 256: one partly filled round
+    ((4096, 3200, 4096), "NN", "256x256", False),
+    ((8192, 1024, 8192), "NN", "256x256", True),     # 128 tiles, 128 k-tiles: split k loop
+    ((2048, 1024, 16384), "NN", "256x256", True),
+    ((4096, 1376, 4096), "NN", "128x128", False),    # 352 tiles of 128 x 128: one round at two per CU
+    ((3072, 2560, 4096), "NN", "128x128", False),
+    ((1024, 512, 2048), "NN", "128x128", True),
+    ((2048, 2048, 2048), "NN", "128x128", False),
+    ((8192, 1024, 8192), "TN", "128x128", False),    # transposed operands never split
+    ((4096, 2752, 4096), "TN", "256x256", False),
+])
+def test_tile_choice(gpu, shape, lay, tile, split):
+    ge = gpu
+    m, n, k = shape
+    h = ge.gemm_epilog_plan_ex(m, n, k, ("f16", "f16", "f16"), "RELU_BIAS", int(lay[0] == "T"), int(lay[1] == "T"))
+    try:
+        d = ge.gemm_epilog_describe(h)
+        assert f"tile {tile}" in d and ("split" in d) == split, (shape, lay, d)
+    finally:
+        ge.gemm_epilog_free(h)

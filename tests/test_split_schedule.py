@@ -14,8 +14,9 @@ run per compute unit, so every split workgroup is resident at once."""
 import pytest
 
 
-def plan(tiles, kt, cus=256, run=None):
-    rem = tiles % cus
+def plan(tiles, kt, cus=256, run=None, slots=None):
+    """slots: workgroups per round (2 cus for the 128 x 128 tile, two per CU)."""
+    rem = tiles % (slots or cus)
     if not (rem != 0 and rem * 2 <= cus and kt >= 2):
         return None
     units = rem * kt
@@ -85,6 +86,15 @@ def test_sparse_last_round_splits():
     dp, u, wgs = plan(272, 64)
     assert (dp, u, wgs) == (256, 16, 64)
     check(272, 64)
+
+
+def test_two_workgroups_per_cu_rounds():
+    # 128 x 128 tiles run two per CU: 352 of them (4096 x 1376) fill one round and do not
+    # split; 32 (1024 x 512) still do, in runs of 8 of their 32 k-tiles
+    assert plan(352, 64, slots=512) is None
+    assert plan(32, 32, slots=512) == (0, 8, 128)
+    assert plan(600, 64, slots=512) == (512, 22, 256)
+    check(600, 64)
 
 
 def test_full_or_mostly_full_rounds_do_not_split():

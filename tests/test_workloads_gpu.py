@@ -109,6 +109,23 @@ def test_ffn_f16_unfused_matches_fused(gpu, ffn):
         assert_close(gu["D"][r0:r1], o["D"], "f16", "unfused vs oracle chain")
 
 
+def test_ffn_f16_aux_bias_none(gpu, ffn):
+    # the other epilogues the benchmark times on the headline inputs
+    W, A, B, bias = ffn
+    groups = sample_groups(W.m, count=4)
+    print(f"[case] {W.name} RELU_AUX_BIAS", flush=True)
+    g = R.run(gpu, "RELU_AUX_BIAS", "f16", A, B, bias)
+    assert "persistent" in g["desc"]
+    check_rows(g["D_dev"], W, A, B, bias, groups, "RELU_AUX_BIAS", "f16", want_mask=g["mask_dev"])
+    relu_mask_invariants(g["D_dev"], g["mask_dev"], W.m)
+    del g
+    for ep in ("BIAS", "NONE"):
+        print(f"[case] {W.name} {ep}", flush=True)
+        g = R.run(gpu, ep, "f16", A, B, bias)
+        check_rows(g["D_dev"], W, A, B, bias, groups, ep, "f16")
+        del g
+
+
 def test_ffn_bf16_gelu_bias(gpu):
     W = inputs.WORKLOADS["ffn_gelu_bf16_4096x11008x4096"]
     A, B, bias = W.a(), W.b(), W.bias()
@@ -201,3 +218,29 @@ def test_square_f16_4096_fused_and_unfused(gpu):
     check_rows(gf["D_dev"], W, A, B, bias, sample_groups(W.m), "RELU_BIAS", "f16")
     gu = R.run(gpu, "RELU_BIAS_UNFUSED", "f16", A, B, bias)
     assert_close(gu["D"], gf["D"], "f16", "unfused vs fused")
+
+
+def test_shard8_shapes(gpu):
+    # one GPU's share of an 8-way split along n, as the benchmark times it
+    W = inputs.WORKLOADS["ffn_shard8_f16_4096x1376x4096"]
+    A, B, bias = W.a(), W.b(), W.bias()
+    print(f"[case] {W.name} RELU_BIAS", flush=True)
+    g = R.run(gpu, "RELU_BIAS", "f16", A, B, bias)
+    check_rows(g["D_dev"], W, A, B, bias, sample_groups(W.m, count=4), "RELU_BIAS", "f16")
+    del g
+    W = inputs.WORKLOADS["mlp_shard8_bf16_8192x1024x8192"]
+    A, B, bias = W.a(), W.b(), W.bias()
+    print(f"[case] {W.name} forward and backward", flush=True)
+    g = R.run(gpu, "RELU_AUX_BIAS", "bf16", A, B, bias)
+    groups = sample_groups(W.m, count=4)
+    check_rows(g["D_dev"], W, A, B, bias, groups, "RELU_AUX_BIAS", "bf16", want_mask=g["mask_dev"])
+    mask_dev = g["mask_dev"]
+    del g
+    A2, B2 = W.a2(), W.b2()
+    gb = R.run(gpu, "DRELU_BGRAD", "bf16", A2, B2, mask=mask_dev)
+    a2, b2, mask_np = to_np(A2), to_np(B2), to_np(mask_dev)
+    for grp in groups:
+        r0, r1 = 32 * grp, 32 * grp + 32
+        ob = oracle.gemm_epilog(a2[r0:r1], b2, "DRELU_BGRAD", mask=mask_np[grp:grp + 1], ab="bf16")
+        assert_close(to_np(gb["D_dev"][r0:r1]), ob["D"], "bf16", f"dz rows {r0}:{r1}")
+        assert_bgrad(gb["bgrad"][r0:r1], ob["bgrad"], ob["absum"], "bf16")
