@@ -18,7 +18,8 @@ struct TileCfg {
   const char* loop;   // main loop of the direct-to-LDS kernels
 };
 
-enum CfgId { CFG_S = 0, CFG_M, CFG_L, CFG_LH, CFG_LA, CFG_LI, CFG_LS, CFG_LSH, CFG_LM, CFG_W4, CFG_W4S, CFG_P, CFG_COUNT };
+enum CfgId { CFG_S = 0, CFG_M, CFG_L, CFG_LH, CFG_LA, CFG_LI, CFG_LS, CFG_LSH, CFG_LM, CFG_W4, CFG_W4S, CFG_P, CFG_LM4,
+             CFG_COUNT };
 
 constexpr TileCfg kTiles[CFG_COUNT] = {
     {64, 64, 32, 32, 0, 2, "S", ""},
@@ -33,6 +34,7 @@ constexpr TileCfg kTiles[CFG_COUNT] = {
     {256, 256, 128, 128, 64, 2, "W4", "lockstep"},                      // 4 waves of 128 x 128
     {256, 256, 128, 128, 32, 4, "W4S", "lockstep spread interleaved"},
     {256, 256, 128, 64, 32, 4, "P", "ping-pong"},                       // 8 waves in two groups
+    {128, 128, 64, 64, 64, 2, "LM4", "lockstep"},                       // 4 waves of 64 x 64, two per CU
 };
 
 inline bool cfg_is_dtl(int c) { return c >= CFG_L; }
@@ -117,6 +119,7 @@ LaunchFn pick_cfg(int cfg) {
       case CFG_W4: return &launch_dtl<DT, EP, 256, 256, 128, 128, 64, 2, LOCKSTEP>;
       case CFG_W4S: return &launch_dtl<DT, EP, 256, 256, 128, 128, 32, 4, LOCKSTEP_SPREAD_ILV>;
       case CFG_P: return &launch_dtl<DT, EP, 256, 256, 128, 64, 32, 4, PINGPONG>;
+      case CFG_LM4: return &launch_dtl<DT, EP, 128, 128, 64, 64, 64, 2, LOCKSTEP>;
       default: break;
     }
   }

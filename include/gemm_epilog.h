@@ -113,7 +113,7 @@ typedef enum {
  *   out     : receives the handle; untouched on error.
  * Allocates the workspace on the current device: the per-tile bias-gradient
  * partial sums for DRELU_BGRAD, T1 and T2 for RELU_BIAS_UNFUSED, nothing otherwise.
- * Environment (tuning experiments): GE_TILE=S|M|L|LH|LA|LI|LS|LSH|LM|W4|W4S|P forces a tile configuration;
+ * Environment (tuning experiments): GE_TILE=S|M|L|LH|LA|LI|LS|LSH|LM|LM4|W4|W4S|P forces a tile configuration;
  * GE_GROUP_M=g (1..1024) sets how many m-tiles share one group of the tile order;
  * GE_STREAMK=0 keeps a sparse last round of tiles whole instead of splitting its k loop;
  * GE_SK_RUN=r sets the k-tiles per split run (at least one run per compute unit);
@@ -185,7 +185,8 @@ ge_status_t gemm_epilog_execute(ge_handle_t h, const void* A, const void* B, con
  * Candidates: for fp32 the 64x64 and 128x128 tiles; for fp16/bf16 with transposed
  * operands the 256x256 and 128x128 lockstep tiles; otherwise the 256x256 tile
  * (persistent, one workgroup per tile, with copies on all or half of the waves) and
- * the 128x128 tile, each with and without the split tail where it applies. A candidate
+ * the 128x128 tile with eight or four waves, each with and without the split tail
+ * where it applies. A candidate
  * whose workspace cannot be allocated is skipped. The call synchronises `stream`, must
  * not overlap another execute of this plan, and runs on the device current at plan
  * time. On an error the plan keeps its configuration (GE_ERR_HIP if a launch or an

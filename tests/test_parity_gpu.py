@@ -19,7 +19,7 @@ from tests.helpers import assert_bgrad, assert_close, assert_mask, tight_ratio, 
 pytestmark = pytest.mark.gpu
 
 DTS = ["f32", "f16", "bf16"]
-TILES16 = ["S", "M", "L", "L-nosk", "LH", "LA", "LI", "LS", "LSH", "LM", "LM-nosk", "W4", "W4S", "P"]
+TILES16 = ["S", "M", "L", "L-nosk", "LH", "LA", "LI", "LS", "LSH", "LM", "LM-nosk", "LM4", "W4", "W4S", "P"]
 TILES = {"f32": ["S", "M"], "f16": TILES16, "bf16": TILES16}
 # the last shape (k a multiple of 64 over 4 k-tiles) runs the persistent kernel in "L"
 INT_SHAPES = [(1, 8, 8), (33, 136, 72), (200, 264, 200), (300, 520, 136), (300, 520, 256)]
