@@ -241,6 +241,49 @@ def run_variant(ge, W, epilog, dtype, steps, warmup, device_rng, layout="NN", co
     return out
 
 
+PROBE_HEADLINE_CASE = "f16 N(0,1/64) (the FFN workload's operands)"
+
+
+def mfma_probe(ge, iters: int = 20000, workgroups: int = 512, only=None):
+    """The MFMA-only probe (gemm_epilog_mfma_probe) on the value distributions of the
+    workloads and on constant values: what the matrix cores sustain on those values
+    under the power limit. Each case: one warm-up launch, then 5 timed with HIP events.
+    `only`: names of the cases to run (all by default)."""
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(0)
+    n = 1 << 19   # 1 MiB of fp16/bf16 values
+    makers = {
+        PROBE_HEADLINE_CASE: ("f16", lambda: torch.randn(n, device="cuda", generator=g) / 64),
+        "f16 N(0,1)": ("f16", lambda: torch.randn(n, device="cuda", generator=g)),
+        "bf16 N(0,1/64)": ("bf16", lambda: torch.randn(n, device="cuda", generator=g) / 64),
+        "f16 constant 1/64": ("f16", lambda: torch.full((n,), 1.0 / 64, device="cuda")),
+        "f16 zeros": ("f16", lambda: torch.zeros(n, device="cuda")),
+    }
+    out = torch.empty(workgroups * 256, dtype=torch.float32, device="cuda")
+    flop = workgroups * 16 * iters * 32768
+    res = {}
+    for name, (dt, make) in makers.items():
+        if only is not None and name not in only:
+            continue
+        ops = make().to(torch.float16 if dt == "f16" else torch.bfloat16)
+        ge.gemm_epilog_mfma_probe(ops, dt, iters, workgroups, out)
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            ge.gemm_epilog_mfma_probe(ops, dt, iters, workgroups, out)
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        t = sorted(times)[2]
+        res[name] = {"ms": round(t, 3), "tflops": round(flop / (t * 1e-3) / 1e12, 1),
+                     "frac_of_peak": round(flop / (t * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4)}
+    return {"probe": "back-to-back v_mfma_f32_32x32x16 alternating two operand pairs, 4 chains per wave, "
+                     "no memory traffic", "workgroups": workgroups, "iters": iters, "flop_per_launch": flop,
+            "cases": res}
+
+
 def run_autotune(ge, W, steps: int, warmup: int, repeats: int = 20):
     """The plan's table choice against gemm_epilog_autotune's measured choice on the
     same inputs: both timed like a variant, plus the wall time of the search."""
@@ -346,6 +389,8 @@ def main():
     ap.add_argument("--no-variants", action="store_true", help="time only the headline kernel")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--skip-cpu", action="store_true", help="leave out the cpu_baseline leg (profiling runs)")
+    ap.add_argument("--mfma-probe", action="store_true",
+                    help="only run the MFMA-rate probe on the workloads' value distributions and print its line")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run the 1 GiB copy that calibrates the HBM byte counters")
     ap.add_argument("--only", choices=sorted(VARIANTS) + sorted(COLD_VARIANTS) +
@@ -366,6 +411,9 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_probe:
         copy_probe()
+        return
+    if args.mfma_probe:
+        print(json.dumps(mfma_probe(ge)), flush=True)
         return
     if args.only in ("autotune_small", "autotune_headline"):
         wname = "relu_bias_f16_1024x512x2048" if args.only == "autotune_small" else inputs.HEADLINE
@@ -401,6 +449,10 @@ def main():
     log(f"[bench] headline: {r}")
 
     traffic = read_traffic(kernel_desc)
+    # what the matrix cores alone sustain on the headline's operand values (the MFMA-only
+    # probe): the practical ceiling under the power limit, next to the spec peak
+    probe_tflops = mfma_probe(ge, only=(PROBE_HEADLINE_CASE,))["cases"][PROBE_HEADLINE_CASE]["tflops"]
+    log(f"[bench] mfma probe on the headline's value distribution: {probe_tflops} TFLOP/s")
 
     variants = {}
     if not args.no_variants:
@@ -459,7 +511,9 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_F16_TFLOPS, 4), "traffic": traffic,
                      "kernel_ms_mean": round(r["event_ms_mean"], 4), "kernel_ms_median": round(r["event_ms_median"], 4),
-                     "kernel_ms_p10": round(r["event_ms_p10"], 4), "kernel_ms_p90": round(r["event_ms_p90"], 4)},
+                     "kernel_ms_p10": round(r["event_ms_p10"], 4), "kernel_ms_p90": round(r["event_ms_p90"], 4),
+                     "mfma_only_on_same_values": probe_tflops,
+                     "frac_of_mfma_only": round(achieved / probe_tflops, 4)},
         "cpu_baseline": cpu,
         "variants": variants,
     }

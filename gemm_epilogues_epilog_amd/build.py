@@ -16,7 +16,7 @@ OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libgemm_epilog.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.hip", "inst_f32.hip", "inst_f16.hip", "inst_bf16.hip",
+SOURCES = ["api.hip", "probe.hip", "inst_f32.hip", "inst_f16.hip", "inst_bf16.hip",
            "inst_f16_lay1.hip", "inst_f16_lay2.hip", "inst_f16_lay3.hip",
            "inst_bf16_lay1.hip", "inst_bf16_lay2.hip", "inst_bf16_lay3.hip"]
 

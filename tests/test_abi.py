@@ -143,3 +143,14 @@ def test_product_path_does_not_import_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle|liboracle|oracle\.cpp", text, flags=re.M), \
                     f"{f} reaches into the oracle"
+
+
+def test_mfma_probe_rejects_bad_arguments_on_host():
+    lib = ge.load()
+    assert lib.gemm_epilog_mfma_probe(None, 64, 1, 10, 1, 16, None) == 3          # NULL operands
+    assert lib.gemm_epilog_mfma_probe(16, 64, 1, 10, 1, None, None) == 3          # NULL out
+    assert lib.gemm_epilog_mfma_probe(16, 64, 0, 10, 1, 16, None) == 2            # fp32 operands
+    assert lib.gemm_epilog_mfma_probe(16, 8, 1, 10, 1, 16, None) == 1             # fewer than 16 bytes
+    assert lib.gemm_epilog_mfma_probe(16, 64, 1, 0, 1, 16, None) == 1             # iters < 1
+    assert lib.gemm_epilog_mfma_probe(16, 64, 1, 10, 0, 16, None) == 1            # no workgroups
+    assert lib.gemm_epilog_mfma_probe(24, 64, 1, 10, 1, 16, None) == 4            # operands not 16-byte aligned
