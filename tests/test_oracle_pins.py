@@ -150,6 +150,27 @@ def test_worked_example(dt):
     assert np.array_equal(w(o4["bgrad"]), np.array(fx["bgrad"], np.float32))
 
 
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("ta,tb", [(True, False), (False, True), (True, True)])
+def test_worked_example_transposed(dt, ta, tb):
+    fx = json.load(open(os.path.join(GOLDEN, "worked_example_3x2x2_transposed.json")))
+    base = json.load(open(os.path.join(GOLDEN, "worked_example_3x2x2.json")))
+    cast = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dt]
+    A = np_of(torch.tensor(fx["At"] if ta else base["A"]).to(cast), dt)
+    B = np_of(torch.tensor(fx["Bt"] if tb else base["B"]).to(cast), dt)
+    bias = np_of(torch.tensor(fx["bias"]).to(cast), dt)
+    w = lambda a: oracle.to_f32(a, dt)
+    kw = dict(ab=dt, trans_a=ta, trans_b=tb)
+    o = oracle.gemm_epilog(A, B, "RELU_AUX_BIAS", bias=bias, want_pre=True, **kw)
+    assert np.array_equal(w(o["D"]), np.array(fx["relu"], np.float32))
+    assert np.array_equal(o["pre"], np.array(fx["pre"], np.float32))
+    assert np.array_equal(o["mask"], np.array(fx["mask_words"], np.uint32))
+    assert np.array_equal(w(oracle.gemm_epilog(A, B, "NONE", **kw)["D"]), np.array(fx["AB"], np.float32))
+    o4 = oracle.gemm_epilog(A, B, "DRELU_BGRAD", mask=np.array(fx["mask_words"], np.uint32), **kw)
+    assert np.array_equal(w(o4["D"]), np.array(fx["dz"], np.float32))
+    assert np.array_equal(w(o4["bgrad"]), np.array(fx["bgrad"], np.float32))
+
+
 def test_mask_layout_fixture():
     fx = json.load(open(os.path.join(GOLDEN, "mask_layout_40x3.json")))
     m, n, k = fx["m"], fx["n"], fx["k"]
