@@ -11,6 +11,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <new>
@@ -268,6 +269,9 @@ ge_status_t build_plan(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt, ge_epilo
                              " split over " + std::to_string(h->sk_wgs) + "x" + std::to_string(h->sk_units) +
                              " k-tiles)"
                        : std::string());
+  if (const char* lg = std::getenv("GE_LOG"); lg && lg[0] == '1')
+    std::fprintf(stderr, "gemm_epilog_plan: m=%lld n=%lld k=%lld -> %s, workspace %zu bytes\n", (long long)m,
+                 (long long)n, (long long)k, h->desc.c_str(), h->ws_bytes);
   *out = h;
   return GE_OK;
 }

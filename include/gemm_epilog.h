@@ -117,7 +117,8 @@ typedef enum {
  * GE_GROUP_M=g (1..1024) sets how many m-tiles share one group of the tile order;
  * GE_STREAMK=0 keeps a sparse last round of tiles whole instead of splitting its k loop;
  * GE_SK_RUN=r sets the k-tiles per split run (at least one run per compute unit);
- * GE_PERSIST=0 launches one workgroup per tile instead of the persistent kernel.
+ * GE_PERSIST=0 launches one workgroup per tile instead of the persistent kernel;
+ * GE_LOG=1 prints each plan's configuration and workspace size to stderr.
  */
 ge_status_t gemm_epilog_plan(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt, ge_epilog_t ep,
                              ge_handle_t* out);

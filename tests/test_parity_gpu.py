@@ -280,3 +280,18 @@ def test_tile_choice(gpu, shape, lay, tile, split):
         assert f"tile {tile}" in d and ("split" in d) == split, (shape, lay, d)
     finally:
         ge.gemm_epilog_free(h)
+
+
+def test_plan_log(gpu, capfd):
+    ge = gpu
+    with R.env({"GE_LOG": "1"}):
+        h = ge.gemm_epilog_plan(1024, 512, 2048, ("f16", "f16", "f16"), "RELU_BIAS")
+    try:
+        err = capfd.readouterr().err
+        assert "gemm_epilog_plan: m=1024 n=512 k=2048 -> " + ge.gemm_epilog_describe(h) in err, err
+    finally:
+        ge.gemm_epilog_free(h)
+    with R.env({"GE_LOG": "0"}):
+        h = ge.gemm_epilog_plan(1024, 512, 2048, ("f16", "f16", "f16"), "RELU_BIAS")
+    ge.gemm_epilog_free(h)
+    assert "gemm_epilog_plan" not in capfd.readouterr().err
