@@ -103,8 +103,8 @@ bool env_off(const char* name) {
 //                  operands, whose plans do not split;
 //   otherwise:     the 128 x 128 tile (two workgroups per compute unit).
 // fp32: the register-staged tiles, the largest that still gives every compute unit a
-// tile. With an operand stored transposed (lay != 0) the 256 x 256 tile runs one
-// workgroup per tile (LH) instead of the persistent kernel.
+// tile. With an operand stored transposed (lay != 0) the 256 x 256 tile never splits its
+// k loop.
 int choose_cfg(int64_t m, int n, int64_t k, ge_dtype_t ab, int cus, int lay) {
   const char* env = std::getenv("GE_TILE");
   if (env && env[0]) {
@@ -117,7 +117,7 @@ int choose_cfg(int64_t m, int n, int64_t k, ge_dtype_t ab, int cus, int lay) {
   if (ab != GE_F32) {
     const int64_t t = tiles(gek::CFG_L);
     const int64_t kt = cdiv(k, gek::kTiles[gek::CFG_L].bk);
-    if (t >= cus || 2 * t > cus || (kt >= 128 && lay == 0)) return lay ? gek::CFG_LH : gek::CFG_L;
+    if (t >= cus || 2 * t > cus || (kt >= 128 && lay == 0)) return gek::CFG_L;
     return gek::CFG_LM;
   }
   if (tiles(gek::CFG_M) >= cus) return gek::CFG_M;
@@ -216,7 +216,7 @@ ge_status_t build_plan(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt, ge_epilo
   }
 
   // ---- persistent kernel: one workgroup per compute unit walks the tiles ----
-  if (gek::cfg_can_persist(h->cfg) && lay == 0 && h->dp_tiles == tiles && allow_persist) {
+  if (gek::cfg_can_persist(h->cfg) && h->dp_tiles == tiles && allow_persist) {
     const int kt = (int)cdiv(k, tc.bk);
     if (k % tc.bk == 0 && kt % tc.stages == 0 && kt >= 2 * tc.stages) h->persist_grid = std::min(tiles, cus);
   }
@@ -408,7 +408,8 @@ ge_status_t gemm_epilog_autotune(ge_handle_t h, const void* A, const void* B, co
   if (h->dt.ab == GE_F32) {
     cands = {{gek::CFG_S, false, false}, {gek::CFG_M, false, false}};
   } else if (h->lay != 0) {
-    cands = {{gek::CFG_LH, false, false}, {gek::CFG_LM, false, false}};
+    cands = {{gek::CFG_L, false, true}, {gek::CFG_L, false, false}, {gek::CFG_LH, false, false},
+             {gek::CFG_LM, false, false}};
   } else {
     cands = {{gek::CFG_L, true, true},   {gek::CFG_L, false, true},   {gek::CFG_L, false, false},
              {gek::CFG_LH, true, false}, {gek::CFG_LH, false, false}, {gek::CFG_LM, true, false},

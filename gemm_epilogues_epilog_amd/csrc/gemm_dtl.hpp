@@ -573,6 +573,11 @@ struct FragRead {
       return i32x4{lo[0], lo[1], hi[0], hi[1]};
     }
   }
+  // mn-major only: half h (k values 4 h .. 4 h + 3 of the lane's eight) of a fragment
+  __device__ __forceinline__ i32x2 read_half(const char* stage, int s, int blk, int h) const {
+    static_assert(!KMAJ, "k-major fragments are one 16-byte read");
+    return ds_read_tr(stage + rd[blk] + 16 * s * G::ROWB + h * 4 * G::ROWB);
+  }
 };
 
 // Copies and fragment reads of both operands for LAY != 0 (the lockstep loop without
@@ -604,6 +609,42 @@ struct OperandsT {
     ca.issue(kt * BK, K, w, sA);
     cb.issue(kt * BK, K, w, sA + C::A_BYTES);
   }
+  // One instruction's worth of the fragments of k-step s, in the order the step's MFMAs
+  // consume them: B block 0, the A blocks, then B blocks 1 .. NB-1; a k-major block is
+  // one piece (ds_read_b128), an mn-major block two (its halves, ds_read_b64_tr_b16).
+  static constexpr int PA = TA ? 2 : 1, PB = TB ? 1 : 2;
+  static constexpr int PIECES = PB * NB + PA * MB;
+  __device__ __forceinline__ void read_piece(const char* base, int s, int q, Frags<MB, NB>& f) const {
+    int bq = q;   // piece index among the B pieces
+    if (q >= PB) {
+      if (q < PB + PA * MB) {
+        const int blk = (q - PB) / PA;
+        if constexpr (TA) {
+          const i32x2 v = fa.read_half(base, s, blk, (q - PB) % PA);
+          if ((q - PB) % PA == 0) {
+            f.a[blk][0] = v[0];
+            f.a[blk][1] = v[1];
+          } else {
+            f.a[blk][2] = v[0];
+            f.a[blk][3] = v[1];
+          }
+        } else {
+          f.a[blk] = fa.read(base, s, blk);
+        }
+        return;
+      }
+      bq = q - PA * MB;
+    }
+    const int blk = bq / PB;
+    if constexpr (TB) {
+      const i32x4 v = fb.read(base, s, blk);
+      f.b[blk][0] = i32x2{v[0], v[1]};
+      f.b[blk][1] = i32x2{v[2], v[3]};
+    } else {
+      f.b[blk][bq % PB] = fb.read_half(base, s, blk, bq % PB);
+    }
+  }
+
   // Every fragment of k-step s from the stage at `base`.
   __device__ __forceinline__ void read_step(const char* base, int s, Frags<MB, NB>& f) const {
 #pragma unroll
@@ -848,6 +889,101 @@ struct CopyPlan {
   }
 };
 
+// Copies of the persistent kernel for operands in either storage order (LAY != 0), on the
+// pattern of CopyPlan: per operand two lane offsets (the swizzle repeats with the parity
+// of the copy instruction) and the instruction's row block in the descriptor's base.
+// k-major tile (A as stored, or B given as B^T): MN rows of 2 BK bytes; rows past the
+// operand's extent fall outside the descriptor's range and read as zero.
+template <int MN, int BK, int INST>
+struct KMajorCopy {
+  using G = TileGeom<MN, BK, true>;
+  static_assert(G::RPI % 8 == 0 || G::ROWB == 64, "swizzle period");
+  const char* tile;
+  int64_t rows_left;   // rows from this wave's first copied row to the extent
+  int64_t ldb;
+  uint32_t lane_off[2];
+  __device__ __forceinline__ void init(int K, int lane) {
+    ldb = (int64_t)K * 2;
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      const int row = par * G::RPI + lane / G::CHUNKS;
+      const int c = (lane % G::CHUNKS) ^ G::swz(row);
+      lane_off[par] = (uint32_t)((lane / G::CHUNKS) * ldb + c * 16);
+    }
+  }
+  __device__ __forceinline__ void retarget(const void* X, int64_t mn0, int64_t mndim, int w, int) {
+    tile = static_cast<const char*>(X) + mn0 * ldb;
+    rows_left = mndim - mn0 - (int64_t)w * INST * G::RPI;
+  }
+  __device__ __forceinline__ void issue(int64_t k0, int w, uint32_t dst) const {
+#pragma unroll
+    for (int j = 0; j < INST; ++j) {
+      const int idx = w * INST + j;
+      const int par = ((INST % 2 == 0) ? j : idx) & 1;
+      const int64_t left = rows_left - (int64_t)j * G::RPI;
+      const uint32_t range = left >= G::RPI ? 0x7fffffffu : left > 0 ? (uint32_t)(left * ldb) : 0u;
+      const char* base = tile + k0 * 2 + (int64_t)idx * G::RPI * ldb;
+      copy_to_lds_b128(make_srd(base, range), par ? lane_off[1] : lane_off[0], dst + idx * 1024);
+    }
+  }
+};
+// mn-major tile (B as stored, or A given as A^T): BK rows of 2 MN bytes; columns past the
+// operand's extent get an out-of-range offset.
+template <int MN, int BK, int INST>
+struct MNMajorCopy {
+  using G = TileGeom<MN, BK, false>;
+  static_assert(G::RPI % 2 == 0, "swizzle period");
+  const char* tile;
+  int64_t ldb;
+  uint32_t lane_off[2];
+  __device__ __forceinline__ void init(int, int) {}
+  __device__ __forceinline__ void retarget(const void* X, int64_t mn0, int64_t mndim, int, int lane) {
+    ldb = mndim * 2;
+    tile = static_cast<const char*>(X) + mn0 * 2;
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      const int row = par * G::RPI + lane / G::CHUNKS;
+      const int c = (lane % G::CHUNKS) ^ G::swz(row);
+      lane_off[par] = (mn0 + c * 8 < mndim) ? (uint32_t)((lane / G::CHUNKS) * ldb + c * 16) : kOOB;
+    }
+  }
+  __device__ __forceinline__ void issue(int64_t k0, int w, uint32_t dst) const {
+#pragma unroll
+    for (int j = 0; j < INST; ++j) {
+      const int idx = w * INST + j;
+      const int par = ((INST % 2 == 0) ? j : idx) & 1;
+      const char* base = tile + (k0 + (int64_t)idx * G::RPI) * ldb;
+      copy_to_lds_b128(make_srd(base, 0x7fffffffu), par ? lane_off[1] : lane_off[0], dst + idx * 1024);
+    }
+  }
+};
+
+template <int BM, int BN, int WM, int WN, int BK, int STAGES, int CW, int LAY>
+struct CopyPlanT {
+  using C = DtlCfg<BM, BN, WM, WN, BK, STAGES, CW>;
+  static constexpr bool TA = (LAY & 1) != 0, TB = (LAY & 2) != 0;
+  std::conditional_t<TA, MNMajorCopy<BM, BK, C::A_INST>, KMajorCopy<BM, BK, C::A_INST>> ca;
+  std::conditional_t<TB, KMajorCopy<BN, BK, C::B_INST>, MNMajorCopy<BN, BK, C::B_INST>> cb;
+  int w;
+  uint32_t lds_base;
+  __device__ __forceinline__ CopyPlanT(const Args& p, int w_, int lane, uint32_t lds) {
+    w = w_;
+    lds_base = lds;
+    ca.init(p.k, lane);
+    cb.init(p.k, lane);
+  }
+  __device__ __forceinline__ void retarget(const Args& p, int64_t m0, int n0, int lane) {
+    ca.retarget(p.A, m0, p.m, w, lane);
+    cb.retarget(p.B, n0, p.n, w, lane);
+  }
+  __device__ __forceinline__ void issue_tile(int kt, int stage) const {
+    const int64_t k0 = (int64_t)kt * BK;
+    const uint32_t sA = lds_base + stage * C::STAGE;
+    ca.issue(k0, w, sA);
+    cb.issue(k0, w, sA + C::A_BYTES);
+  }
+};
+
 // ---- persistent lockstep kernel --------------------------------------------------
 // gridDim.x workgroups (one per compute unit) walk the tile order with that stride.
 // The k loop runs on from one tile into the next: during a tile's last STAGES
@@ -862,17 +998,26 @@ struct CopyPlan {
 // which also lets the compiler treat the bias loads as done by the epilogue.
 // Requires K % BK == 0, KT % STAGES == 0 and KT >= 2 STAGES: k-tile t of every tile
 // sits in stage t % STAGES.
-template <int DT, int EP, int BM, int BN, int WM, int WN, int BK, int STAGES, int CW, int PRE>
+// LAY != 0: operands in the storage orders of OperandsT (their fragment pieces) and
+// CopyPlanT (their copies); the schedule is the same.
+template <int DT, int EP, int BM, int BN, int WM, int WN, int BK, int STAGES, int CW, int PRE, int LAY = 0>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_persist_kernel(Args p) {
   using C = DtlCfg<BM, BN, WM, WN, BK, STAGES, CW>;
-  using O = Operands<DT, BM, BN, WM, WN, BK, STAGES, CW>;
+  using O = std::conditional_t<LAY == 0, Operands<DT, BM, BN, WM, WN, BK, STAGES, CW>,
+                               OperandsT<DT, BM, BN, WM, WN, BK, STAGES, CW, LAY>>;
+  using CP = std::conditional_t<LAY == 0, CopyPlan<BM, BN, WM, WN, BK, STAGES, CW>,
+                                CopyPlanT<BM, BN, WM, WN, BK, STAGES, CW, LAY>>;
   using F = Frags<C::MB, C::NB>;
   constexpr int MB = C::MB, NB = C::NB, KS = C::KSTEPS, NMMA = MB * NB;
+  constexpr int PIECES = [] {
+    if constexpr (LAY == 0) return F::PIECES;
+    else return O::PIECES;
+  }();
   constexpr int EPI_BYTES = 32 * WN * 2;   // epilogue rows of one wave
   static_assert(DT == F16 || DT == BF16, "16-bit types only");
   static_assert(C::LDS + C::NW * EPI_BYTES <= 160 * 1024, "LDS");
   static_assert(KS % 2 == 0, "every k-tile starts on fragment buffer 0");
-  static_assert(PRE >= 0 && PRE < NMMA && F::PIECES <= NMMA, "MFMA slots");
+  static_assert(PRE >= 0 && PRE < NMMA && (LAY != 0 || F::PIECES <= NMMA), "MFMA slots");
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS + C::NW * EPI_BYTES];
 
   const int T = p.tiles_m * p.tiles_n;
@@ -890,8 +1035,12 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_persist_ke
   int n0 = tn * BN;
   const uint32_t lds = (uint32_t)(uintptr_t)(lds_void*)smem;
   const O op(p, m0, n0, w, wm, wn, lane, lds);   // fragment reads only
-  CopyPlan<BM, BN, WM, WN, BK, STAGES, CW> cp(p, w, lane, lds);
+  CP cp(p, w, lane, lds);
   cp.retarget(p, m0, n0, lane);
+  auto piece = [&](const char* base, int s, int q, F& f) {
+    if constexpr (LAY == 0) read_piece(op, base, s, q, f);
+    else op.read_piece(base, s, q, f);
+  };
 
   // Epilogue inputs, loaded when a tile starts and used in its epilogue (after the
   // k loop's vmcnt waits, so the epilogue never waits on the copies in flight then):
@@ -930,7 +1079,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_persist_ke
   F fr[2];
   auto read_all = [&](const char* base, int s, F& f) {
 #pragma unroll
-    for (int q = 0; q < F::PIECES; ++q) read_piece(op, base, s, q, f);
+    for (int q = 0; q < PIECES; ++q) piece(base, s, q, f);
   };
 
   // One k-tile in stage u. NEXT = false: copies of this tile's k-tile kt + STAGES;
@@ -968,7 +1117,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_persist_ke
       const int rs = last ? 0 : s + 1;
       const bool reads = !NEXT || !last || kt + 1 < KT;
       const int i0 = last ? PRE : 0;
-      const int per = (F::PIECES + NMMA - i0 - 1) / (NMMA - i0);
+      const int per = (PIECES + NMMA - i0 - 1) / (NMMA - i0);
 #pragma unroll
       for (int i = i0; i < NMMA; ++i) {
         const int a = i / MB, b = i % MB;
@@ -976,7 +1125,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_persist_ke
 #pragma unroll
         for (int e = 0; e < per; ++e) {
           const int q = (i - i0) * per + e;
-          if (q < F::PIECES && reads) read_piece(op, rbase, rs, q, fr[buf ^ 1]);
+          if (q < PIECES && reads) piece(rbase, rs, q, fr[buf ^ 1]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }

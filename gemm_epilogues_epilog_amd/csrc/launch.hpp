@@ -75,8 +75,15 @@ hipError_t launch_dtl(const Args& a, int grid, hipStream_t s) {
   constexpr int CW = (LOOP == LOCKSTEP_HALF || LOOP == LOCKSTEP_SPREAD_ILV_HALF || LOOP == PERSIST)
                          ? (BM / WM) * (BN / WN) / 2 : 0;
   if constexpr (LAY != 0) {
-    static_assert(LOOP == LOCKSTEP || LOOP == LOCKSTEP_HALF, "transposed operands: plain lockstep loop");
+    static_assert(LOOP == LOCKSTEP || LOOP == LOCKSTEP_HALF || LOOP == PERSIST,
+                  "transposed operands: plain lockstep loop or the persistent kernel");
     fn = reinterpret_cast<const void*>(&gemm_dtl_kernel<DT, EP, BM, BN, WM, WN, BK, ST, false, false, CW, LAY>);
+    if constexpr (LOOP == PERSIST) {
+      if (a.persist_grid > 0) {
+        fn = reinterpret_cast<const void*>(&gemm_persist_kernel<DT, EP, BM, BN, WM, WN, BK, ST, CW, kPersistPre, LAY>);
+        grid = a.persist_grid;
+      }
+    }
   } else if constexpr (LOOP == PINGPONG) {
     fn = reinterpret_cast<const void*>(&gemm_pp_kernel<DT, EP, BM, BN, WM, WN, BK, ST>);
   } else {
@@ -140,13 +147,15 @@ LaunchFn pick(int ep, int cfg) {
 }
 
 // Operands stored transposed (LAY bit 0: A as (k,m), bit 1: B as (n,k)), 16-bit
-// types, in the 256 x 256 tile with copies on waves 0-3 (LH) or the 128 x 128 tile
-// (LM).
-inline bool cfg_has_layouts(int c) { return c == CFG_LH || c == CFG_LM; }
+// types: the 256 x 256 tile persistent (L; one workgroup per tile when the k loop does
+// not suit the persistent kernel) or with copies on waves 0-3 (LH), or the 128 x 128
+// tile (LM).
+inline bool cfg_has_layouts(int c) { return c == CFG_L || c == CFG_LH || c == CFG_LM; }
 
 template <int DT, int EP, int LAY>
 LaunchFn pick_cfg_t(int cfg) {
   switch (cfg) {
+    case CFG_L: return &launch_dtl<DT, EP, 256, 256, 128, 64, 64, 2, PERSIST, LAY>;
     case CFG_LH: return &launch_dtl<DT, EP, 256, 256, 128, 64, 64, 2, LOCKSTEP_HALF, LAY>;
     case CFG_LM: return &launch_dtl<DT, EP, 128, 128, 32, 64, 64, 2, LOCKSTEP, LAY>;
     default: return nullptr;

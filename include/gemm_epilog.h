@@ -141,8 +141,9 @@ typedef enum { GE_OP_N = 0, GE_OP_T = 1 } ge_op_t;
  * GE_OP_T, m follows the rules of n: a multiple of 8 and at most 2^20, else
  * GE_ERR_NOT_SUPPORTED. Every other argument, rule and error is that of
  * gemm_epilog_plan, which equals gemm_epilog_plan_ex(..., GE_OP_N, GE_OP_N, out).
- * Plans with a transposed operand run the 256 x 256 tile one workgroup per tile
- * (or the 128 x 128 tile below one tile per compute unit); GE_TILE may pick LH or LM.
+ * Plans with a transposed operand run the same tiles as untransposed ones, the
+ * persistent 256 x 256 kernel included, but never split their k loop (a small grid
+ * with a deep k loop keeps the 128 x 128 tile); GE_TILE may pick L, LH or LM.
  */
 ge_status_t gemm_epilog_plan_ex(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt, ge_epilog_t ep, ge_op_t op_a,
                                 ge_op_t op_b, ge_handle_t* out);

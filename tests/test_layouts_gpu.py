@@ -22,8 +22,10 @@ from tests.helpers import assert_bgrad, assert_close, assert_mask, tight_ratio, 
 pytestmark = pytest.mark.gpu
 
 LAYOUTS = {"TN": (True, False), "NT": (False, True), "TT": (True, True)}
-TILES = [None, "LH", "LM"]
-INT_SHAPES = [(8, 8, 8), (40, 136, 72), (200, 264, 200), (304, 520, 136), (512, 520, 256)]
+TILES = [None, "L", "LH", "LM"]
+# the last two run the persistent kernel under "L" (k a multiple of 64 over an even number
+# of at least 4 k-tiles); the others fall back to one workgroup per tile
+INT_SHAPES = [(8, 8, 8), (40, 136, 72), (200, 264, 200), (304, 520, 136), (512, 520, 256), (264, 392, 512)]
 RAGGED_M = [(33, 136, 72), (300, 520, 256)]   # A not transposed: m need not be a multiple of 8
 
 
@@ -95,15 +97,17 @@ def test_random_parity_layouts(gpu, dt, lay, shape):
     assert_bgrad(gb["bgrad"], ob["bgrad"], ob["absum"], dt)
 
 
-@pytest.mark.parametrize("tile", ["LH", "LM"])
+@pytest.mark.parametrize("tile", ["L", "LH", "LM"])
 def test_layout_does_not_change_bits(gpu, tile):
     # one tile configuration, one k order: the storage order of the operands only changes
     # how they reach LDS, so the random-input results agree bit for bit (the reference
     # keeps whole tiles, as the transposed plans always do: a split k loop adds its
     # partial sums in another order)
-    m, n, k = 512, 520, 1032
+    m, n, k = 512, 520, 1024
     A, B, bias, A2, B2 = inputs.small_case(m, n, k, "bf16")
     ref = R.run(gpu, "RELU_AUX_BIAS", "bf16", A, B, bias, tile=tile + "-nosk")
+    if tile == "L":
+        assert "persistent workgroups" in ref["desc"], ref["desc"]
     for lay, (ta, tb) in LAYOUTS.items():
         g = R.run(gpu, "RELU_AUX_BIAS", "bf16", stored(A, ta), stored(B, tb), bias, tile=tile,
                   trans_a=ta, trans_b=tb)
@@ -115,7 +119,7 @@ def test_plan_describes_layout(gpu):
     h = ge.gemm_epilog_plan_ex(4096, 4096, 512, ("bf16", "bf16", "bf16"), "DRELU_BGRAD", 1, 0)
     try:
         d = ge.gemm_epilog_describe(h)
-        assert "op_a T op_b N" in d and "tile 256x256" in d and "persistent" not in d, d
+        assert "op_a T op_b N" in d and "tile 256x256" in d and "persistent workgroups" in d, d
     finally:
         ge.gemm_epilog_free(h)
     h = ge.gemm_epilog_plan_ex(256, 256, 512, ("f16", "f16", "f16"), "NONE", 0, 1)
