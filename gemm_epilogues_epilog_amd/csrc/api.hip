@@ -101,7 +101,10 @@ bool env_off(const char* name) {
 //   KT >= 128:     the 256 x 256 tile with its k loop split across the idle CUs (3-9%
 //                  faster: long runs amortise the partial sums); not for transposed
 //                  operands, whose plans do not split;
-//   otherwise:     the 128 x 128 tile (two workgroups per compute unit).
+//   otherwise:     the 128 x 128 tile (two workgroups per compute unit), with four
+//                  waves of 64 x 64 (LM4) when its grid fills the CUs without a
+//                  split and KT >= 64 or two workgroups per CU, else eight waves of
+//                  32 x 64 (LM).
 // fp32: the register-staged tiles, the largest that still gives every compute unit a
 // tile. With an operand stored transposed (lay != 0) the 256 x 256 tile never splits its
 // k loop.
@@ -118,6 +121,14 @@ int choose_cfg(int64_t m, int n, int64_t k, ge_dtype_t ab, int cus, int lay) {
     const int64_t t = tiles(gek::CFG_L);
     const int64_t kt = cdiv(k, gek::kTiles[gek::CFG_L].bk);
     if (t >= cus || 2 * t > cus || (kt >= 128 && lay == 0)) return gek::CFG_L;
+    // 128 x 128 tiles: four waves of 64 x 64 (LM4) beat eight of 32 x 64 (LM) by 1-2.4%
+    // once the grid fills the CUs and either k spans 64 or more k-tiles or the grid
+    // fills two workgroups per CU; LM4 cannot split a sparse grid's k loop (measured at
+    // 4096x1376x4096, 3072x2560x4096, 2048x2048x4096, 4096x2048x2048, 2048x4096x6144;
+    // LM stays ahead at 2048^3 and 1536x2048x4096)
+    const int64_t tm = tiles(gek::CFG_LM), rem = tm % (2 * (int64_t)cus);
+    const bool lm_splits = rem != 0 && 2 * rem <= cus && kt >= 2;
+    if (lay == 0 && !lm_splits && tm >= cus && (kt >= 64 || tm >= 2 * (int64_t)cus)) return gek::CFG_LM4;
     return gek::CFG_LM;
   }
   if (tiles(gek::CFG_M) >= cus) return gek::CFG_M;

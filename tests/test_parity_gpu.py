@@ -264,10 +264,12 @@ def test_persistent_random_matches_one_tile_per_workgroup(gpu):
     ((4096, 3200, 4096), "NN", "256x256", False),
     ((8192, 1024, 8192), "NN", "256x256", True),     # 128 tiles, 128 k-tiles: split k loop
     ((2048, 1024, 16384), "NN", "256x256", True),
-    ((4096, 1376, 4096), "NN", "128x128", False),    # 352 tiles of 128 x 128: one round at two per CU
-    ((3072, 2560, 4096), "NN", "128x128", False),
-    ((1024, 512, 2048), "NN", "128x128", True),
-    ((2048, 2048, 2048), "NN", "128x128", False),
+    ((4096, 1376, 4096), "NN", "128x128 waves 2x2", False),    # 352 tiles of 128 x 128: one round at two per CU
+    ((3072, 2560, 4096), "NN", "128x128 waves 2x2", False),
+    ((1024, 512, 2048), "NN", "128x128 waves 4x2", True),
+    ((2048, 2048, 2048), "NN", "128x128 waves 4x2", False),    # 32 k-tiles, one round: eight waves
+    ((4096, 2048, 2048), "NN", "128x128 waves 2x2", False),    # 32 k-tiles but two workgroups per CU
+    ((1536, 2048, 4096), "NN", "128x128 waves 4x2", False),    # 192 tiles, fewer than the CUs: eight waves
     ((8192, 1024, 8192), "TN", "128x128", False),    # transposed operands never split
     ((4096, 2752, 4096), "TN", "256x256", False),
 ])
