@@ -128,3 +128,24 @@ def test_plan_describes_layout(gpu):
         assert "op_a N op_b T" in d and "tile 128x128" in d, d
     finally:
         ge.gemm_epilog_free(h)
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("lay", list(LAYOUTS))
+@pytest.mark.parametrize("tile", [None, "L"])
+def test_integer_exact_fp32_vectors_layouts(gpu, dt, lay, tile):
+    # fp32 bias and bgrad with 16-bit matrices handed over transposed
+    ta, tb = LAYOUTS[lay]
+    m, n, k = 264, 392, 512
+    A, B, bias, A2, B2 = inputs.integer_case(m, n, k, dt, vec="f32")
+    As, Bs, A2s, B2s = stored(A, ta), stored(B, tb), stored(A2, ta), stored(B2, tb)
+    kw = dict(trans_a=ta, trans_b=tb)
+    o = oracle.gemm_epilog(to_np(As), to_np(Bs), "RELU_AUX_BIAS", bias=to_np(bias), ab=dt, vec="f32", **kw)
+    g = R.run(gpu, "RELU_AUX_BIAS", dt, As, Bs, bias, vec="f32", tile=tile, **kw)
+    assert np.array_equal(g["D"].view(np.uint8), o["D"].view(np.uint8)), g["desc"]
+    assert np.array_equal(g["mask"].view(np.uint32), o["mask"]), g["desc"]
+    mask = torch.from_numpy(o["mask"].view(np.int32).copy())
+    gb = R.run(gpu, "DRELU_BGRAD", dt, A2s, B2s, mask=mask, vec="f32", tile=tile, **kw)
+    ob = oracle.gemm_epilog(to_np(A2s), to_np(B2s), "DRELU_BGRAD", mask=o["mask"], ab=dt, vec="f32", **kw)
+    assert np.array_equal(gb["D"].view(np.uint8), ob["D"].view(np.uint8)), gb["desc"]
+    assert np.array_equal(gb["bgrad"], ob["bgrad"]), gb["desc"]
