@@ -149,3 +149,26 @@ def test_integer_exact_fp32_vectors_layouts(gpu, dt, lay, tile):
     ob = oracle.gemm_epilog(to_np(A2s), to_np(B2s), "DRELU_BGRAD", mask=o["mask"], ab=dt, vec="f32", **kw)
     assert np.array_equal(gb["D"].view(np.uint8), ob["D"].view(np.uint8)), gb["desc"]
     assert np.array_equal(gb["bgrad"], ob["bgrad"]), gb["desc"]
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("lay", list(LAYOUTS))
+def test_random_parity_layouts_persistent(gpu, dt, lay):
+    # the persistent kernel with transposed operands on normal inputs: GELU (not exact
+    # on integers) and the ReLU mask within the tolerances
+    ta, tb = LAYOUTS[lay]
+    m, n, k = 520, 776, 1024
+    A, B, bias, _, _ = inputs.small_case(m, n, k, dt, std=1.0, std_bias=1.0)
+    As, Bs = stored(A, ta), stored(B, tb)
+    a, b, c = to_np(As), to_np(Bs), to_np(bias)
+    wa, wb = oracle.to_f32(to_np(A), dt), oracle.to_f32(to_np(B), dt)
+    kw = dict(trans_a=ta, trans_b=tb)
+    g = R.run(gpu, "GELU_BIAS", dt, As, Bs, bias, tile="L", **kw)
+    assert "persistent workgroups" in g["desc"], g["desc"]
+    o = oracle.gemm_epilog(a, b, "GELU_BIAS", bias=c, ab=dt, **kw)
+    assert_close(g["D"], o["D"], dt, g["desc"])
+    assert tight_ratio(g["D"], o["D"], dt, wa, wb, 1.13) <= 4.0
+    g = R.run(gpu, "RELU_AUX_BIAS", dt, As, Bs, bias, tile="L", **kw)
+    o = oracle.gemm_epilog(a, b, "RELU_AUX_BIAS", bias=c, ab=dt, want_pre=True, **kw)
+    assert_close(g["D"], o["D"], dt, g["desc"])
+    assert_mask(g["mask"], o["mask"], o["pre"], m)
