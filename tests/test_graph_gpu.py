@@ -2,8 +2,8 @@
 new operand values written into the captured buffers, with eager work in between, and
 must give the bits of an eager execute of the same plan on the same values. Covers the
 split tail (whose flags carry the frozen epoch of the capture), the persistent kernel,
-DRELU_BGRAD with its second pass, the three-kernel unfused chain and transposed
-operands."""
+DRELU_BGRAD with its second pass, the three-kernel unfused chain, transposed operands
+(one workgroup per tile and persistent) and the four-wave 128 x 128 tile."""
 import numpy as np
 import pytest
 import torch
@@ -20,6 +20,9 @@ CASES = [
     ("bgrad split tail", 1024, 512, 2048, "f16", "DRELU_BGRAD", False, False, "split"),
     ("unfused", 512, 520, 256, "f16", "RELU_BIAS_UNFUSED", False, False, ""),
     ("A transposed", 512, 520, 264, "bf16", "RELU_AUX_BIAS", True, False, "op_a T"),
+    ("A transposed, persistent", 4096, 4096, 256, "bf16", "RELU_AUX_BIAS", True, False, "persistent"),
+    ("B transposed, persistent", 4096, 4096, 256, "f16", "DRELU_BGRAD", False, True, "persistent"),
+    ("four-wave 128x128", 4096, 1376, 4096, "f16", "RELU_BIAS", False, False, "waves 2x2"),
 ]
 
 
@@ -32,7 +35,8 @@ def test_graph_replays_match_eager(gpu, case):
     A, B, bias, A2, B2 = inputs.small_case(m, n, k, dt, std=k ** -0.5, std_bias=0.5)
     a_shape = (k, m) if ta else (m, k)
     Ad = torch.empty(a_shape, dtype=t, device="cuda")
-    Bd = B.cuda()
+    Bkn = B.cuda()                                   # (k, n), for the mask's forward pass
+    Bd = B.t().contiguous().cuda() if tb else Bkn    # in the storage order the plan takes
     bd = bias.cuda()
     D = torch.empty(m, n, dtype=t, device="cuda")
     groups = (m + 31) // 32
@@ -41,7 +45,7 @@ def test_graph_replays_match_eager(gpu, case):
     if ep == "DRELU_BGRAD":
         # a mask from a forward of other operands, fixed for every replay
         hf = ge.gemm_epilog_plan(m, n, k, (dt, dt, dt), "RELU_AUX_BIAS")
-        ge.gemm_epilog_execute(hf, A.cuda(), Bd, bd, D, aux, None)
+        ge.gemm_epilog_execute(hf, A.cuda(), Bkn, bd, D, aux, None)
         torch.cuda.synchronize()
         ge.gemm_epilog_free(hf)
     h = ge.gemm_epilog_plan_ex(m, n, k, (dt, dt, dt), ep, int(ta), int(tb))
