@@ -171,6 +171,31 @@ def test_worked_example_transposed(dt, ta, tb):
     assert np.array_equal(w(o4["bgrad"]), np.array(fx["bgrad"], np.float32))
 
 
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+def test_unfused_chain_rounds_its_intermediate(dt):
+    """The unfused chain stores the product in D's type (T1) before the bias add, so its
+    result differs from the fused one exactly where rounding 1 + small to that type
+    loses the small terms (fixture: up, down and a tie to even). Dropping T1's rounding
+    makes the chain equal the fused result and fails the 16-bit cases; rounding fp32
+    changes nothing, so there the two agree."""
+    fx = json.load(open(os.path.join(GOLDEN, "unfused_intermediate_rounding.json")))
+    case = fx["cases"][dt]
+    cast = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dt]
+    A = np_of(torch.tensor(fx["A"], dtype=torch.float64).to(cast), dt)
+    B = np_of(torch.tensor(case["B"], dtype=torch.float64).to(cast), dt)
+    bias = np_of(torch.tensor(fx["bias"], dtype=torch.float64).to(cast), dt)
+    w = lambda a: oracle.to_f32(a, dt)
+    f = oracle.gemm_epilog(A, B, "RELU_BIAS", bias=bias, ab=dt)
+    u = oracle.gemm_epilog(A, B, "RELU_BIAS_UNFUSED", bias=bias, ab=dt)
+    assert np.array_equal(w(f["D"]), np.array(case["fused_D"], np.float32))
+    assert np.array_equal(w(u["D"]), np.array(case["unfused_D"], np.float32))
+    assert not np.signbit(w(u["D"])).any()
+    if dt != "f32":
+        assert np.array_equal(f["D"].view(np.uint16), np.array(case["fused_D_bits"], np.uint16))
+        assert np.array_equal(u["D"].view(np.uint16), np.array(case["unfused_D_bits"], np.uint16))
+        assert not np.array_equal(f["D"].view(np.uint16), u["D"].view(np.uint16))
+
+
 def test_mask_layout_fixture():
     fx = json.load(open(os.path.join(GOLDEN, "mask_layout_40x3.json")))
     m, n, k = fx["m"], fx["n"], fx["k"]
