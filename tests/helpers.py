@@ -33,7 +33,9 @@ def assert_close(y: np.ndarray, y_ref: np.ndarray, dt: str, what: str = "D"):
     y_ref = widen(y_ref, dt)
     err = np.abs(y - y_ref)
     bound = TOL[dt] * np.maximum(1.0, np.abs(y_ref))
-    bad = err > bound
+    # "not within" rather than "beyond": a NaN error (an element never written, or a
+    # NaN where the reference is finite) fails too
+    bad = ~(err <= bound) | (~np.isfinite(y) & np.isfinite(y_ref))
     if bad.any():
         idx = np.argwhere(bad)[:5]
         raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} elements outside tolerance, e.g. "
@@ -70,7 +72,7 @@ def assert_bgrad(bg: np.ndarray, bg_ref: np.ndarray, absum: np.ndarray, dt: str)
     # the reference is rounded to dt too: allow the output rounding on top of 1e-3
     rnd = {"f16": 2.0 ** -11, "bf16": 2.0 ** -8, "f32": 2.0 ** -24}[dt]
     bound = BGRAD_TOL * absum + rnd * np.abs(r) + 1e-30
-    bad = np.abs(g - r) > bound
+    bad = ~(np.abs(g - r) <= bound) | (~np.isfinite(g) & np.isfinite(r))
     assert not bad.any(), f"bgrad: {int(bad.sum())} of {bad.size} outside 1e-3 * sum|dz|"
 
 
@@ -83,4 +85,14 @@ def tight_ratio(y: np.ndarray, y_ref: np.ndarray, dt: str, A: np.ndarray, B: np.
     k = A.shape[1]
     absprod = np.abs(A.astype(np.float64)) @ np.abs(B.astype(np.float64))
     scale = 2.0 ** -p * np.abs(y_ref) + act_slope * k * 2.0 ** -24 * absprod + 1e-7
-    return float((np.abs(y - y_ref) / scale).max())
+    ratio = np.abs(y - y_ref) / scale
+    # NaN anywhere (an unwritten element) counts as an unbounded error
+    return float("inf") if np.isnan(ratio).any() else float(ratio.max())
+
+
+def assert_all_finite(t, what: str):
+    """Every element of a full-size device output is finite (outputs are filled with NaN
+    before each run, so this also shows that every element was written)."""
+    import torch
+    bad = int((~torch.isfinite(t)).sum().item())
+    assert bad == 0, f"{what}: {bad} non-finite elements (unwritten or NaN)"

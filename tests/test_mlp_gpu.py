@@ -9,7 +9,7 @@ import torch
 
 import oracle
 from gemm_epilogues_epilog_amd import inputs
-from tests.helpers import assert_bgrad, assert_close, assert_mask, to_np
+from tests.helpers import assert_all_finite, assert_bgrad, assert_close, assert_mask, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -59,6 +59,9 @@ def test_mlp_step_8192_sampled_rows(gpu):
         print("[case] mlp step 8192 bf16: step", flush=True)
         g = st.step(X.cuda(), W1.cuda(), b1.cuda(), W2.cuda(), dY.cuda())
         torch.cuda.synchronize()
+        for name, t in (("H", st.H), ("Y", st.Y), ("dW2", g["dW2"]), ("dZ1", g["dZ1"]), ("db1", g["db1"]),
+                        ("dW1", g["dW1"])):
+            assert_all_finite(t, name)
         H, mask, Y = to_np(st.H), to_np(st.mask), to_np(st.Y)
         dW2, dZ1, db1, dW1 = to_np(g["dW2"]), to_np(g["dZ1"]), to_np(g["db1"]), to_np(g["dW1"])
     x, w1, bb1, w2, dy = (to_np(t) for t in (X, W1, b1, W2, dY))

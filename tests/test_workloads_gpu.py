@@ -12,7 +12,7 @@ import torch
 import oracle
 from gemm_epilogues_epilog_amd import inputs
 from tests import gpu_runner as R
-from tests.helpers import assert_bgrad, assert_close, assert_mask, tight_ratio, to_np
+from tests.helpers import assert_all_finite, assert_bgrad, assert_close, assert_mask, tight_ratio, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -25,7 +25,9 @@ def sample_groups(m, count=8, seed=1234):
 
 
 def check_rows(gD, W, A, B, bias, groups, epilog, dt, want_mask=None):
-    """Oracle on each sampled 32-row group; gD: device D."""
+    """Oracle on each sampled 32-row group; gD: device D, which must also be finite
+    everywhere (it is NaN-filled before the run, so an unwritten element fails)."""
+    assert_all_finite(gD, f"{W.name} {epilog} D")
     a_all, b, c_all = to_np(A), to_np(B), to_np(bias)
     wb = oracle.to_f32(b, dt)
     worst = 0.0
@@ -100,6 +102,7 @@ def test_ffn_f16_unfused_matches_fused(gpu, ffn):
     W, A, B, bias = ffn
     gf = R.run(gpu, "RELU_BIAS", "f16", A, B, bias)
     gu = R.run(gpu, "RELU_BIAS_UNFUSED", "f16", A, B, bias)
+    assert_all_finite(gu["D_dev"], "unfused D")
     assert_close(gu["D"], gf["D"], "f16", "unfused vs fused")
     groups = sample_groups(W.m)[:4]
     a, b, c = to_np(A), to_np(B), to_np(bias)
@@ -146,6 +149,8 @@ def test_mlp_bf16_8192_forward_backward(gpu):
     print(f"[case] {W.name} backward", flush=True)
     A2, B2 = W.a2(), W.b2()
     gb = R.run(gpu, "DRELU_BGRAD", "bf16", A2, B2, mask=mask_dev)
+    assert_all_finite(gb["D_dev"], "backward D")
+    assert np.isfinite(oracle.to_f32(gb["bgrad"], "bf16")).all(), "bgrad"
     a2, b2 = to_np(A2), to_np(B2)
     mask_np = to_np(mask_dev)
     for grp in groups:
@@ -194,6 +199,8 @@ def test_mlp_bf16_8192_backward_with_weights_as_stored(gpu):
     print(f"[case] {W.name} DRELU_BGRAD, A as its transpose", flush=True)
     gb = R.run(gpu, "DRELU_BGRAD", "bf16", A2.t().contiguous(), B2, mask=mask_dev, trans_a=True)
     assert "op_a T" in gb["desc"]
+    assert_all_finite(gb["D_dev"], "dX D")
+    assert np.isfinite(oracle.to_f32(gb["bgrad"], "bf16")).all(), "dX bgrad"
     for grp in groups:
         r0, r1 = 32 * grp, 32 * grp + 32
         ob = oracle.gemm_epilog(a2[r0:r1], b2, "DRELU_BGRAD", mask=mask_np[grp:grp + 1], ab="bf16")
@@ -203,6 +210,7 @@ def test_mlp_bf16_8192_backward_with_weights_as_stored(gpu):
     print(f"[case] {W.name} NONE, B as its transpose", flush=True)
     g = R.run(gpu, "NONE", "bf16", A2, B2.t().contiguous(), trans_b=True)
     assert "op_b T" in g["desc"]
+    assert_all_finite(g["D_dev"], "dW D")
     for grp in groups[:4]:
         r0, r1 = 32 * grp, 32 * grp + 32
         o = oracle.gemm_epilog(a2[r0:r1], b2, "NONE", ab="bf16")
@@ -217,6 +225,7 @@ def test_square_f16_4096_fused_and_unfused(gpu):
     assert "persistent" in gf["desc"]
     check_rows(gf["D_dev"], W, A, B, bias, sample_groups(W.m), "RELU_BIAS", "f16")
     gu = R.run(gpu, "RELU_BIAS_UNFUSED", "f16", A, B, bias)
+    assert_all_finite(gu["D_dev"], "square unfused D")
     assert_close(gu["D"], gf["D"], "f16", "unfused vs fused")
 
 
@@ -238,6 +247,8 @@ def test_shard8_shapes(gpu):
     del g
     A2, B2 = W.a2(), W.b2()
     gb = R.run(gpu, "DRELU_BGRAD", "bf16", A2, B2, mask=mask_dev)
+    assert_all_finite(gb["D_dev"], "shard backward D")
+    assert np.isfinite(oracle.to_f32(gb["bgrad"], "bf16")).all(), "shard bgrad"
     a2, b2, mask_np = to_np(A2), to_np(B2), to_np(mask_dev)
     for grp in groups:
         r0, r1 = 32 * grp, 32 * grp + 32
