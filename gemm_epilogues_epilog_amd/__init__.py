@@ -202,6 +202,25 @@ def gemm_epilog_describe(handle) -> str:
 
 
 _TORCH_NAME = {"torch.float32": "f32", "torch.float16": "f16", "torch.bfloat16": "bf16"}
+_BIAS_EPILOGS = ("RELU_BIAS", "GELU_BIAS", "RELU_AUX_BIAS", "BIAS", "RELU_BIAS_UNFUSED")
+
+
+def _require(t, name: str, dtype_name: str, numel: int, device) -> None:
+    """A caller-supplied tensor that the kernels will read or write through its data
+    pointer: a contiguous device tensor on `device`, of element type `dtype_name`
+    ("f32", "f16", "bf16" or "i32") and exactly `numel` elements. Raises ValueError,
+    before any pointer reaches the library, when it is not."""
+    if not getattr(t, "is_cuda", False):
+        raise ValueError(f"{name} must be a device tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the operands on {device}")
+    got = "i32" if str(t.dtype) == "torch.int32" else _TORCH_NAME.get(str(t.dtype))
+    if got != dtype_name:
+        raise ValueError(f"{name} must hold {dtype_name} elements, not {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() != numel:
+        raise ValueError(f"{name} must have {numel} elements, not {t.numel()}")
 
 
 class Matmul:
@@ -233,29 +252,42 @@ class Matmul:
     def describe(self) -> str:
         return gemm_epilog_describe(self.handle) if self.handle is not None else ""
 
-    def _outputs(self, A, B, relu_aux, out, bgrad):
-        """Check the operands against the plan and allocate the outputs not given."""
+    def _outputs(self, A, B, bias, relu_aux, out, bgrad):
+        """Check the operands and every tensor given against the plan, then plan (once)
+        and allocate the outputs not given."""
         import torch
-        if self.handle is None:
-            self.plan()
         for name, t in (("A", A), ("B", B)):
-            if not (t.is_cuda and t.is_contiguous() and _TORCH_NAME.get(str(t.dtype)) == self.dtype):
+            if not (getattr(t, "is_cuda", False) and t.is_contiguous() and _TORCH_NAME.get(str(t.dtype)) == self.dtype):
                 raise ValueError(f"{name} must be a contiguous {self.dtype} device tensor")
+        if B.device != A.device:
+            raise ValueError("A and B must be on the same device")
         a_shape = (self.k, self.m) if self.trans_a else (self.m, self.k)
         b_shape = (self.n, self.k) if self.trans_b else (self.k, self.n)
         if tuple(A.shape) != a_shape or tuple(B.shape) != b_shape:
             raise ValueError("operand shapes do not match the plan")
-        if out is None:
-            out = torch.empty((self.m, self.n), dtype=A.dtype, device=A.device)
+        dev = A.device
         aux_words = (self.m + 31) // 32
+        if self.epilog in _BIAS_EPILOGS:
+            if bias is None:
+                raise ValueError(f"{self.epilog} needs a bias of m = {self.m} values")
+            _require(bias, "bias", self.vec_dtype, self.m, dev)
+        if out is not None:
+            _require(out, "out", self.dtype, self.m * self.n, dev)
+        if relu_aux is not None:
+            _require(relu_aux, "relu_aux", "i32", aux_words * self.n, dev)
+        if bgrad is not None:
+            _require(bgrad, "bgrad", self.vec_dtype, self.m, dev)
+        if self.epilog == "DRELU_BGRAD" and relu_aux is None:
+            raise ValueError("DRELU_BGRAD needs the relu_aux mask of the forward pass")
+        if self.handle is None:
+            self.plan()
+        if out is None:
+            out = torch.empty((self.m, self.n), dtype=A.dtype, device=dev)
         if self.epilog == "RELU_AUX_BIAS" and relu_aux is None:
-            relu_aux = torch.empty((aux_words, self.n), dtype=torch.int32, device=A.device)
-        if self.epilog == "DRELU_BGRAD":
-            if relu_aux is None:
-                raise ValueError("DRELU_BGRAD needs the relu_aux mask of the forward pass")
-            if bgrad is None:
-                vt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[self.vec_dtype]
-                bgrad = torch.empty(self.m, dtype=vt, device=A.device)
+            relu_aux = torch.empty((aux_words, self.n), dtype=torch.int32, device=dev)
+        if self.epilog == "DRELU_BGRAD" and bgrad is None:
+            vt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[self.vec_dtype]
+            bgrad = torch.empty(self.m, dtype=vt, device=dev)
         return relu_aux, out, bgrad
 
     def _result(self, out, relu_aux, bgrad):
@@ -266,7 +298,7 @@ class Matmul:
         return out
 
     def execute(self, A, B, bias=None, relu_aux=None, out=None, bgrad=None, stream=None):
-        relu_aux, out, bgrad = self._outputs(A, B, relu_aux, out, bgrad)
+        relu_aux, out, bgrad = self._outputs(A, B, bias, relu_aux, out, bgrad)
         gemm_epilog_execute(self.handle, A, B, bias, out, relu_aux, bgrad, stream)
         return self._result(out, relu_aux, bgrad)
 
@@ -274,7 +306,7 @@ class Matmul:
         """Time the candidate configurations on these operands and keep the fastest in
         the plan (gemm_epilog_autotune). Returns (ms per execute, the result as
         execute returns it)."""
-        relu_aux, out, bgrad = self._outputs(A, B, relu_aux, out, bgrad)
+        relu_aux, out, bgrad = self._outputs(A, B, bias, relu_aux, out, bgrad)
         ms = gemm_epilog_autotune(self.handle, A, B, bias, out, relu_aux, bgrad, stream, repeats)
         return ms, self._result(out, relu_aux, bgrad)
 
