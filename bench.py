@@ -68,7 +68,7 @@ FLUSH_BYTES = 1 << 30
 # The sources that define the headline kernel's device code: the kernel headers and the
 # fp16 instantiation unit (the host runtime in api.hip only picks the configuration,
 # which the counter summary's `kernel` line pins separately).
-KERNEL_SOURCES = ("gemm_dtl.hpp", "gemm_generic.hpp", "kernels.hpp", "launch.hpp", "inst_f16.hip")
+KERNEL_SOURCES = ("gemm_dtl.hpp", "gemm_generic.hpp", "kernels.hpp", "launch.hpp", "tiles.hpp", "inst_f16.hip")
 
 
 def kernel_source_hash() -> str:

@@ -5,7 +5,8 @@ libgemm_epilog.so (built by gemm_epilogues_epilog_amd/build.py). There is no CPU
 fallback; if the library is missing every call raises.
 
 Low-level functions carry the names of the C ABI in include/gemm_epilog.h:
-gemm_epilog_plan, gemm_epilog_plan_ex, gemm_epilog_execute, gemm_epilog_autotune,
+gemm_epilog_plan, gemm_epilog_plan_ex, gemm_epilog_plan_info, gemm_epilog_execute,
+gemm_epilog_autotune, gemm_epilog_lost_waits,
 gemm_epilog_free, gemm_epilog_aux_bytes, gemm_epilog_workspace_bytes,
 gemm_epilog_describe, gemm_epilog_status_string.
 Pointers may be given as torch tensors (device memory), integers or None.
@@ -32,8 +33,8 @@ EPILOG = {"NONE": 0, "RELU_BIAS": 1, "GELU_BIAS": 2, "RELU_AUX_BIAS": 3, "DRELU_
           "RELU_BIAS_UNFUSED": 100}
 STATUS = {0: "GE_OK", 1: "GE_ERR_INVALID_VALUE", 2: "GE_ERR_NOT_SUPPORTED", 3: "GE_ERR_NULL_POINTER",
           4: "GE_ERR_MISALIGNED", 5: "GE_ERR_ALLOC", 6: "GE_ERR_HIP"}
-EXPORTS = ("gemm_epilog_plan", "gemm_epilog_plan_ex", "gemm_epilog_execute", "gemm_epilog_autotune",
-           "gemm_epilog_mfma_probe", "gemm_epilog_free",
+EXPORTS = ("gemm_epilog_plan", "gemm_epilog_plan_ex", "gemm_epilog_plan_info", "gemm_epilog_execute",
+           "gemm_epilog_autotune", "gemm_epilog_mfma_probe", "gemm_epilog_lost_waits", "gemm_epilog_free",
            "gemm_epilog_aux_bytes", "gemm_epilog_workspace_bytes", "gemm_epilog_describe",
            "gemm_epilog_status_string")
 OP_N, OP_T = 0, 1
@@ -41,6 +42,13 @@ OP_N, OP_T = 0, 1
 
 class ge_dtypes_t(ctypes.Structure):
     _fields_ = [("ab", ctypes.c_int), ("d", ctypes.c_int), ("vec", ctypes.c_int)]
+
+
+class ge_plan_info_t(ctypes.Structure):
+    _fields_ = [("tile_m", ctypes.c_int), ("tile_n", ctypes.c_int), ("tile_k", ctypes.c_int), ("waves", ctypes.c_int),
+                ("tiles", ctypes.c_int64), ("persistent_workgroups", ctypes.c_int), ("whole_tiles", ctypes.c_int),
+                ("split_workgroups", ctypes.c_int), ("split_run_ktiles", ctypes.c_int), ("group_m", ctypes.c_int),
+                ("workspace_bytes", ctypes.c_size_t)]
 
 
 class GemmEpilogError(RuntimeError):
@@ -66,12 +74,17 @@ def load() -> ctypes.CDLL:
     L.gemm_epilog_plan.restype = c_int
     L.gemm_epilog_plan_ex.argtypes = [i64, i64, i64, ge_dtypes_t, c_int, c_int, c_int, ctypes.POINTER(vp)]
     L.gemm_epilog_plan_ex.restype = c_int
+    L.gemm_epilog_plan_info.argtypes = [i64, i64, i64, ge_dtypes_t, c_int, c_int, c_int, c_int,
+                                        ctypes.POINTER(ge_plan_info_t)]
+    L.gemm_epilog_plan_info.restype = c_int
     L.gemm_epilog_execute.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
     L.gemm_epilog_execute.restype = c_int
     L.gemm_epilog_autotune.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, c_int, ctypes.POINTER(ctypes.c_float)]
     L.gemm_epilog_autotune.restype = c_int
     L.gemm_epilog_mfma_probe.argtypes = [vp, ctypes.c_size_t, c_int, c_int, c_int, vp, vp]
     L.gemm_epilog_mfma_probe.restype = c_int
+    L.gemm_epilog_lost_waits.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_uint32)]
+    L.gemm_epilog_lost_waits.restype = c_int
     L.gemm_epilog_free.argtypes = [vp]
     L.gemm_epilog_free.restype = c_int
     L.gemm_epilog_aux_bytes.argtypes = [i64, i64]
@@ -138,6 +151,23 @@ def gemm_epilog_plan_ex(m: int, n: int, k: int, dtypes, epilog, op_a: int = OP_N
     return h.value
 
 
+def gemm_epilog_plan_info(m: int, n: int, k: int, dtypes, epilog, op_a: int = OP_N, op_b: int = OP_N,
+                          compute_units: int = 256, check: bool = True):
+    """The configuration a plan would take on a device with `compute_units` compute
+    units, computed on the host without any HIP call: a dict of ge_plan_info_t's
+    fields (or (status, dict) with check=False)."""
+    ab, d, vec = (_dt(x) for x in dtypes)
+    info = ge_plan_info_t()
+    st = load().gemm_epilog_plan_info(int(m), int(n), int(k), ge_dtypes_t(ab, d, vec), _ep(epilog), int(op_a),
+                                      int(op_b), int(compute_units), ctypes.byref(info))
+    out = {name: getattr(info, name) for name, _ in ge_plan_info_t._fields_}
+    if not check:
+        return st, out
+    if st != 0:
+        raise GemmEpilogError(st, "gemm_epilog_plan_info")
+    return out
+
+
 def gemm_epilog_execute(handle, A, B, bias=None, D=None, aux=None, bgrad=None, stream=None, check: bool = True):
     """Enqueue one execute. stream: hipStream_t as int, a torch stream, or None for
     torch's current stream on the current device."""
@@ -187,6 +217,21 @@ def gemm_epilog_mfma_probe(operands, dtype, iters: int, workgroups: int, out, st
     if check and st != 0:
         raise GemmEpilogError(st, "gemm_epilog_mfma_probe")
     return st
+
+
+def gemm_epilog_lost_waits(handle, stream=None) -> int:
+    """Synchronise the stream and return (and reset) the count of split-tail waits of
+    this plan that ran out (their tiles hold NaN)."""
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream().cuda_stream
+    elif not isinstance(stream, int):
+        stream = stream.cuda_stream
+    n = ctypes.c_uint32(0)
+    st = load().gemm_epilog_lost_waits(handle, stream, ctypes.byref(n))
+    if st != 0:
+        raise GemmEpilogError(st, "gemm_epilog_lost_waits")
+    return int(n.value)
 
 
 def gemm_epilog_free(handle) -> int:

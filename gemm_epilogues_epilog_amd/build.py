@@ -1,7 +1,8 @@
 """Compile the HIP library libgemm_epilog.so for gfx950 (in-tree, next to this file).
 
-Each translation unit is compiled by hipcc in parallel, then linked into one shared
-library that exports the C ABI of include/gemm_epilog.h.
+Each translation unit is compiled in parallel (the HIP units by hipcc, the host-only
+plan arithmetic by g++), then linked into one shared library that exports the C ABI of
+include/gemm_epilog.h.
 """
 import os
 import subprocess
@@ -28,9 +29,18 @@ FLAGS = [
 ]
 
 
+# Host-only C++ (the plan arithmetic): plain g++, no HIP.
+HOST_SOURCES = ["plan_host.cpp"]
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE, "-I", CSRC]
+
+
 def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(OBJ, src.replace(".hip", ".o"))
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    if src in HOST_SOURCES:
+        obj = os.path.join(OBJ, src.replace(".cpp", ".o"))
+        cmd = ["g++", *HOST_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    else:
+        obj = os.path.join(OBJ, src.replace(".hip", ".o"))
+        cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -42,7 +52,7 @@ def _compile(src: str, verbose: bool) -> str:
 def build(verbose: bool = False, jobs: int = 8) -> str:
     os.makedirs(OBJ, exist_ok=True)
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+        objs = list(ex.map(lambda s: _compile(s, verbose), HOST_SOURCES + SOURCES))
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", LIB + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)

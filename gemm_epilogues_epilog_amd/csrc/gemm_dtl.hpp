@@ -15,8 +15,8 @@
 // layout (k contiguous per lane) produced from the n-contiguous tile.
 //
 // Pipeline. STAGES LDS stages form a ring. The copies are inline assembly, ordered
-// by hand with vmcnt / lgkmcnt waits and workgroup barriers (the lockstep, persistent
-// and ping-pong loops below describe their schedules): the compiler would otherwise
+// by hand with vmcnt / lgkmcnt waits and workgroup barriers (the lockstep and
+// persistent loops below describe their schedules): the compiler would otherwise
 // make every LDS read wait for every copy still in flight.
 //
 // Epilogue. Each wave writes its finished (activated, rounded) accumulators to LDS
@@ -31,6 +31,7 @@
 #include <type_traits>
 
 #include "kernels.hpp"
+#include "tiles.hpp"
 
 namespace gek {
 
@@ -400,20 +401,6 @@ struct Operands {
       copy_to_lds_b128(rb, off, sB + (w * C::B_INST + j) * 1024);
     }
   }
-  // Copy instruction j of k-tile kt, j in [0, INST): A instructions first, then B.
-  __device__ __forceinline__ void issue_one(int kt, int stage, int j) const {
-    const int k0 = kt * BK;
-    const bool tail = k0 + BK > K;
-    const uint32_t sA = lds_base + stage * C::STAGE;
-    if (j < C::A_INST) {
-      const uint32_t off = (tail && k0 + a_chunk[j] * 8 >= K) ? kOOB : a_src[j];
-      copy_to_lds_b128(make_srd(Abase + (int64_t)k0 * 2), off, sA + (w * C::A_INST + j) * 1024);
-    } else {
-      const int jb = j - C::A_INST;
-      const uint32_t off = (tail && k0 + b_row[jb] >= K) ? kOOB : b_src[jb];
-      copy_to_lds_b128(make_srd(Bbase + (int64_t)k0 * N * 2), off, sA + C::A_BYTES + (w * C::B_INST + jb) * 1024);
-    }
-  }
   // All copies of k-tile kt: in KSTEPS parts (A then B of each) when the counts divide,
   // else all A then all B.
   __device__ __forceinline__ void issue_tile(int kt, int stage) const {
@@ -423,19 +410,6 @@ struct Operands {
         issue_range(kt, stage, part * A_PART, (part + 1) * A_PART, part * B_PART, (part + 1) * B_PART);
     } else {
       issue_range(kt, stage, 0, C::A_INST, 0, C::B_INST);
-    }
-  }
-
-  // Fragments of k-step s from the stage at `base`.
-  __device__ __forceinline__ void read_step(const char* base, int s, i32x4 (&fa)[MB], i32x4 (&fb)[NB]) const {
-#pragma unroll
-    for (int b = 0; b < MB; ++b) fa[b] = *reinterpret_cast<const i32x4*>(base + a_rd[s] + b * 32 * C::A_ROWB);
-#pragma unroll
-    for (int a = 0; a < NB; ++a) {
-      const char* q = base + b_rd[a] + 16 * s * C::B_ROWB;
-      const i32x2 lo = ds_read_tr(q);
-      const i32x2 hi = ds_read_tr(q + 4 * C::B_ROWB);
-      fb[a] = i32x4{lo[0], lo[1], hi[0], hi[1]};
     }
   }
 };
@@ -461,14 +435,6 @@ __device__ __forceinline__ void read_piece(const O& op, const char* base, int s,
     const int n = (q - 2 - MB) / 2 + 1, h = (q - 2 - MB) % 2;
     f.b[n][h] = ds_read_tr(base + op.b_rd[n] + 16 * s * BROW + h * 4 * BROW);
   }
-}
-
-template <int DT, int MB, int NB>
-__device__ __forceinline__ void mma_step(f32x16 (&acc)[NB][MB], const i32x4 (&fa)[MB], const i32x4 (&fb)[NB]) {
-#pragma unroll
-  for (int a = 0; a < NB; ++a)
-#pragma unroll
-    for (int b = 0; b < MB; ++b) acc[a][b] = Tr<DT>::mma(fb[a], fa[b], acc[a][b]);
 }
 
 // ---- operands in either storage order ----------------------------------------------
@@ -662,17 +628,14 @@ struct OperandsT {
 // All waves run the same schedule. At the end of k-tile t every wave waits until
 // its own copies of tile t+1 have landed and its reads of tile t are done, and one
 // barrier publishes tile t+1 and releases stage t % STAGES.
-//   SPREAD = false: the copies of tile t + STAGES go to that stage at once.
-//   SPREAD = true:  the copies of tile t + STAGES - 1 are issued during tile t, one
-//                   at a time between its MFMAs, into the stage tile t-1 released,
-//                   so no wave queues a burst of copies behind the texture unit.
+// The copies of tile t + STAGES go to the released stage right after that barrier.
 //   ILV = true:     each MFMA of a k-step is followed by one fragment read of the
 //                   next step, in consumption order, instead of a block of reads.
 //
 // lockstep_tile accumulates the k-tiles [kb, kb + nt) of one output tile into acc.
 // It expects no copy of its own in flight and every wave done with the LDS; on
 // return every copy has landed, but reads of the last stage may still be in flight.
-template <int DT, int BM, int BN, int WM, int WN, int BK, int STAGES, bool SPREAD, bool ILV, int CW, int LAY = 0>
+template <int DT, int BM, int BN, int WM, int WN, int BK, int STAGES, bool ILV, int CW, int LAY = 0>
 __device__ __forceinline__ void lockstep_tile(const Args& p, char* smem, int64_t m0, int n0, int kb, int nt,
                                               f32x16 (&acc)[WN / 32][WM / 32]) {
   using C = DtlCfg<BM, BN, WM, WN, BK, STAGES, CW>;
@@ -680,15 +643,10 @@ __device__ __forceinline__ void lockstep_tile(const Args& p, char* smem, int64_t
                                OperandsT<DT, BM, BN, WM, WN, BK, STAGES, CW, LAY>>;
   using F = Frags<C::MB, C::NB>;
   static_assert(DT == F16 || DT == BF16, "16-bit types only");
-  static_assert(LAY == 0 || (!SPREAD && !ILV), "transposed operands use the plain lockstep loop");
+  static_assert(LAY == 0 || !ILV, "transposed operands use the plain lockstep loop");
   static_assert(C::KSTEPS % 2 == 0, "every tile starts on fragment buffer 0");
-  static_assert(!SPREAD || STAGES >= 3, "spread copies run STAGES - 2 tiles ahead");
   constexpr int MB = C::MB, NB = C::NB, KS = C::KSTEPS;
   constexpr int NMMA = MB * NB;                          // MFMAs per k-step
-  static_assert(!SPREAD || C::INST % KS == 0, "copies split evenly over the k-steps");
-  constexpr int PER_STEP = C::INST / KS;                 // spread copies per k-step
-  static_assert(!SPREAD || NMMA % PER_STEP == 0, "copies spread evenly over the MFMAs");
-  constexpr int EVERY = SPREAD ? NMMA / PER_STEP : 1;
   static_assert(!ILV || F::PIECES <= NMMA, "one fragment read per MFMA");
 
   const int lane = threadIdx.x & 63;
@@ -716,12 +674,11 @@ __device__ __forceinline__ void lockstep_tile(const Args& p, char* smem, int64_t
   };
 
   // prologue: tile 0 complete, the next tiles in flight
-  constexpr int AHEAD = SPREAD ? STAGES - 1 : STAGES;   // tiles issued before the loop
   if (copier) {
 #pragma unroll
-    for (int t = 0; t < AHEAD; ++t)
+    for (int t = 0; t < STAGES; ++t)
       if (t < KT) op.issue_tile(kb + t, t);
-    wait_tiles<C::INST, AHEAD - 1>(min(AHEAD - 1, KT - 1));
+    wait_tiles<C::INST, STAGES - 1>(min(STAGES - 1, KT - 1));
   }
   barrier_only();
   read_all(smem, 0, fr[0]);
@@ -730,12 +687,7 @@ __device__ __forceinline__ void lockstep_tile(const Args& p, char* smem, int64_t
   // can be in a steady tile).
   auto wait_next_tile = [&](int kt, auto steady_tag) {
     if constexpr (decltype(steady_tag)::value) {
-      if constexpr (SPREAD) wait_vmcnt<((STAGES - 3) * KS + KS - 1) * PER_STEP>();
-      else wait_vmcnt<(STAGES - 2) * C::INST>();
-    } else if constexpr (SPREAD) {
-      const int whole = max(0, min(STAGES - 3, KT - 2 - kt));
-      const int n = whole * KS + (kt + STAGES - 1 < KT ? KS - 1 : 0);   // in units of PER_STEP
-      wait_tiles<PER_STEP, (STAGES - 3) * KS + KS - 1>(n);
+      wait_vmcnt<(STAGES - 2) * C::INST>();
     } else {
       wait_tiles<C::INST, STAGES - 2>(min(STAGES - 2, KT - 2 - kt));
     }
@@ -747,9 +699,6 @@ __device__ __forceinline__ void lockstep_tile(const Args& p, char* smem, int64_t
     constexpr bool STEADY = decltype(steady_tag)::value;
     const char* cur = smem + u * C::STAGE;
     const char* nxt = smem + ((u + 1) % STAGES) * C::STAGE;
-    const int kc = kt + STAGES - 1;                 // SPREAD: tile copied during this one
-    const int uc = (u + STAGES - 1) % STAGES;       // ... into the stage tile kt-1 released
-    const bool copy = STEADY || kc < KT;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       const int buf = s & 1;
@@ -759,9 +708,7 @@ __device__ __forceinline__ void lockstep_tile(const Args& p, char* smem, int64_t
         wait_lgkmcnt<0>();                // this wave's reads of stage u are done
         if (copier) wait_next_tile(kt, steady_tag);   // this wave's copies of tile kt+1 have landed
         barrier_only();
-        if constexpr (!SPREAD) {
-          if (copier && (STEADY || kt + STAGES < KT)) op.issue_tile(kb + kt + STAGES, u);
-        }
+        if (copier && (STEADY || kt + STAGES < KT)) op.issue_tile(kb + kt + STAGES, u);
       }
       const char* rbase = last ? nxt : cur;
       const int rs = last ? 0 : s + 1;
@@ -778,17 +725,14 @@ __device__ __forceinline__ void lockstep_tile(const Args& p, char* smem, int64_t
             if (i < F::PIECES && reads) read_piece(op, rbase, rs, i, fr[buf ^ 1]);
           }
         }
-        if constexpr (SPREAD && LAY == 0) {
-          if (i % EVERY == 0 && copy && copier) op.issue_one(kb + kc, uc, (i / EVERY) * KS + s);
-        }
-        if constexpr (ILV || SPREAD) __builtin_amdgcn_sched_barrier(0);
+        if constexpr (ILV) __builtin_amdgcn_sched_barrier(0);
       }
       // keep each k-step's reads next to its MFMAs (no hoisting across steps)
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // A tile is steady when its reads of tile kt+1 and its copies (of tile kt + STAGES,
-  // or kt + STAGES - 1 when spread) stay below KT.
+  // A tile is steady when its reads of tile kt+1 and its copies of tile kt + STAGES
+  // stay below KT.
   int kt = 0;
   for (; kt + 2 * STAGES <= KT; kt += STAGES) {
 #pragma unroll
@@ -802,8 +746,7 @@ __device__ __forceinline__ void lockstep_tile(const Args& p, char* smem, int64_t
 }
 
 // One workgroup per output tile. LAY: storage order of the operands (OperandsT).
-template <int DT, int EP, int BM, int BN, int WM, int WN, int BK, int STAGES, bool SPREAD, bool ILV, int CW,
-          int LAY = 0>
+template <int DT, int EP, int BM, int BN, int WM, int WN, int BK, int STAGES, bool ILV, int CW, int LAY = 0>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_dtl_kernel(Args p) {
   using C = DtlCfg<BM, BN, WM, WN, BK, STAGES>;
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
@@ -816,7 +759,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_dtl_kernel
   const int wm = w % C::WAVES_M, wn = w / C::WAVES_M;
 
   f32x16 acc[C::NB][C::MB];
-  lockstep_tile<DT, BM, BN, WM, WN, BK, STAGES, SPREAD, ILV, CW, LAY>(p, smem, m0, n0, 0, (p.k + BK - 1) / BK, acc);
+  lockstep_tile<DT, BM, BN, WM, WN, BK, STAGES, ILV, CW, LAY>(p, smem, m0, n0, 0, (p.k + BK - 1) / BK, acc);
 
   // every wave is done with the stages: reuse them as per-wave epilogue scratch
   wait_lgkmcnt<0>();
@@ -1203,11 +1146,30 @@ struct PartialLayout {
 };
 constexpr int kDeviceScope = 16;   // cache-policy bit sc1 of a buffer instruction
 
-// Spin limit of the owner's wait (about a second): a partial that never arrives
-// turns the tile into NaN instead of hanging the device.
-constexpr int kSkSpinLimit = 1 << 20;
+// Flag protocol of a published partial. A flag is 0 when idle. The run that computed
+// the partial swaps 0 -> epoch once its stores have completed. The owner waits (a
+// bounded spin, p.sk_spin_limit polls, about a second by default) for the epoch, adds
+// the partial and swaps epoch -> 0. If the wait runs out, the owner swaps 0 -> kSkAbort
+// (unless the epoch arrived meanwhile), counts the loss in p.sk_flag[p.sk_wgs] and gives
+// the tile's D NaN; the publisher that finds kSkAbort resets the flag to 0 instead of
+// publishing. So every flag is 0 again when the kernel ends, lost wait or not, and a
+// later execute with the same epoch (a replay of a captured graph) never finds a stale
+// one.
+constexpr uint32_t kSkAbort = 0xffffffffu;   // epochs stay below 2^31
 
-template <int DT, int EP, int BM, int BN, int WM, int WN, int BK, int STAGES, bool SPREAD, bool ILV, int CW>
+__device__ __forceinline__ bool sk_wait_flag(uint32_t* flag, uint32_t epoch, uint32_t spin_limit) {
+  for (uint32_t spins = 0; spins < spin_limit; ++spins) {
+    if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch) return true;
+    __builtin_amdgcn_s_sleep(8);
+  }
+  uint32_t expected = 0u;
+  if (__hip_atomic_compare_exchange_strong(flag, &expected, kSkAbort, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT))
+    return false;                 // abandoned: the late publisher will reset it
+  return expected == epoch;       // published while the spin ran out
+}
+
+template <int DT, int EP, int BM, int BN, int WM, int WN, int BK, int STAGES, bool ILV, int CW>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_sk_kernel(Args p) {
   using C = DtlCfg<BM, BN, WM, WN, BK, STAGES>;
   using PL = PartialLayout<C::MB, C::NB>;
@@ -1221,33 +1183,26 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_sk_kernel(
 
   // ---- this workgroup's pieces: a whole tile, or a run's partial and owner piece ----
   const bool split = (int)blockIdx.x >= p.dp_tiles;
-  int r = 0;              // run
-  int pa_t = 0, pa_kb = 0, pa_nt = 0;   // partial piece (pa_nt == 0: none)
-  int pos, kb, nt;        // whole tile or owner piece (nt == 0: none)
+  int r = 0;                                   // run
+  SkRun run{0, 0, 0, 0, 0, 0};
+  int pos, nt;                                 // whole tile or owner piece (nt == 0: none)
   if (!split) {
     pos = xcd_remap(blockIdx.x, p.dp_tiles);
-    kb = 0;
     nt = KT;
   } else {
     r = xcd_remap(blockIdx.x - p.dp_tiles, p.sk_wgs);
-    const int u0 = r * p.sk_units;
-    const int u1 = min((p.tiles_m * p.tiles_n - p.dp_tiles) * KT, u0 + p.sk_units);
-    const int ts = (u0 + KT - 1) / KT * KT;   // first tile start at or after u0
-    if (u0 < min(ts, u1)) {
-      pa_t = u0 / KT;
-      pa_kb = u0 - pa_t * KT;
-      pa_nt = min(ts, u1) - u0;
-    }
-    pos = p.dp_tiles + ts / KT;
-    kb = 0;
-    nt = max(0, u1 - ts);
+    run = sk_run(r, p.sk_units, KT, p.tiles_m * p.tiles_n - p.dp_tiles, p.sk_wgs);
+    pos = p.dp_tiles + run.own_t;
+    nt = run.own_nt;
   }
+  const int pa_t = run.pa_t, pa_kb = run.pa_kb, pa_nt = run.pa_nt;
 
   f32x16 acc[NB][MB];
+  bool lost = false;   // the owner: a partner's partial did not arrive in time
   if (pa_nt > 0) {
     int tm, tn;
     raster(p, p.dp_tiles + pa_t, tm, tn);
-    lockstep_tile<DT, BM, BN, WM, WN, BK, STAGES, SPREAD, ILV, CW>(p, smem, (int64_t)tm * BM, tn * BN, pa_kb, pa_nt, acc);
+    lockstep_tile<DT, BM, BN, WM, WN, BK, STAGES, ILV, CW>(p, smem, (int64_t)tm * BM, tn * BN, pa_kb, pa_nt, acc);
     // store the partial at device scope, then publish it once every wave's stores
     // have completed
     const __amdgpu_buffer_rsrc_t slot = rsrc(reinterpret_cast<char*>(p.sk_partial) + (size_t)r * slot_bytes);
@@ -1264,48 +1219,54 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_sk_kernel(
     wait_vmcnt<0>();
     wait_lgkmcnt<0>();   // also: every wave is done with the LDS before the next piece
     barrier_only();
-    if (threadIdx.x == 0) __hip_atomic_store(p.sk_flag + r, p.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) {
+      uint32_t expected = 0u;
+      if (!__hip_atomic_compare_exchange_strong(p.sk_flag + r, &expected, p.epoch, __ATOMIC_RELAXED,
+                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+        __hip_atomic_store(p.sk_flag + r, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // owner gave up
+    }
   }
   if (nt == 0) return;
 
   int tm, tn;
   raster(p, pos, tm, tn);
-  lockstep_tile<DT, BM, BN, WM, WN, BK, STAGES, SPREAD, ILV, CW>(p, smem, (int64_t)tm * BM, tn * BN, kb, nt, acc);
+  lockstep_tile<DT, BM, BN, WM, WN, BK, STAGES, ILV, CW>(p, smem, (int64_t)tm * BM, tn * BN, 0, nt, acc);
   if (split) {
-    // the owner: add the partials of the runs that hold the rest of the tile
-    const int t = pos - p.dp_tiles;
-    const int last = min(((t + 1) * KT - 1) / p.sk_units, p.sk_wgs - 1);
-    bool lost = false;
-    for (int o = r + 1; o <= last; ++o) {
-      int spins = 0;
-      // the partial's loads are issued only after its flag has been seen (control
-      // dependency) and read the memory side (device scope)
-      while (__hip_atomic_load(p.sk_flag + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != p.epoch) {
-        if (++spins > kSkSpinLimit) {
-          lost = true;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(8);
-      }
-      const __amdgpu_buffer_rsrc_t slot = rsrc(reinterpret_cast<char*>(p.sk_partial) + (size_t)o * slot_bytes);
-      // sixteen loads in flight at a time, then the adds
-      constexpr int BATCH = PL::QUADS < 16 ? PL::QUADS : 16;
-      static_assert(PL::QUADS % BATCH == 0, "load batches");
-#pragma unroll
-      for (int q0 = 0; q0 < PL::QUADS; q0 += BATCH) {
-        i32x4 v[BATCH];
-#pragma unroll
-        for (int j = 0; j < BATCH; ++j)
-          v[j] = __builtin_amdgcn_raw_buffer_load_b128(slot, PL::off(w, q0 + j, lane), 0, kDeviceScope);
-#pragma unroll
-        for (int j = 0; j < BATCH; ++j) {
-          const int q = q0 + j, a = q / (4 * MB), bb = (q / 4) % MB, r4 = q % 4;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[a][bb][4 * r4 + e] += __int_as_float(v[j][e]);
-        }
-      }
+    // the owner: one thread waits for the partials of runs r+1 .. last, which hold the
+    // rest of the tile, and tells the workgroup through LDS whether all arrived
+    __shared__ uint32_t lost_any;
+    if (threadIdx.x == 0) {
+      uint32_t lost = 0u;
+      for (int o = r + 1; o <= run.last; ++o) lost += sk_wait_flag(p.sk_flag + o, p.epoch, p.sk_spin_limit) ? 0u : 1u;
+      if (lost) __hip_atomic_fetch_add(p.sk_flag + p.sk_wgs, lost, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      lost_any = lost;
     }
-    if (lost) {
+    wait_lgkmcnt<0>();
+    barrier_only();
+    // the partials' loads follow the flags seen before the barrier and read the memory
+    // side (device scope)
+    lost = lost_any != 0u;
+    if (!lost) {
+      for (int o = r + 1; o <= run.last; ++o) {
+        const __amdgpu_buffer_rsrc_t slot = rsrc(reinterpret_cast<char*>(p.sk_partial) + (size_t)o * slot_bytes);
+        // sixteen loads in flight at a time, then the adds
+        constexpr int BATCH = PL::QUADS < 16 ? PL::QUADS : 16;
+        static_assert(PL::QUADS % BATCH == 0, "load batches");
+#pragma unroll
+        for (int q0 = 0; q0 < PL::QUADS; q0 += BATCH) {
+          i32x4 v[BATCH];
+#pragma unroll
+          for (int j = 0; j < BATCH; ++j)
+            v[j] = __builtin_amdgcn_raw_buffer_load_b128(slot, PL::off(w, q0 + j, lane), 0, kDeviceScope);
+#pragma unroll
+          for (int j = 0; j < BATCH; ++j) {
+            const int q = q0 + j, a = q / (4 * MB), bb = (q / 4) % MB, r4 = q % 4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[a][bb][4 * r4 + e] += __int_as_float(v[j][e]);
+          }
+        }
+      }
+    } else {
 #pragma unroll
       for (int a = 0; a < NB; ++a)
 #pragma unroll
@@ -1315,107 +1276,27 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_sk_kernel(
     }
   }
   // every wave is done with the stages: reuse them as per-wave epilogue scratch
+  wait_vmcnt<0>();
   wait_lgkmcnt<0>();
   barrier_only();
   if (split && threadIdx.x == 0) {
-    // Every wave has passed its waits: clear the flags this owner consumed (no other
-    // workgroup reads them). A flag then holds the epoch only between its run's publish
-    // and its owner's wait, so a later execute that repeats this epoch (a replay of a
-    // captured graph, whose arguments are frozen) waits for its own partials.
-    const int t = pos - p.dp_tiles;
-    const int last = min(((t + 1) * KT - 1) / p.sk_units, p.sk_wgs - 1);
-    for (int o = r + 1; o <= last; ++o)
-      __hip_atomic_store(p.sk_flag + o, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // every wave has read the partials: set the consumed flags (epoch) back to 0; an
+    // abandoned flag (kSkAbort) is reset by its late publisher
+    for (int o = r + 1; o <= run.last; ++o) {
+      uint32_t expected = p.epoch;
+      __hip_atomic_compare_exchange_strong(p.sk_flag + o, &expected, 0u, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
   epilogue_lds<DT, EP, MB, NB, WN>(p, acc, (int64_t)tm * BM + wm * WM, tn * BN + wn * WN, lane,
                                    smem + w * C::SCRATCH);
-}
-
-// ---- ping-pong main loop -------------------------------------------------------
-// The workgroup's waves form two groups, G0 = waves 0 .. NW/2-1 and G1 = the rest;
-// waves are dealt to the four SIMDs in order, so every SIMD runs one wave of each
-// group. The groups alternate between a memory phase M(t) (read all fragments of
-// k-tile t into registers, issue this wave's copies of tile t + STAGES - 1, wait for
-// the reads) and a compute phase C(t) (all MFMAs of tile t back to back), offset by
-// one phase, with one workgroup barrier between phases:
-//
-//   phase   0      1      2      3      4     ...
-//   G0     M(0)   C(0)   M(1)   C(1)   M(2)
-//   G1      -     M(0)   C(0)   M(1)   C(1)
-//
-// so in every phase one wave per SIMD issues MFMAs while the other issues LDS reads
-// and copies. Tile t lives in stage t % STAGES; G1 reads it last, in phase 2t+1, so
-// from phase 2t+2 its stage may be refilled with tile t + STAGES, whose copies are
-// issued in M(t+1) of both groups and must have landed at the barrier that opens
-// phase 2(t + STAGES).
-template <int DT, int EP, int BM, int BN, int WM, int WN, int BK, int STAGES>
-__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_pp_kernel(Args p) {
-  using C = DtlCfg<BM, BN, WM, WN, BK, STAGES>;
-  using O = Operands<DT, BM, BN, WM, WN, BK, STAGES>;
-  static_assert(DT == F16 || DT == BF16, "16-bit types only");
-  static_assert(C::NW == 8, "two groups of one wave per SIMD");
-  static_assert(STAGES >= 3, "copies of tile t + STAGES - 1 go out in M(t)");
-  constexpr int MB = C::MB, NB = C::NB, KS = C::KSTEPS;
-
-  __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
-
-  int tm, tn;
-  tile_coords(p, tm, tn);
-  const int64_t m0 = (int64_t)tm * BM;
-  const int n0 = tn * BN;
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = w % C::WAVES_M, wn = w / C::WAVES_M;
-  const bool g1 = w >= C::NW / 2;
-  const O op(p, m0, n0, w, wm, wn, lane, (uint32_t)(uintptr_t)(lds_void*)smem);
-  const int KT = (p.k + BK - 1) / BK;
-
-  f32x16 acc[NB][MB];
-#pragma unroll
-  for (int a = 0; a < NB; ++a)
-#pragma unroll
-    for (int b = 0; b < MB; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
-  i32x4 fa[KS][MB];
-  i32x4 fb[KS][NB];
-
-  // prologue: tiles 0 .. STAGES-2 in flight; tile 0 published by the first barrier
-#pragma unroll
-  for (int t = 0; t < STAGES - 1; ++t)
-    if (t < KT) op.issue_tile(t, t);
-  wait_tiles<C::INST, STAGES - 2>(min(STAGES - 2, KT - 1));
-  barrier_only();
-  if (g1) barrier_only();   // G1 sits out phase 0
-
-  // Before the barrier that opens phase 2(t+1), every wave has issued the copies of
-  // tiles up to t + STAGES - 1 (G0 in M(t), G1 in M(t)); tile t+1 must have landed,
-  // so the copies of tiles t+2 .. t+STAGES-1 may still be in flight.
-  auto wait_tile_after = [&](int t) {
-    wait_tiles<C::INST, STAGES - 2>(min(STAGES - 2, KT - 2 - t));
-  };
-
-  for (int t = 0; t < KT; ++t) {
-    const char* cur = smem + (t % STAGES) * C::STAGE;
-    // ---- M(t) ----
-#pragma unroll
-    for (int s = 0; s < KS; ++s) op.read_step(cur, s, fa[s], fb[s]);
-    if (t + STAGES - 1 < KT) op.issue_tile(t + STAGES - 1, (t + STAGES - 1) % STAGES);
-    wait_lgkmcnt<0>();
-    if (g1) wait_tile_after(t);   // G1's M(t) ends right before phase 2(t+1)
-    barrier_only();
-    // ---- C(t) ----
-    __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int s = 0; s < KS; ++s) mma_step<DT, MB, NB>(acc, fa[s], fb[s]);
-    __builtin_amdgcn_s_setprio(0);
-    if (!g1) wait_tile_after(t);  // G0's C(t) ends right before phase 2(t+1)
-    barrier_only();
+  if (lost) {
+    // the epilogue above wrote the mask (no bit set) and NaN row sums; an activation
+    // may have turned the NaN accumulators into zeros, so D's tile is written again
+    // with them as they are
+    epilogue_lds<DT, NONE, MB, NB, WN>(p, acc, (int64_t)tm * BM + wm * WM, tn * BN + wn * WN, lane,
+                                       smem + w * C::SCRATCH);
   }
-  if (!g1) barrier_only();   // G0 sits out the last phase (G1's final C)
-
-  // every wave is done with the stages: reuse them as per-wave epilogue scratch
-  epilogue_lds<DT, EP, MB, NB, WN>(p, acc, m0 + wm * WM, n0 + wn * WN, lane, smem + w * C::SCRATCH);
 }
 
 }  // namespace gek

@@ -1,50 +1,14 @@
-// Kernel-configuration table shared by the host runtime and the per-type
-// instantiation units.
+// Kernel launchers of each tile configuration (tiles.hpp), shared by the host runtime
+// and the per-type instantiation units.
 #pragma once
 
 #include <hip/hip_runtime.h>
 
 #include "gemm_dtl.hpp"
 #include "gemm_generic.hpp"
+#include "tiles.hpp"
 
 namespace gek {
-
-// Workgroup tile (BM x BN), wave tile (WM x WN), k-tile and LDS stages of each
-// configuration. S and M use the register-staged kernel (any type); the L family
-// uses the direct-to-LDS kernel (16-bit types only).
-struct TileCfg {
-  int bm, bn, wm, wn, bk, stages;
-  const char* name;
-  const char* loop;   // main loop of the direct-to-LDS kernels
-};
-
-enum CfgId { CFG_S = 0, CFG_M, CFG_L, CFG_LH, CFG_LA, CFG_LI, CFG_LS, CFG_LSH, CFG_LM, CFG_W4, CFG_W4S, CFG_P, CFG_LM4,
-             CFG_COUNT };
-
-constexpr TileCfg kTiles[CFG_COUNT] = {
-    {64, 64, 32, 32, 0, 2, "S", ""},
-    {128, 128, 64, 64, 0, 2, "M", ""},
-    {256, 256, 128, 64, 64, 2, "L", "persistent lockstep interleaved, copies on waves 0-3"},   // 8 waves (default)
-    {256, 256, 128, 64, 64, 2, "LH", "lockstep, copies on waves 0-3"},
-    {256, 256, 128, 64, 64, 2, "LA", "lockstep"},
-    {256, 256, 128, 64, 64, 2, "LI", "lockstep interleaved"},
-    {256, 256, 128, 64, 32, 4, "LS", "lockstep spread interleaved"},
-    {256, 256, 128, 64, 32, 4, "LSH", "lockstep spread interleaved, copies on waves 0-3"},
-    {128, 128, 32, 64, 64, 2, "LM", "lockstep"},                        // 8 waves of 32 x 64, two per CU
-    {256, 256, 128, 128, 64, 2, "W4", "lockstep"},                      // 4 waves of 128 x 128
-    {256, 256, 128, 128, 32, 4, "W4S", "lockstep spread interleaved"},
-    {256, 256, 128, 64, 32, 4, "P", "ping-pong"},                       // 8 waves in two groups
-    {128, 128, 64, 64, 64, 2, "LM4", "lockstep"},                       // 4 waves of 64 x 64, two per CU
-};
-
-inline bool cfg_is_dtl(int c) { return c >= CFG_L; }
-// Configurations whose kernel can split the last round's K loop (8-wave lockstep
-// loops; the 4-wave tile has no registers left for the partial sums).
-inline bool cfg_can_split(int c) { return c >= CFG_L && c <= CFG_LM; }
-
-// Configurations with a persistent kernel, used when the tile grid is not split and
-// k spans a whole number of stage rings, at least two.
-inline bool cfg_can_persist(int c) { return c == CFG_L; }
 
 using LaunchFn = hipError_t (*)(const Args&, int grid, hipStream_t);
 
@@ -56,10 +20,11 @@ hipError_t launch_generic(const Args& a, int grid, hipStream_t s) {
   return hipLaunchKernel(fn, dim3(grid), dim3((BM / WM) * (BN / WN) * 64), params, 0, s);
 }
 
-// Main loop of a configuration: the lockstep loop's switches (interleaved reads,
-// spread copies, copies on half the waves) or the ping-pong loop.
-enum Loop { LOCKSTEP = 0, LOCKSTEP_ILV = 1, LOCKSTEP_SPREAD_ILV = 2, PINGPONG = 3, LOCKSTEP_HALF = 4,
-            LOCKSTEP_SPREAD_ILV_HALF = 5, PERSIST = 6 };
+// Main loop of a configuration: plain lockstep (every wave copies), lockstep with copies
+// on half the waves, or the persistent kernel (interleaved reads, copies on half the
+// waves; one workgroup per tile with the same loop where the persistent kernel does not
+// apply).
+enum Loop { LOCKSTEP = 0, LOCKSTEP_HALF = 1, PERSIST = 2 };
 
 // MFMAs of a k-tile's last step that the persistent loop issues before its barrier.
 constexpr int kPersistPre = 4;
@@ -70,27 +35,23 @@ hipError_t launch_dtl(const Args& a, int grid, hipStream_t s) {
   Args copy = a;
   void* params[] = {&copy};
   const void* fn;
-  constexpr bool SPREAD = LOOP == LOCKSTEP_SPREAD_ILV || LOOP == LOCKSTEP_SPREAD_ILV_HALF;
-  constexpr bool ILV = LOOP == LOCKSTEP_ILV || LOOP == PERSIST || SPREAD;
-  constexpr int CW = (LOOP == LOCKSTEP_HALF || LOOP == LOCKSTEP_SPREAD_ILV_HALF || LOOP == PERSIST)
-                         ? (BM / WM) * (BN / WN) / 2 : 0;
+  constexpr bool ILV = LOOP == PERSIST;
+  constexpr int CW = (LOOP == LOCKSTEP_HALF || LOOP == PERSIST) ? (BM / WM) * (BN / WN) / 2 : 0;
   if constexpr (LAY != 0) {
     static_assert(LOOP == LOCKSTEP || LOOP == LOCKSTEP_HALF || LOOP == PERSIST,
                   "transposed operands: plain lockstep loop or the persistent kernel");
-    fn = reinterpret_cast<const void*>(&gemm_dtl_kernel<DT, EP, BM, BN, WM, WN, BK, ST, false, false, CW, LAY>);
+    fn = reinterpret_cast<const void*>(&gemm_dtl_kernel<DT, EP, BM, BN, WM, WN, BK, ST, false, CW, LAY>);
     if constexpr (LOOP == PERSIST) {
       if (a.persist_grid > 0) {
         fn = reinterpret_cast<const void*>(&gemm_persist_kernel<DT, EP, BM, BN, WM, WN, BK, ST, CW, kPersistPre, LAY>);
         grid = a.persist_grid;
       }
     }
-  } else if constexpr (LOOP == PINGPONG) {
-    fn = reinterpret_cast<const void*>(&gemm_pp_kernel<DT, EP, BM, BN, WM, WN, BK, ST>);
   } else {
-    fn = reinterpret_cast<const void*>(&gemm_dtl_kernel<DT, EP, BM, BN, WM, WN, BK, ST, SPREAD, ILV, CW>);
+    fn = reinterpret_cast<const void*>(&gemm_dtl_kernel<DT, EP, BM, BN, WM, WN, BK, ST, ILV, CW>);
     if constexpr ((BM / WM) * (BN / WN) == 8) {   // the split tail exists for the 8-wave tiles
       if (a.dp_tiles < grid) {
-        fn = reinterpret_cast<const void*>(&gemm_sk_kernel<DT, EP, BM, BN, WM, WN, BK, ST, SPREAD, ILV, CW>);
+        fn = reinterpret_cast<const void*>(&gemm_sk_kernel<DT, EP, BM, BN, WM, WN, BK, ST, ILV, CW>);
         grid = a.dp_tiles + a.sk_wgs;
       }
     }
@@ -104,9 +65,6 @@ hipError_t launch_dtl(const Args& a, int grid, hipStream_t s) {
   return hipLaunchKernel(fn, dim3(grid), dim3((BM / WM) * (BN / WN) * 64), params, 0, s);
 }
 
-// Partial-accumulator bytes of one split workgroup of a configuration (one tile, fp32).
-inline size_t sk_slot_bytes(const TileCfg& c) { return (size_t)c.bm * c.bn * sizeof(float); }
-
 template <int DT, int EP>
 LaunchFn pick_cfg(int cfg) {
   switch (cfg) {
@@ -118,14 +76,7 @@ LaunchFn pick_cfg(int cfg) {
     switch (cfg) {
       case CFG_L: return &launch_dtl<DT, EP, 256, 256, 128, 64, 64, 2, PERSIST>;
       case CFG_LH: return &launch_dtl<DT, EP, 256, 256, 128, 64, 64, 2, LOCKSTEP_HALF>;
-      case CFG_LA: return &launch_dtl<DT, EP, 256, 256, 128, 64, 64, 2, LOCKSTEP>;
-      case CFG_LI: return &launch_dtl<DT, EP, 256, 256, 128, 64, 64, 2, LOCKSTEP_ILV>;
-      case CFG_LS: return &launch_dtl<DT, EP, 256, 256, 128, 64, 32, 4, LOCKSTEP_SPREAD_ILV>;
-      case CFG_LSH: return &launch_dtl<DT, EP, 256, 256, 128, 64, 32, 4, LOCKSTEP_SPREAD_ILV_HALF>;
       case CFG_LM: return &launch_dtl<DT, EP, 128, 128, 32, 64, 64, 2, LOCKSTEP>;
-      case CFG_W4: return &launch_dtl<DT, EP, 256, 256, 128, 128, 64, 2, LOCKSTEP>;
-      case CFG_W4S: return &launch_dtl<DT, EP, 256, 256, 128, 128, 32, 4, LOCKSTEP_SPREAD_ILV>;
-      case CFG_P: return &launch_dtl<DT, EP, 256, 256, 128, 64, 32, 4, PINGPONG>;
       case CFG_LM4: return &launch_dtl<DT, EP, 128, 128, 64, 64, 64, 2, LOCKSTEP>;
       default: break;
     }
@@ -147,11 +98,9 @@ LaunchFn pick(int ep, int cfg) {
 }
 
 // Operands stored transposed (LAY bit 0: A as (k,m), bit 1: B as (n,k)), 16-bit
-// types: the 256 x 256 tile persistent (L; one workgroup per tile when the k loop does
-// not suit the persistent kernel) or with copies on waves 0-3 (LH), or the 128 x 128
-// tile (LM).
-inline bool cfg_has_layouts(int c) { return c == CFG_L || c == CFG_LH || c == CFG_LM; }
-
+// types: the configurations cfg_has_layouts names (the 256 x 256 tile persistent, with
+// one workgroup per tile when the k loop does not suit the persistent kernel, or with
+// copies on waves 0-3; the 128 x 128 tile).
 template <int DT, int EP, int LAY>
 LaunchFn pick_cfg_t(int cfg) {
   switch (cfg) {

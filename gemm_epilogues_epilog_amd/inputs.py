@@ -172,3 +172,16 @@ def integer_case(m: int, n: int, k: int, dtype: str, seed: int = 0, vec: Optiona
     A2 = torch.randint(-2, 3, (m, k), generator=g).to(TORCH_DT[dtype])
     B2 = torch.randint(-2, 3, (k, n), generator=g).to(TORCH_DT[dtype])
     return A, B, bias, A2, B2
+
+
+def integer_tie_case(m: int, n: int, k: int, dtype: str, seed: int = 0, vec: Optional[str] = None):
+    """As integer_case, but with an integer bias in [-8, 8]: pre-activations are
+    integers, and a share of them is exactly 0 (the ReLU tie)."""
+    v = vec or dtype
+    g = torch.Generator().manual_seed(_mix(seed, 98, m * 131 + n * 17 + k))
+    A = torch.randint(-2, 3, (m, k), generator=g).to(TORCH_DT[dtype])
+    B = torch.randint(-2, 3, (k, n), generator=g).to(TORCH_DT[dtype])
+    bias = torch.randint(-8, 9, (m,), generator=g).to(torch.float32).to(TORCH_DT[v])
+    A2 = torch.randint(-2, 3, (m, k), generator=g).to(TORCH_DT[dtype])
+    B2 = torch.randint(-2, 3, (k, n), generator=g).to(TORCH_DT[dtype])
+    return A, B, bias, A2, B2

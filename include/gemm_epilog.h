@@ -113,7 +113,7 @@ typedef enum {
  *   out     : receives the handle; untouched on error.
  * Allocates the workspace on the current device: the per-tile bias-gradient
  * partial sums for DRELU_BGRAD, T1 and T2 for RELU_BIAS_UNFUSED, nothing otherwise.
- * Environment (tuning experiments): GE_TILE=S|M|L|LH|LA|LI|LS|LSH|LM|LM4|W4|W4S|P forces a tile configuration;
+ * Environment (tuning experiments): GE_TILE=S|M|L|LH|LM|LM4 forces a tile configuration;
  * GE_GROUP_M=g (1..1024) sets how many m-tiles share one group of the tile order;
  * GE_STREAMK=0 keeps a sparse last round of tiles whole instead of splitting its k loop;
  * GE_SK_RUN=r sets the k-tiles per split run (at least one run per compute unit);
@@ -196,6 +196,47 @@ ge_status_t gemm_epilog_execute(ge_handle_t h, const void* A, const void* B, con
  */
 ge_status_t gemm_epilog_autotune(ge_handle_t h, const void* A, const void* B, const void* bias, void* D, void* aux,
                                  void* bgrad, void* stream, int repeats, float* best_ms);
+
+/* What a plan decides, as reported by gemm_epilog_plan_info. */
+typedef struct {
+  int tile_m, tile_n, tile_k;  /* workgroup tile and k-tile (tile_k 0: register-staged kernel) */
+  int waves;                   /* waves per workgroup */
+  int64_t tiles;               /* output tiles */
+  int persistent_workgroups;   /* > 0: that many workgroups walk the tiles; 0: one per tile */
+  int whole_tiles;             /* tiles computed whole (== tiles unless the last round is split) */
+  int split_workgroups;        /* workgroups sharing the k loops of the remaining tiles */
+  int split_run_ktiles;        /* k-tiles per split workgroup */
+  int group_m;                 /* m-tiles per group of the tile order */
+  size_t workspace_bytes;      /* device workspace the plan allocates */
+} ge_plan_info_t;
+
+/*
+ * gemm_epilog_plan_info - the configuration gemm_epilog_plan_ex would choose for this
+ * problem on a gfx950 device with `compute_units` compute units, computed on the host
+ * with no HIP call and no allocation (no device needed). The plan step of [P2] (body:
+ * the costly choices are made once, when planning), exposed for inspection.
+ *   m .. op_b      : as for gemm_epilog_plan_ex, same rules and errors.
+ *   compute_units  : 1 .. 4096 (else GE_ERR_INVALID_VALUE); 256 on MI355X.
+ *   info           : receives the decisions (GE_ERR_NULL_POINTER if NULL).
+ * Honours the same environment switches as gemm_epilog_plan.
+ */
+ge_status_t gemm_epilog_plan_info(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt, ge_epilog_t ep, ge_op_t op_a,
+                                  ge_op_t op_b, int compute_units, ge_plan_info_t* info);
+
+/*
+ * gemm_epilog_lost_waits - how many split-tail waits of this plan's executes ran out
+ * since the plan was made or since the last call, and reset the count.
+ * A plan whose last round of tiles is split hands parts of a tile's k loop to other
+ * workgroups; the workgroup that finishes the tile waits, bounded (about a second),
+ * for their partial sums. A wait that runs out gives that tile NaN in D instead of
+ * hanging the device, and leaves the plan's flags clean for later executes. This call
+ * synchronises `stream` (hipStream_t, NULL = null stream), reads the count from the
+ * plan's workspace and clears it; a plan without a split tail reports 0 at once.
+ *   h     : the plan (GE_ERR_NULL_POINTER if NULL).
+ *   count : receives the count (GE_ERR_NULL_POINTER if NULL).
+ * GE_ERR_HIP if a copy or the synchronisation fails. Must not overlap an execute of h.
+ */
+ge_status_t gemm_epilog_lost_waits(ge_handle_t h, void* stream, uint32_t* count);
 
 /* gemm_epilog_free - release a plan and its workspace. NULL is accepted (GE_OK).
  * Must not be called while an execute on this plan may still be running. */

@@ -172,3 +172,35 @@ def test_random_parity_layouts_persistent(gpu, dt, lay):
     o = oracle.gemm_epilog(a, b, "RELU_AUX_BIAS", bias=c, ab=dt, want_pre=True, **kw)
     assert_close(g["D"], o["D"], dt, g["desc"])
     assert_mask(g["mask"], o["mask"], o["pre"], m)
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("lay", list(LAYOUTS))
+def test_persistent_transposed_many_tiles_integer_exact(gpu, dt, lay):
+    """The persistent kernel with operands stored transposed walks several tiles per
+    workgroup: 528 tiles of a ragged 4000 x 8200 output on 256 workgroups, so every tile
+    after a workgroup's first starts from operands its copy plan fetched during the
+    previous tile (the retargeted k-major and mn-major copies, with their row and column
+    limits on the ragged tiles). Integer inputs make every epilogue bit-exact."""
+    ta, tb = LAYOUTS[lay]
+    m, n, k = 4000, 8200, 256
+    print(f"[case] persistent transposed integer {dt} {lay} m={m} n={n} k={k}", flush=True)
+    A, B, bias, A2, B2 = inputs.integer_case(m, n, k, dt)
+    As, Bs = stored(A, ta), stored(B, tb)
+    a, b, c = to_np(A), to_np(B), to_np(bias)   # the oracle on the product's own orientation
+    kw = dict(trans_a=ta, trans_b=tb)
+    for ep in ("NONE", "BIAS", "RELU_BIAS"):
+        g = R.run(gpu, ep, dt, As, Bs, bias, tile="L", **kw)
+        assert "persistent workgroups" in g["desc"] and "grid 528" in g["desc"], g["desc"]
+        o = oracle.gemm_epilog(a, b, ep, bias=c, ab=dt)
+        assert np.array_equal(g["D"].view(np.uint8), o["D"].view(np.uint8)), f"{ep} {g['desc']}"
+    g = R.run(gpu, "RELU_AUX_BIAS", dt, As, Bs, bias, tile="L", **kw)
+    o = oracle.gemm_epilog(a, b, "RELU_AUX_BIAS", bias=c, ab=dt)
+    assert np.array_equal(g["D"].view(np.uint8), o["D"].view(np.uint8)), g["desc"]
+    assert np.array_equal(g["mask"].view(np.uint32), o["mask"]), g["desc"]
+    mask = torch.from_numpy(o["mask"].view(np.int32).copy())
+    gb = R.run(gpu, "DRELU_BGRAD", dt, stored(A2, ta), stored(B2, tb), mask=mask, tile="L", **kw)
+    assert "persistent workgroups" in gb["desc"], gb["desc"]
+    ob = oracle.gemm_epilog(to_np(A2), to_np(B2), "DRELU_BGRAD", mask=o["mask"], ab=dt)
+    assert np.array_equal(gb["D"].view(np.uint8), ob["D"].view(np.uint8)), gb["desc"]
+    assert np.array_equal(gb["bgrad"].view(np.uint8), ob["bgrad"].view(np.uint8)), gb["desc"]

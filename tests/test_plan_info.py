@@ -1,0 +1,91 @@
+"""The plan's decisions on the host, through gemm_epilog_plan_info (no HIP call): the
+measured tile rule, where the persistent kernel and the split tail apply, the tile order
+groups, and the workspace. CPU tests; one GPU test checks that a real plan agrees."""
+import pytest
+
+import gemm_epilogues_epilog_amd as ge
+
+F16 = ("f16", "f16", "f16")
+
+
+def info(m, n, k, lay="NN", ep="RELU_BIAS", dts=F16, cus=256):
+    return ge.gemm_epilog_plan_info(m, n, k, dts, ep, int(lay[0] == "T"), int(lay[1] == "T"), compute_units=cus)
+
+
+@pytest.mark.parametrize("shape,lay,tile,waves,split", [
+    ((4096, 11008, 4096), "NN", 256, 8, False),   # the 7B FFN layer: 688 tiles, last round 69% full, not split
+    ((4096, 2752, 4096), "NN", 256, 8, False),    # 176 tiles of 256 x 256: one partly filled round
+    ((4096, 3200, 4096), "NN", 256, 8, False),
+    ((8192, 1024, 8192), "NN", 256, 8, True),     # 128 tiles, 128 k-tiles: split k loop
+    ((2048, 1024, 16384), "NN", 256, 8, True),
+    ((4096, 1376, 4096), "NN", 128, 4, False),    # 352 tiles of 128 x 128: one round at two per CU
+    ((3072, 2560, 4096), "NN", 128, 4, False),
+    ((1024, 512, 2048), "NN", 128, 8, True),
+    ((2048, 2048, 2048), "NN", 128, 8, False),    # 32 k-tiles, one round: eight waves
+    ((4096, 2048, 2048), "NN", 128, 4, False),    # 32 k-tiles but two workgroups per CU
+    ((1536, 2048, 4096), "NN", 128, 8, False),    # 192 tiles, fewer than the CUs: eight waves
+    ((8192, 1024, 8192), "TN", 128, 8, False),    # transposed operands never split
+    ((4096, 2752, 4096), "TN", 256, 8, False),
+])
+def test_tile_rule(shape, lay, tile, waves, split):
+    r = info(*shape, lay=lay)
+    assert (r["tile_m"], r["tile_n"], r["waves"]) == (tile, tile, waves), r
+    assert (r["split_workgroups"] > 0) == split, r
+
+
+@pytest.mark.parametrize("shape,persistent", [
+    ((4096, 11008, 4096), 256), ((4096, 11008, 4160), 0), ((4096, 11008, 4040), 0),
+    ((4096, 11008, 128), 0), ((4352, 4096, 1024), 0), ((4096, 4096, 256), 256),
+])
+def test_persistent_conditions(shape, persistent, monkeypatch):
+    # the persistent kernel runs only when k is a multiple of 64 spanning an even number
+    # (at least 4) of k-tiles and the tile grid is not split
+    monkeypatch.setenv("GE_TILE", "L")
+    assert info(*shape)["persistent_workgroups"] == persistent
+
+
+def test_group_of_m_tiles_follows_the_size_of_A():
+    assert info(4096, 11008, 4096)["group_m"] == 8
+    assert info(65536, 8192, 16384)["group_m"] == 4   # A of 2 GiB outgrows the 256 MB MALL
+
+
+def test_workspace():
+    assert info(4096, 11008, 4096)["workspace_bytes"] == 0
+    # DRELU_BGRAD: one fp32 row sum per row and 64-column wave tile
+    assert info(8192, 8192, 8192, ep="DRELU_BGRAD", dts=("bf16", "bf16", "bf16"))["workspace_bytes"] == 128 * 8192 * 4
+    # the unfused chain: T1 and T2 in D's type
+    assert info(4096, 11008, 4096, ep="RELU_BIAS_UNFUSED")["workspace_bytes"] == 2 * 4096 * 11008 * 2
+    # the split tail: the flag region, then one fp32 256 x 256 tile per split workgroup
+    r = info(4352, 4096, 1024)
+    assert r["split_workgroups"] == 64 and r["workspace_bytes"] == 4096 + 64 * 256 * 256 * 4
+
+
+def test_errors_and_device_size():
+    st, _ = ge.gemm_epilog_plan_info(8, 12, 8, F16, "RELU_BIAS", check=False)
+    assert st == 2
+    st, _ = ge.gemm_epilog_plan_info(8, 8, 8, F16, "RELU_BIAS", compute_units=0, check=False)
+    assert st == 1
+    # a smaller device: the 7B FFN grid is several full rounds on 80 compute units
+    r = info(4096, 11008, 4096, cus=80)
+    assert r["persistent_workgroups"] == 80 and r["split_workgroups"] == 0
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("shape,lay,ep", [
+    ((4096, 11008, 4096), "NN", "RELU_BIAS"), ((1024, 512, 2048), "NN", "RELU_BIAS"),
+    ((8192, 1024, 8192), "NN", "DRELU_BGRAD"), ((4096, 1376, 4096), "NN", "RELU_AUX_BIAS"),
+    ((8192, 1024, 8192), "TN", "DRELU_BGRAD"), ((4096, 11008, 4096), "NN", "RELU_BIAS_UNFUSED"),
+])
+def test_plan_agrees_with_plan_info(gpu, shape, lay, ep):
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    r = info(*shape, lay=lay, ep=ep, cus=cus)
+    h = gpu.gemm_epilog_plan_ex(*shape, F16, ep, int(lay[0] == "T"), int(lay[1] == "T"))
+    try:
+        d = gpu.gemm_epilog_describe(h)
+        assert f"tile {r['tile_m']}x{r['tile_n']}" in d and f"grid {r['tiles']}" in d, (d, r)
+        assert ("persistent workgroups" in d) == (r["persistent_workgroups"] > 0), (d, r)
+        assert ("split over" in d) == (r["split_workgroups"] > 0), (d, r)
+        assert gpu.gemm_epilog_workspace_bytes(h) == r["workspace_bytes"]
+    finally:
+        gpu.gemm_epilog_free(h)

@@ -2,30 +2,52 @@
 
 The plan gives the last, partly empty round of T tiles on P compute units
 (T % P tiles) to runs of sk_units k-tiles, one workgroup per run, which computes its
-partial piece (if any) before its owner piece (if any). This model restates the
-plan's choice and the kernel's piece arithmetic and checks the invariants the kernel
-relies on: every (tile, k-tile) is computed exactly once, each tile has exactly one
-owner piece starting at k = 0, each run publishes at most one partial (which never
-starts at k = 0), and the runs an owner waits for are exactly the runs that hold the
-rest of its tile, each of which publishes before it waits for anything. Every
-published flag has exactly one owner that waits for it, which is what lets that owner
-clear it afterwards. The run length may also be forced (GE_SK_RUN), never below one
-run per compute unit, so every split workgroup is resident at once."""
+partial piece (if any) before its owner piece (if any). The plan's numbers (whole
+tiles, run length, split workgroups) come from the library's own host plan unit
+through gemm_epilog_plan_info (no HIP call). This file models the kernel's piece
+arithmetic independently and checks the invariants the kernel relies on: every
+(tile, k-tile) is computed exactly once, each tile has exactly one owner piece
+starting at k = 0, each run publishes at most one partial (which never starts at
+k = 0), and the runs an owner waits for are exactly the runs that hold the rest of
+its tile, each of which publishes before it waits for anything. Every published flag
+has exactly one owner that waits for it, which is what lets that owner clear it
+afterwards. The run length may also be forced (GE_SK_RUN), never below one run per
+compute unit, so every split workgroup is resident at once. The kernel's own run
+arithmetic (gek::sk_run) is checked against the same invariants under the sanitizers
+(tests/test_plan_sanitize.py)."""
+import os
+
 import pytest
+
+import gemm_epilogues_epilog_amd as ge
 
 
 def plan(tiles, kt, cus=256, run=None, slots=None):
-    """slots: workgroups per round (2 cus for the 128 x 128 tile, two per CU)."""
-    rem = tiles % (slots or cus)
-    if not (rem != 0 and rem * 2 <= cus and kt >= 2):
+    """The library's split of `tiles` output tiles of k-tiles `kt`: (whole tiles, run
+    length, split workgroups), or None when the plan does not split. slots = 2 cus
+    asks for the 128 x 128 tile (two workgroups per CU), else the 256 x 256 tile."""
+    lm = slots is not None and slots == 2 * cus
+    bm = 128 if lm else 256
+    saved = {k: os.environ.get(k) for k in ("GE_TILE", "GE_SK_RUN", "GE_STREAMK")}
+    os.environ["GE_TILE"] = "LM" if lm else "LH"
+    os.environ.pop("GE_STREAMK", None)
+    if run is not None:
+        os.environ["GE_SK_RUN"] = str(run)
+    else:
+        os.environ.pop("GE_SK_RUN", None)
+    try:
+        info = ge.gemm_epilog_plan_info(bm * tiles, bm, 64 * kt, ("f16", "f16", "f16"), "RELU_BIAS",
+                                        compute_units=cus)
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    assert info["tiles"] == tiles and info["tile_m"] == bm
+    if info["split_workgroups"] == 0:
         return None
-    units = rem * kt
-    per = max(-(-units // cus), -(-kt // 4))
-    if run is not None and run >= 1:
-        per = max(run, -(-units // cus))
-    if per >= kt:
-        return None
-    return tiles - rem, per, -(-units // per)
+    return info["whole_tiles"], info["split_run_ktiles"], info["split_workgroups"]
 
 
 def xcd_remap(i, g):
