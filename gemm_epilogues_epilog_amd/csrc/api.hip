@@ -323,7 +323,7 @@ ge_status_t gemm_epilog_lost_waits(ge_handle_t h, void* stream, uint32_t* count)
   *count = 0;
   if (h->L.sk_wgs == 0) return GE_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  uint32_t* word = reinterpret_cast<uint32_t*>(static_cast<char*>(h->ws) + h->L.off_sk_flag) + h->L.sk_wgs;
+  uint32_t* word = reinterpret_cast<uint32_t*>(static_cast<char*>(h->ws) + h->L.off_sk_flag) + gek::kSkLostWord;
   uint32_t v = 0;
   if (hipMemcpyAsync(&v, word, sizeof(v), hipMemcpyDeviceToHost, s) != hipSuccess ||
       hipMemsetAsync(word, 0, sizeof(v), s) != hipSuccess || hipStreamSynchronize(s) != hipSuccess)

@@ -1150,7 +1150,7 @@ constexpr int kDeviceScope = 16;   // cache-policy bit sc1 of a buffer instructi
 // the partial swaps 0 -> epoch once its stores have completed. The owner waits (a
 // bounded spin, p.sk_spin_limit polls, about a second by default) for the epoch, adds
 // the partial and swaps epoch -> 0. If the wait runs out, the owner swaps 0 -> kSkAbort
-// (unless the epoch arrived meanwhile), counts the loss in p.sk_flag[p.sk_wgs] and gives
+// (unless the epoch arrived meanwhile), counts the loss in p.sk_flag[kSkLostWord], gives
 // the tile's D NaN; the publisher that finds kSkAbort resets the flag to 0 instead of
 // publishing. So every flag is 0 again when the kernel ends, lost wait or not, and a
 // later execute with the same epoch (a replay of a captured graph) never finds a stale
@@ -1238,7 +1238,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_sk_kernel(
     if (threadIdx.x == 0) {
       uint32_t lost = 0u;
       for (int o = r + 1; o <= run.last; ++o) lost += sk_wait_flag(p.sk_flag + o, p.epoch, p.sk_spin_limit) ? 0u : 1u;
-      if (lost) __hip_atomic_fetch_add(p.sk_flag + p.sk_wgs, lost, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (lost) __hip_atomic_fetch_add(p.sk_flag + kSkLostWord, lost, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       lost_any = lost;
     }
     wait_lgkmcnt<0>();

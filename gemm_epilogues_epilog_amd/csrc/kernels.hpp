@@ -71,8 +71,8 @@ struct Args {
   int32_t sk_wgs;     // split workgroups
   uint32_t epoch;     // changes every execute; marks this execute's partials
   float* sk_partial;  // per split workgroup: one tile of fp32 partial accumulators
-  uint32_t* sk_flag;  // per split workgroup: epoch of its published partial; then the
-                      // count of owner waits that ran out
+  uint32_t* sk_flag;  // per split workgroup: epoch of its published partial (and the
+                      // count of owner waits that ran out at word kSkLostWord)
   uint32_t sk_spin_limit;   // polls of an owner's bounded wait for a partial
   // Persistent kernels: workgroups launched (one per compute unit), each walking the
   // tile order with that stride; 0 when the plan launches one workgroup per tile.

@@ -14,6 +14,8 @@
 
 #include "tiles.hpp"
 
+static_assert(geh::kSkFlagRegion == gek::kSkFlagWords * sizeof(uint32_t), "flag region");
+
 namespace geh {
 
 namespace {
@@ -171,7 +173,7 @@ ge_status_t make_layout(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt, ge_epil
       }
       // a run of k-tiles holds at most one tile start when per < kt; every split
       // workgroup's flag fits the fixed flag region
-      if (per < kt && cdiv(units, per) < (int64_t)(kSkFlagRegion / sizeof(uint32_t))) {
+      if (per < kt && cdiv(units, per) < (int64_t)gek::kSkLostWord) {
         L.dp_tiles = (int)(tiles - rem);
         L.sk_units = (int)per;
         L.sk_wgs = (int)cdiv(units, per);
@@ -186,9 +188,10 @@ ge_status_t make_layout(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt, ge_epil
   }
 
   // ---- workspace: [split flags][DRELU_BGRAD row sums | unfused T1, T2][split partials] ----
-  // The flags (one word per split workgroup, then the count of owner waits that ran
-  // out) come first, in a region of fixed size, so their place does not move with the
-  // problem: a workspace reused across problems keeps them at 0 between executes.
+  // The flags (one word per split workgroup, and the count of owner waits that ran out
+  // in the region's last word) come first, in a region of fixed size, so their place
+  // does not move with the problem: a workspace reused across problems keeps them at 0
+  // between executes.
   const size_t es = elem_size(dt.d);
   L.sk_flag_bytes = L.sk_wgs ? kSkFlagRegion : 0;
   L.off_sk_flag = 0;

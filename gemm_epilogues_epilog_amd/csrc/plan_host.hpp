@@ -14,8 +14,8 @@
 
 namespace geh {
 
-// Bytes of the split tail's flag region at the start of a workspace: one word per split
-// workgroup (fewer than 1024) and the count of owner waits that ran out.
+// Bytes of the split tail's flag region at the start of a workspace (gek::kSkFlagWords
+// words: the flags, then the count of owner waits that ran out in the last word).
 constexpr size_t kSkFlagRegion = 4096;
 
 // Everything a plan decides before it touches a device.

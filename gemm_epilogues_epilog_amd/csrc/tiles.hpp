@@ -41,6 +41,13 @@ constexpr bool cfg_can_persist(int c) { return c == CFG_L; }
 // tile (LM).
 constexpr bool cfg_has_layouts(int c) { return c == CFG_L || c == CFG_LH || c == CFG_LM; }
 
+// The split tail's flag words at the start of a workspace: one per split workgroup
+// (fewer than kSkFlagWords - 1) and, in the last word, the count of owner waits that
+// ran out. Both sit at fixed places, so a workspace reused by problems of different
+// layouts never finds a count where a flag belongs.
+constexpr int kSkFlagWords = 1024;
+constexpr int kSkLostWord = kSkFlagWords - 1;
+
 // Partial-accumulator bytes of one split workgroup of a configuration (one tile, fp32).
 constexpr size_t sk_slot_bytes(const TileCfg& c) { return (size_t)c.bm * c.bn * sizeof(float); }
 

@@ -170,8 +170,8 @@ void check_layout(long long m, long long n, long long k, ge_dtype_t t, ge_epilog
                 "regions disjoint", m, n, k, cfg);
       }
       if (L.sk_wgs) {
-        check(L.off_sk_flag == 0 && L.sk_flag_bytes == geh::kSkFlagRegion && (size_t)(L.sk_wgs + 1) * 4 <= L.sk_flag_bytes,
-              "flag region first and large enough", m, n, k, cfg);
+        check(L.off_sk_flag == 0 && L.sk_flag_bytes == geh::kSkFlagRegion && L.sk_wgs < gek::kSkLostWord,
+              "flag region first; flags clear of the lost-wait count", m, n, k, cfg);
         check_split(L, (int)((k + tc.bk - 1) / tc.bk), cus, m, n, k);
       }
       const std::string d = geh::describe(dt, ep, L);
