@@ -6,7 +6,7 @@ fallback; if the library is missing every call raises.
 
 Low-level functions carry the names of the C ABI in include/gemm_epilog.h:
 gemm_epilog_plan, gemm_epilog_plan_ex, gemm_epilog_plan_info, gemm_epilog_execute,
-gemm_epilog_autotune, gemm_epilog_lost_waits,
+gemm_epilog_execute_noalloc, gemm_epilog_autotune, gemm_epilog_lost_waits,
 gemm_epilog_free, gemm_epilog_aux_bytes, gemm_epilog_workspace_bytes,
 gemm_epilog_describe, gemm_epilog_status_string.
 Pointers may be given as torch tensors (device memory), integers or None.
@@ -32,8 +32,10 @@ DTYPES = {"f32": F32, "f16": F16, "bf16": BF16}
 EPILOG = {"NONE": 0, "RELU_BIAS": 1, "GELU_BIAS": 2, "RELU_AUX_BIAS": 3, "DRELU_BGRAD": 4, "BIAS": 5,
           "RELU_BIAS_UNFUSED": 100}
 STATUS = {0: "GE_OK", 1: "GE_ERR_INVALID_VALUE", 2: "GE_ERR_NOT_SUPPORTED", 3: "GE_ERR_NULL_POINTER",
-          4: "GE_ERR_MISALIGNED", 5: "GE_ERR_ALLOC", 6: "GE_ERR_HIP"}
+          4: "GE_ERR_MISALIGNED", 5: "GE_ERR_ALLOC", 6: "GE_ERR_HIP", 7: "GE_ERR_SCRATCH"}
+NOALLOC_SCRATCH_BYTES = 64 << 20
 EXPORTS = ("gemm_epilog_plan", "gemm_epilog_plan_ex", "gemm_epilog_plan_info", "gemm_epilog_execute",
+           "gemm_epilog_execute_noalloc",
            "gemm_epilog_autotune", "gemm_epilog_mfma_probe", "gemm_epilog_lost_waits", "gemm_epilog_free",
            "gemm_epilog_aux_bytes", "gemm_epilog_workspace_bytes", "gemm_epilog_describe",
            "gemm_epilog_status_string")
@@ -79,6 +81,9 @@ def load() -> ctypes.CDLL:
     L.gemm_epilog_plan_info.restype = c_int
     L.gemm_epilog_execute.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
     L.gemm_epilog_execute.restype = c_int
+    L.gemm_epilog_execute_noalloc.argtypes = [i64, i64, i64, ge_dtypes_t, c_int, c_int, c_int,
+                                              vp, vp, vp, vp, vp, vp, vp]
+    L.gemm_epilog_execute_noalloc.restype = c_int
     L.gemm_epilog_autotune.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, c_int, ctypes.POINTER(ctypes.c_float)]
     L.gemm_epilog_autotune.restype = c_int
     L.gemm_epilog_mfma_probe.argtypes = [vp, ctypes.c_size_t, c_int, c_int, c_int, vp, vp]
@@ -179,6 +184,25 @@ def gemm_epilog_execute(handle, A, B, bias=None, D=None, aux=None, bgrad=None, s
     st = load().gemm_epilog_execute(handle, _ptr(A), _ptr(B), _ptr(bias), _ptr(D), _ptr(aux), _ptr(bgrad), stream)
     if check and st != 0:
         raise GemmEpilogError(st, "gemm_epilog_execute")
+    return st
+
+
+def gemm_epilog_execute_noalloc(m: int, n: int, k: int, dtypes, epilog, A, B, bias=None, D=None, aux=None,
+                                bgrad=None, op_a: int = OP_N, op_b: int = OP_N, stream=None, check: bool = True):
+    """Plan and enqueue in one call that allocates nothing: the workspace is the library's
+    static per-device scratch (NOALLOC_SCRATCH_BYTES). Calls that overlap on one device
+    race. Returns the status (raises unless check=False)."""
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream().cuda_stream
+    elif not isinstance(stream, int):
+        stream = stream.cuda_stream
+    ab, d, vec = (_dt(x) for x in dtypes)
+    st = load().gemm_epilog_execute_noalloc(int(m), int(n), int(k), ge_dtypes_t(ab, d, vec), _ep(epilog), int(op_a),
+                                            int(op_b), _ptr(A), _ptr(B), _ptr(bias), _ptr(D), _ptr(aux), _ptr(bgrad),
+                                            stream)
+    if check and st != 0:
+        raise GemmEpilogError(st, "gemm_epilog_execute_noalloc")
     return st
 
 

@@ -11,6 +11,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -181,7 +182,32 @@ ge_status_t query_device(int* dev, int* cus) {
   return GE_OK;
 }
 
+// ---- the static scratch of gemm_epilog_execute_noalloc ----
+// Each device that runs this code object holds its own copy of `scratch`. In host code
+// the name stands for the host-side shadow of the variable, not for device memory:
+// only the address that hipGetSymbolAddress returns, per device, is used.
+constexpr size_t kScratchBytes = GEMM_EPILOG_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+struct ScratchState {
+  std::mutex mu;
+  void* ptr[kMaxDevices] = {};       // device address of `scratch` per device
+  int cus[kMaxDevices] = {};         // compute units per device (0: not yet queried)
+  uint32_t epoch[kMaxDevices] = {};  // execute counter per device
+};
+ScratchState g_scratch;
+
 }  // namespace
+
+namespace gek {
+// Zeroes n words (the split tail's flags in the static scratch); a kernel rather than a
+// memset, so that it may also sit in a captured graph.
+__global__ void clear_words_kernel(uint32_t* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+}  // namespace gek
 
 extern "C" {
 
@@ -194,6 +220,9 @@ const char* gemm_epilog_status_string(ge_status_t s) {
     case GE_ERR_MISALIGNED: return "GE_ERR_MISALIGNED: a pointer violates its alignment rule";
     case GE_ERR_ALLOC: return "GE_ERR_ALLOC: allocation failed";
     case GE_ERR_HIP: return "GE_ERR_HIP: a HIP runtime call failed";
+    case GE_ERR_SCRATCH:
+      return "GE_ERR_SCRATCH: the problem needs more workspace than the 64 MiB static scratch of "
+             "gemm_epilog_execute_noalloc";
   }
   return "unknown status";
 }
@@ -316,6 +345,77 @@ ge_status_t gemm_epilog_autotune(ge_handle_t h, const void* A, const void* B, co
   }
   if (best_ms) *best_ms = best / (float)repeats;
   return GE_OK;
+}
+
+ge_status_t gemm_epilog_execute_noalloc(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt, ge_epilog_t ep,
+                                        ge_op_t op_a, ge_op_t op_b, const void* A, const void* B, const void* bias,
+                                        void* D, void* aux, void* bgrad, void* stream) {
+  // host-only validation first, as for plan_ex and execute
+  int lay = 0;
+  if (ge_status_t st = geh::check_plan_args(m, n, k, dt, ep, op_a, op_b, &lay); st != GE_OK) return st;
+  if (ge_status_t st = geh::check_execute_args(ep, dt, A, B, bias, D, aux, bgrad); st != GE_OK) return st;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return GE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return GE_ERR_NOT_SUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  // once per device: the device's address of the scratch, its compute units, and its
+  // flag words cleared on this stream (ahead of this call's kernels)
+  char* ws = nullptr;
+  int cus = 0;
+  uint32_t epoch = 0;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch.mu);
+    if (!g_scratch.ptr[dev]) {
+      int c = 0;
+      if (ge_status_t st = query_device(&dev, &c); st != GE_OK) return st;
+      void* p = nullptr;
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return GE_ERR_HIP;
+      uint32_t* words = static_cast<uint32_t*>(p);
+      int nw = gek::kSkFlagWords;
+      void* params[] = {&words, &nw};
+      if (hipLaunchKernel(reinterpret_cast<const void*>(&gek::clear_words_kernel), dim3(gek::kSkFlagWords / 256),
+                          dim3(256), params, 0, s) != hipSuccess)
+        return GE_ERR_HIP;
+      g_scratch.ptr[dev] = p;
+      g_scratch.cus[dev] = c;
+    }
+    ws = static_cast<char*>(g_scratch.ptr[dev]);
+    cus = g_scratch.cus[dev];
+    g_scratch.epoch[dev] = g_scratch.epoch[dev] % 0x7fffffffu + 1u;
+    epoch = g_scratch.epoch[dev];
+  }
+
+  // the plan, on the stack: the table's configuration; without the split tail when its
+  // partials do not fit the scratch
+  const int cfg = geh::choose_cfg(m, n, k, dt.ab, cus, lay);
+  const bool persist = !geh::env_off("GE_PERSIST");
+  geh::Layout L;
+  if (ge_status_t st = geh::make_layout(m, n, k, dt, ep, lay, cus, cfg, !geh::env_off("GE_STREAMK"), persist, &L);
+      st != GE_OK)
+    return st;
+  if (L.ws_bytes > kScratchBytes &&
+      geh::make_layout(m, n, k, dt, ep, lay, cus, cfg, false, persist, &L) != GE_OK)
+    return GE_ERR_NOT_SUPPORTED;
+  if (L.ws_bytes > kScratchBytes) return GE_ERR_SCRATCH;
+  ge_plan h;
+  h.m = m;
+  h.n = (int)n;
+  h.k = (int)k;
+  h.dt = dt;
+  h.ep = ep;
+  h.device = dev;
+  h.cus = cus;
+  h.L = L;
+  h.gemm = lookup(dt.ab, ep == GE_EPILOG_RELU_BIAS_UNFUSED ? (int)gek::NONE : (int)ep, cfg, lay);
+  if (!h.gemm) return GE_ERR_NOT_SUPPORTED;
+  h.ws = ws;
+  h.spin_limit = kSkSpinDefault;
+  if (const char* e = std::getenv("GE_SK_SPIN")) {
+    const long v = std::atol(e);
+    if (v >= 0 && v <= (long)kSkSpinDefault) h.spin_limit = (uint32_t)v;
+  }
+  return enqueue(h, ws, epoch, A, B, bias, D, aux, bgrad, s);
 }
 
 ge_status_t gemm_epilog_lost_waits(ge_handle_t h, void* stream, uint32_t* count) {

@@ -100,7 +100,9 @@ typedef enum {
   GE_ERR_NULL_POINTER = 3,  /* a pointer the epilogue needs is NULL */
   GE_ERR_MISALIGNED = 4,    /* a pointer violates its alignment rule */
   GE_ERR_ALLOC = 5,         /* host or device allocation failed in plan */
-  GE_ERR_HIP = 6            /* a HIP runtime call failed (launch, device query) */
+  GE_ERR_HIP = 6,           /* a HIP runtime call failed (launch, device query) */
+  GE_ERR_SCRATCH = 7        /* gemm_epilog_execute_noalloc: the problem needs more workspace
+                               than the static scratch holds */
 } ge_status_t;
 
 /*
@@ -237,6 +239,35 @@ ge_status_t gemm_epilog_plan_info(int64_t m, int64_t n, int64_t k, ge_dtypes_t d
  * GE_ERR_HIP if a copy or the synchronisation fails. Must not overlap an execute of h.
  */
 ge_status_t gemm_epilog_lost_waits(ge_handle_t h, void* stream, uint32_t* count);
+
+/* Bytes of the static device scratch that gemm_epilog_execute_noalloc works in. */
+#define GEMM_EPILOG_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * gemm_epilog_execute_noalloc - gemm_epilog_plan_ex and gemm_epilog_execute in one call
+ * that allocates nothing: for callers that cannot allocate device memory, such as code
+ * under HIP graph capture, tight serving loops and harnesses that forbid hipMalloc.
+ * The plan's decisions are made on the host (as gemm_epilog_plan_info reports them) and
+ * the kernels of gemm_epilog_execute run with their workspace (bias-gradient partial
+ * sums, the unfused chain's T1 and T2, the split tail's partials and flags) in a static
+ * device array of GEMM_EPILOG_NOALLOC_SCRATCH_BYTES (64 MiB) per device, which each GPU
+ * the library runs on holds until the process ends. No hipMalloc, hipFree or other
+ * allocating call is made; the first call on a device takes the array's address once
+ * (hipGetSymbolAddress) and clears its flag words with a kernel on `stream`.
+ *   m .. op_b : as for gemm_epilog_plan_ex, same rules and errors.
+ *   A .. stream : as for gemm_epilog_execute, same rules and errors.
+ * Returns GE_ERR_SCRATCH when the workspace does not fit the scratch even without the
+ * split tail (e.g. DRELU_BGRAD with ceil(n/64) * m * 4 bytes of partial sums above
+ * 64 MiB, or the unfused chain with 2 m n element bytes above it); nothing is launched
+ * then. A split tail that does not fit is left out (the tiles run whole).
+ * Every call on a device shares that device's array, and the array keeps the last
+ * call's contents: calls that overlap on one device (two streams, two threads) race and
+ * give wrong results; calls on one stream are ordered and safe. A split-tail wait that
+ * runs out gives its tile NaN in D, as for gemm_epilog_execute.
+ */
+ge_status_t gemm_epilog_execute_noalloc(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt, ge_epilog_t ep,
+                                        ge_op_t op_a, ge_op_t op_b, const void* A, const void* B, const void* bias,
+                                        void* D, void* aux, void* bgrad, void* stream);
 
 /* gemm_epilog_free - release a plan and its workspace. NULL is accepted (GE_OK).
  * Must not be called while an execute on this plan may still be running. */
