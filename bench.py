@@ -33,6 +33,8 @@ COPY_PROBE_BYTES = 1 << 30
 # inputs drawn on the device[, operand storage "TN" | "NT": A passed as its (k, m)
 # transpose | B passed as its (n, k) transpose]). None stands for the headline workload.
 VARIANTS = {
+    # the headline kernel timed like every variant, beside its unfused chain
+    "ffn_relu_bias_f16": (None, "RELU_BIAS", "f16", False),
     "ffn_unfused_f16": (None, "RELU_BIAS_UNFUSED", "f16", False),
     "ffn_aux_f16": (None, "RELU_AUX_BIAS", "f16", False),
     # the same product with the identity epilogue and with no epilogue: what bias + ReLU
@@ -61,7 +63,8 @@ VARIANTS = {
 LAYOUTS = {"NN": (False, False), "TN": (True, False), "NT": (False, True)}
 # The HBM-bound rows timed cold as well: each execute follows a 1 GiB scratch write, which
 # evicts the 256 MB MALL and the L2s, so the operands come from HBM.
-COLD_VARIANTS = {"small_relu_bias_f16_cold": "small_relu_bias_f16", "ffn_unfused_f16_cold": "ffn_unfused_f16"}
+COLD_VARIANTS = {"small_relu_bias_f16_cold": "small_relu_bias_f16", "ffn_unfused_f16_cold": "ffn_unfused_f16",
+                 "mlp8192_bwd_drelu_bgrad_bf16_cold": "mlp8192_bwd_drelu_bgrad_bf16"}
 FLUSH_BYTES = 1 << 30
 
 
@@ -137,12 +140,19 @@ def device_inputs(W, device_rng: bool):
     return A, B, bias
 
 
-def time_execute(ge, handle, args, steps, warmup, warm_s=0.0):
+WARM_S = 0.5          # every timing starts after at least this much untimed work: the clock settles
+VARIANT_STEPS = 50    # timed executes per variant (after VARIANT_WARMUP and WARM_S of warm-up)
+VARIANT_WARMUP = 10
+HEADLINE_EVENTS = 200  # event-timed executes of the headline kernel (roofline.achieved)
+
+
+def time_execute(ge, handle, args, steps, warmup, warm_s=WARM_S, event_steps=None):
     """Warm up (`warmup` executes, continued until `warm_s` seconds have passed), then
-    time `steps` executes twice: back to back under the host wall clock, bracketed by
-    synchronisations (the throughput), and with one HIP event pair per execute on the
-    launch stream (the kernel durations; the event packets themselves add gaps between
-    the kernels, so this pass does not give the throughput)."""
+    time `steps` executes back to back under the host wall clock, bracketed by
+    synchronisations (the throughput), and then `event_steps` (default `steps`) executes
+    with one HIP event pair each on the launch stream (the kernel durations; the event
+    packets themselves add gaps between the kernels, so this pass does not give the
+    throughput)."""
     import torch
     stream = torch.cuda.current_stream()
     sptr = stream.cuda_stream
@@ -159,7 +169,8 @@ def time_execute(ge, handle, args, steps, warmup, warm_s=0.0):
         ge.gemm_epilog_execute(handle, *args, stream=sptr)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(event_steps or steps)]
     for e0, e1 in ev:
         e0.record(stream)
         ge.gemm_epilog_execute(handle, *args, stream=sptr)
@@ -168,7 +179,8 @@ def time_execute(ge, handle, args, steps, warmup, warm_s=0.0):
     per = sorted(e0.elapsed_time(e1) for e0, e1 in ev)   # ms
     return {"wall_ms_per_step": wall * 1e3 / steps, "event_ms_mean": sum(per) / len(per),
             "event_ms_median": per[len(per) // 2], "event_ms_p10": per[len(per) // 10],
-            "event_ms_p90": per[min(len(per) - 1, (len(per) * 9) // 10)]}
+            "event_ms_p90": per[min(len(per) - 1, (len(per) * 9) // 10)], "timed": len(per),
+            "warmup_executes": done}
 
 
 def time_execute_cold(ge, handle, args, steps):
@@ -179,7 +191,8 @@ def time_execute_cold(ge, handle, args, steps):
     sptr = stream.cuda_stream
     flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda")
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    ge.gemm_epilog_execute(handle, *args, stream=sptr)
+    for _ in range(VARIANT_WARMUP):
+        ge.gemm_epilog_execute(handle, *args, stream=sptr)
     for i, (e0, e1) in enumerate(ev):
         flush.fill_(i)
         e0.record(stream)
@@ -189,7 +202,8 @@ def time_execute_cold(ge, handle, args, steps):
     del flush
     per = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
     return {"wall_ms_per_step": None, "event_ms_mean": sum(per) / len(per), "event_ms_median": per[len(per) // 2],
-            "event_ms_p10": per[len(per) // 10], "event_ms_p90": per[min(len(per) - 1, (len(per) * 9) // 10)]}
+            "event_ms_p10": per[len(per) // 10], "event_ms_p90": per[min(len(per) - 1, (len(per) * 9) // 10)],
+            "timed": len(per), "warmup_executes": VARIANT_WARMUP}
 
 
 def run_variant(ge, W, epilog, dtype, steps, warmup, device_rng, layout="NN", cold=False):
@@ -222,23 +236,35 @@ def run_variant(ge, W, epilog, dtype, steps, warmup, device_rng, layout="NN", co
     if cold:
         r = time_execute_cold(ge, h, (A, B, bias, D, aux, bg), steps)
     else:
-        r = time_execute(ge, h, (A, B, bias, D, aux, bg), steps, warmup, warm_s=0.3)
+        r = time_execute(ge, h, (A, B, bias, D, aux, bg), steps, warmup)
     desc = ge.gemm_epilog_describe(h)
     ge.gemm_epilog_free(h)
     t = r["event_ms_median"] * 1e-3
+    byts = algorithmic_bytes(m, n, k, dtype, epilog)
     out = {"epilog": epilog, "dtype": dtype, "m": m, "n": n, "k": k, "layout": layout, "plan_ms": round(plan_ms, 3),
            "kernel": desc, "median_ms": round(r["event_ms_median"], 4), "p10_ms": round(r["event_ms_p10"], 4),
-           "p90_ms": round(r["event_ms_p90"], 4), "tflops": round(2 * m * n * k / t / 1e12, 1)}
+           "p90_ms": round(r["event_ms_p90"], 4), "timed": r["timed"], "warmup_executes": r["warmup_executes"],
+           "tflops": round(2 * m * n * k / t / 1e12, 1), "algorithmic_bytes": byts,
+           "gbs": round(byts / t / 1e9, 1), "frac_of_hbm": round(byts / t / 1e9 / PEAK_HBM_GBS, 4)}
     if cold:
-        # algorithmic HBM bytes: A, B and D once, the bias; the unfused chain adds its two
-        # elementwise kernels' reads and writes of T1 and T2 (4 m n s)
-        es = 2 if dtype in ("f16", "bf16") else 4
-        byts = es * (m * k + k * n + m * n + m) + (4 * m * n * es if epilog == "RELU_BIAS_UNFUSED" else 0)
-        out.update({"cold": f"each execute after a {FLUSH_BYTES >> 20} MiB scratch write",
-                    "algorithmic_bytes": byts, "hbm_gbs": round(byts / t / 1e9, 1)})
+        out["cold"] = f"each execute after a {FLUSH_BYTES >> 20} MiB scratch write"
     del A, B, D, aux, bg
     torch.cuda.empty_cache()
     return out
+
+
+def algorithmic_bytes(m, n, k, dtype, epilog):
+    """HBM bytes one execute must move at least: A, B and D once, the bias (or, for
+    DRELU_BGRAD, the mask read and bgrad written), the mask written by RELU_AUX_BIAS, and
+    for the unfused chain its two elementwise kernels' reads and writes of T1 and T2."""
+    es = 2 if dtype in ("f16", "bf16") else 4
+    mask = 4 * ((m + 31) // 32) * n
+    byts = es * (m * k + k * n + m * n + m)
+    if epilog in ("RELU_AUX_BIAS", "DRELU_BGRAD"):
+        byts += mask
+    if epilog == "RELU_BIAS_UNFUSED":
+        byts += 4 * m * n * es
+    return byts
 
 
 PROBE_HEADLINE_CASE = "f16 N(0,1/64) (the FFN workload's operands)"
@@ -293,13 +319,13 @@ def run_autotune(ge, W, steps: int, warmup: int, repeats: int = 20):
     h = ge.gemm_epilog_plan(W.m, W.n, W.k, (W.dtype, W.dtype, W.dtype), W.epilog)
     args = (A, B, bias, D, None, None)
     before = ge.gemm_epilog_describe(h)
-    r0 = time_execute(ge, h, args, steps, warmup, warm_s=0.3)
+    r0 = time_execute(ge, h, args, steps, warmup)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     best = ge.gemm_epilog_autotune(h, *args, repeats=repeats)
     search_ms = (time.perf_counter() - t0) * 1e3
     after = ge.gemm_epilog_describe(h)
-    r1 = time_execute(ge, h, args, steps, warmup, warm_s=0.3)
+    r1 = time_execute(ge, h, args, steps, warmup)
     ge.gemm_epilog_free(h)
     del A, B, D
     torch.cuda.empty_cache()
@@ -356,9 +382,23 @@ def run_mlp_step(steps: int, warmup: int, size: int = 8192, dtype: str = "bf16")
             "tflops": round(flops / (wall_ms * 1e-3) / 1e12, 1), "kernels": kernels}
 
 
+def cpu_threads():
+    """Threads for the oracle: every CPU this process may run on, capped at the CPU share
+    the environment grants (OMP_NUM_THREADS, where set). Returns (threads, facts)."""
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count() or 1
+    share = os.environ.get("OMP_NUM_THREADS", "")
+    threads = min(usable, int(share)) if share.isdigit() and int(share) > 0 else usable
+    return threads, {"host_cpus": os.cpu_count(), "usable_cpus": usable,
+                     "cpu_share": int(share) if share.isdigit() else None}
+
+
 def cpu_baseline(W, budget_s: float):
     """The CPU oracle on the whole headline workload, repeated until about budget_s
-    seconds have passed (at least one full pass); inputs are drawn before timing."""
+    seconds have passed (at least one full pass); inputs are drawn before timing.
+    Returns (the cpu_baseline object, the oracle's D of the last pass)."""
     import numpy as np
     import torch
     import oracle
@@ -367,25 +407,45 @@ def cpu_baseline(W, budget_s: float):
         return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
 
     a, b, bias = to_np(W.a()), to_np(W.b()), to_np(W.bias())
-    threads = min(oracle.default_threads(), (W.m + 31) // 32)   # the oracle splits 32-row groups
+    threads, facts = cpu_threads()
+    threads = min(threads, (W.m + 31) // 32)   # the oracle splits 32-row groups
     passes = 0
+    out = None
     t0 = time.perf_counter()
     while passes == 0 or time.perf_counter() - t0 < budget_s:
-        oracle.gemm_epilog(a, b, W.epilog, bias=bias, ab=W.dtype, nthreads=threads)
+        out = oracle.gemm_epilog(a, b, W.epilog, bias=bias, ab=W.dtype, nthreads=threads)
         passes += 1
     dt = time.perf_counter() - t0
     return {"value": round(passes * W.flops() / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
+            "threads": threads, **facts, "kind": "oracle",
             "sample": f"{passes} full pass(es) of {W.name} {W.epilog} ({W.flops() / 1e9:.1f} GFLOP each) "
-                      f"in {dt:.1f} s, {threads} threads, inputs drawn before timing"}
+                      f"in {dt:.1f} s on {threads} threads (every usable CPU, within the CPU share), "
+                      "inputs drawn before timing"}, out["D"]
+
+
+def parity_stats(D_gpu, D_ref, dtype: str):
+    """The GPU's full headline output against the oracle's (from the cpu_baseline pass),
+    in the tolerance of the fused path: |y - y_ref| <= tol max(1, |y_ref|)."""
+    import numpy as np
+    import oracle
+    tol = {"f16": 2e-2, "bf16": 2e-2, "f32": 1e-4}[dtype]
+    y = oracle.to_f32(D_gpu, dtype).astype(np.float64)
+    r = oracle.to_f32(D_ref, dtype).astype(np.float64)
+    err = np.abs(y - r)
+    ratio = err / (tol * np.maximum(1.0, np.abs(r)))
+    bad = ~(ratio <= 1.0)
+    return {"checked": "every element of the headline D against the oracle's", "elements": int(y.size),
+            "outside_tolerance": int(bad.sum()), "non_finite": int((~np.isfinite(y)).sum()),
+            "max_abs_err": float(err.max()), "max_err_over_tol": round(float(ratio.max()), 5),
+            "bitwise_equal_frac": round(float((y == r).mean()), 5), "tolerance": f"{tol} * max(1, |ref|)"}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=1000,
-                    help="untimed executes first; ~0.3 s lets the clock settle under load")
+    ap.add_argument("--warmup", type=int, default=10,
+                    help="untimed executes first (continued until 0.5 s of warm-up: the clock settles under load)")
     ap.add_argument("--no-variants", action="store_true", help="time only the headline kernel")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--skip-cpu", action="store_true", help="leave out the cpu_baseline leg (profiling runs)")
@@ -440,9 +500,12 @@ def main():
     h = ge.gemm_epilog_plan(W.m, W.n, W.k, (W.dtype, W.dtype, W.dtype), W.epilog)
     plan_ms = (time.perf_counter() - t0) * 1e3
     log(f"[bench] plan {plan_ms:.3f} ms: {ge.gemm_epilog_describe(h)}")
-    r = time_execute(ge, h, (A, B, bias, D, None, None), args.steps, args.warmup)
+    r = time_execute(ge, h, (A, B, bias, D, None, None), args.steps, args.warmup,
+                     event_steps=max(args.steps, HEADLINE_EVENTS))
     kernel_desc = ge.gemm_epilog_describe(h)
     ge.gemm_epilog_free(h)
+    torch.cuda.synchronize()
+    D_host = D.cpu().numpy() if not args.skip_cpu else None
     flops = W.flops()
     value = flops / (r["wall_ms_per_step"] * 1e-3) / 1e12
     achieved = flops / (r["event_ms_mean"] * 1e-3) / 1e12
@@ -456,19 +519,19 @@ def main():
 
     variants = {}
     if not args.no_variants:
-        vsteps, vwarm = max(5, args.steps // 4), 5
+        vsteps, vwarm = VARIANT_STEPS, VARIANT_WARMUP
         for name, (wname, ep, dt, dev_rng, *lay) in VARIANTS.items():
-            if name == "small_relu_bias_f16":
-                continue   # latency-bound: a profiling case (--only), not a bench line
             Wv = inputs.WORKLOADS[inputs.HEADLINE if wname is None else wname]
-            steps = vsteps if Wv.flops() < 5e12 else max(3, vsteps // 5)
             log(f"[bench] variant {name}")
-            variants[name] = run_variant(ge, Wv, ep, dt, steps, vwarm, dev_rng, *lay)
+            variants[name] = run_variant(ge, Wv, ep, dt, vsteps, vwarm, dev_rng, *lay)
             log(f"[bench]   {variants[name]}")
-        fused_ms = r["event_ms_median"]
+        # fused and unfused both timed as variants: same warm-up, same number of executes
+        fused_ms = variants["ffn_relu_bias_f16"]["median_ms"]
         unf = variants["ffn_unfused_f16"]["median_ms"]
-        variants["ffn_fusion_saving"] = {"fused_ms": round(fused_ms, 4), "unfused_ms": unf,
-                                         "saving_frac": round(1 - fused_ms / unf, 4)}
+        variants["ffn_fusion_saving"] = {"fused_ms": fused_ms, "unfused_ms": unf,
+                                         "saving_frac": round(1 - fused_ms / unf, 4),
+                                         "timing": "both as variants: event medians of 50 executes after "
+                                                   "10 + 0.5 s of warm-up"}
         sq_f, sq_u = variants["square4096_relu_bias_f16"]["median_ms"], variants["square4096_unfused_f16"]["median_ms"]
         variants["square4096_fusion_saving"] = {"fused_ms": sq_f, "unfused_ms": sq_u,
                                                 "saving_frac": round(1 - sq_f / sq_u, 4)}
@@ -483,14 +546,18 @@ def main():
             variants[f"autotune_{wname}"] = run_autotune(ge, inputs.WORKLOADS[wname], vsteps, vwarm)
             log(f"[bench]   {variants[f'autotune_{wname}']}")
         log("[bench] variant mlp8192_train_step_bf16")
-        variants["mlp8192_train_step_bf16"] = run_mlp_step(max(3, vsteps // 5), 3)
+        variants["mlp8192_train_step_bf16"] = run_mlp_step(vsteps, vwarm)
         log(f"[bench]   {variants['mlp8192_train_step_bf16']}")
 
     del A, B, D
     torch.cuda.empty_cache()
     log("[bench] cpu baseline (oracle)")
-    cpu = None if args.skip_cpu else cpu_baseline(W, args.cpu_budget)
+    cpu, parity = None, None
+    if not args.skip_cpu:
+        cpu, D_ref = cpu_baseline(W, args.cpu_budget)
+        parity = parity_stats(D_host, D_ref, W.dtype)
     log(f"[bench] cpu: {cpu}")
+    log(f"[bench] parity: {parity}")
 
     out = {
         "metric": "fused GEMM+bias+ReLU TFLOP/s & % fp16 MFMA peak (4096x11008x4096)",
@@ -512,9 +579,11 @@ def main():
                      "frac": round(achieved / PEAK_F16_TFLOPS, 4), "traffic": traffic,
                      "kernel_ms_mean": round(r["event_ms_mean"], 4), "kernel_ms_median": round(r["event_ms_median"], 4),
                      "kernel_ms_p10": round(r["event_ms_p10"], 4), "kernel_ms_p90": round(r["event_ms_p90"], 4),
+                     "kernel_timed": r["timed"], "warmup_executes": r["warmup_executes"],
                      "mfma_only_on_same_values": probe_tflops,
                      "frac_of_mfma_only": round(achieved / probe_tflops, 4)},
         "cpu_baseline": cpu,
+        "parity": parity,
         "variants": variants,
     }
     print(json.dumps(out), flush=True)
