@@ -76,15 +76,36 @@ def assert_bgrad(bg: np.ndarray, bg_ref: np.ndarray, absum: np.ndarray, dt: str)
     assert not bad.any(), f"bgrad: {int(bad.sum())} of {bad.size} outside 1e-3 * sum|dz|"
 
 
-def tight_ratio(y: np.ndarray, y_ref: np.ndarray, dt: str, A: np.ndarray, B: np.ndarray, act_slope: float = 1.0):
+GELU_DEVICE_UNITS = 4.0   # the device GELU's error bound in units of 2^-24 (tests/test_gelu_gpu.py)
+
+
+def gelu_device_term(x: np.ndarray, y_ref: np.ndarray) -> np.ndarray:
+    """Bound on the device GELU's own error beyond the output rounding, for
+    pre-activations x (float64): GELU_DEVICE_UNITS 2^-24 (|y_ref| + |x| s |t|), with
+    t = 2 log2(e) u the exp2 argument and s = e/(1+e)^2 the sigmoid's slope (the
+    argument's rounding carried through exp2), plus |x| 2^-53 for the oracle's own
+    cancellation of 1 + tanh(u) in double where x is far below 0."""
+    u = 0.7978845608028654 * (x + 0.044715 * x ** 3)
+    t = 2.0 * np.log2(np.e) * u
+    e = np.exp2(np.clip(-t, -200.0, 200.0))
+    s = e / (1.0 + e) ** 2
+    return GELU_DEVICE_UNITS * 2.0 ** -24 * (np.abs(y_ref) + np.abs(x) * s * np.abs(t)) + np.abs(x) * 2.0 ** -53
+
+
+def tight_ratio(y: np.ndarray, y_ref: np.ndarray, dt: str, A: np.ndarray, B: np.ndarray, act_slope: float = 1.0,
+                gelu_pre: np.ndarray = None):
     """Error relative to a rounding-error model: output rounding 2^-p |y_ref| plus
-    fp32 accumulation k 2^-24 sum_kk |a b|. Returns max ratio (should be O(1))."""
+    fp32 accumulation k 2^-24 sum_kk |a b| (times the activation's slope), plus, for
+    GELU (gelu_pre: the oracle's pre-activations), the device GELU's own error bound.
+    Returns max ratio (should be O(1))."""
     p = {"f16": 11, "bf16": 8, "f32": 24}[dt]
     y = widen(y, dt)
     y_ref = widen(y_ref, dt)
     k = A.shape[1]
     absprod = np.abs(A.astype(np.float64)) @ np.abs(B.astype(np.float64))
     scale = 2.0 ** -p * np.abs(y_ref) + act_slope * k * 2.0 ** -24 * absprod + 1e-7
+    if gelu_pre is not None:
+        scale = scale + gelu_device_term(np.asarray(gelu_pre, np.float64), y_ref)
     ratio = np.abs(y - y_ref) / scale
     # NaN anywhere (an unwritten element) counts as an unbounded error
     return float("inf") if np.isnan(ratio).any() else float(ratio.max())
