@@ -767,30 +767,37 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_dtl_kernel
   epilogue_lds<DT, EP, C::MB, C::NB, WN>(p, acc, m0 + wm * WM, n0 + wn * WN, lane, smem + w * C::SCRATCH);
 }
 
-// Operand copies of the persistent kernel, for K a multiple of BK. A copy
-// instruction idx covers A_RPI rows of A (or B_RPI rows of B); its lanes' offsets
-// inside those rows depend only on the parity of idx (the chunk swizzles repeat with
-// period two in idx), so two offsets per operand stay in VGPRs and the row block goes
-// into the buffer descriptor's base. Rows of A past m fall outside the descriptor's
-// range and read as zero; B columns past n get an out-of-range offset.
+// Operand copies of the persistent kernel, for K a multiple of BK. Each copy wave
+// copies a contiguous block of rows of A (A_INST instructions of A_RPI rows) and of B
+// (B_INST instructions of B_RPI k-rows). Per k-tile it builds one buffer descriptor per
+// operand, with the k-tile and its row block in the base; an instruction's lanes take
+// their offset inside the block from two per-parity lane offsets (the chunk swizzles
+// repeat with the parity of the instruction) plus the instruction's row step, and its
+// LDS slot from M0. Few scalar instructions per copy keep the copy waves close to the
+// others at each k-tile's barrier.
 template <int BM, int BN, int WM, int WN, int BK, int STAGES, int CW>
 struct CopyPlan {
   using C = DtlCfg<BM, BN, WM, WN, BK, STAGES, CW>;
   static_assert(C::A_RPI % 8 == 0 || C::A_ROWB == 64, "A swizzle period");
   static_assert(C::B_RPI % 2 == 0, "B swizzle period");
+  static_assert(C::A_INST % 2 == 0 && C::B_INST % 2 == 0, "copy parity follows j");
 
-  const char* Atile;   // A row m0 of the current tile
-  const char* Btile;   // B column n0 of the current tile
-  int64_t rows_left;   // rows of A from this wave's first copied row to m
+  const char* Arows;   // A at this wave's first copied row of the current tile, k = 0
+  const char* Brows;   // B at this wave's first copied k-row, column n0 of the current tile
+  uint32_t a_valid;    // bytes of this wave's copied rows of A that lie below m (rows * K * 2)
   int N, K, w;
-  uint32_t lds_base;
-  uint32_t a_lane[2], b_lane[2];
+  uint32_t lds_a, lds_b;           // this wave's first LDS copy slot of stage 0 (A, B)
+  uint32_t a_lane[2], b_lane[2];   // lane offsets of an even / odd copy instruction
+  uint32_t a_step, b_step;         // bytes between consecutive copy instructions
 
   __device__ __forceinline__ CopyPlan(const Args& p, int w_, int lane, uint32_t lds) {
     N = p.n;
     K = p.k;
     w = w_;
-    lds_base = lds;
+    lds_a = lds + w * C::A_INST * 1024;
+    lds_b = lds + C::A_BYTES + w * C::B_INST * 1024;
+    a_step = (uint32_t)(C::A_RPI * K * 2);
+    b_step = (uint32_t)(C::B_RPI * N * 2);
 #pragma unroll
     for (int par = 0; par < 2; ++par) {
       const int row = par * C::A_RPI + lane / C::A_CHUNKS;
@@ -799,9 +806,11 @@ struct CopyPlan {
     }
   }
   __device__ __forceinline__ void retarget(const Args& p, int64_t m0, int n0, int lane) {
-    Atile = static_cast<const char*>(p.A) + m0 * (int64_t)K * 2;
-    Btile = static_cast<const char*>(p.B) + (int64_t)n0 * 2;
-    rows_left = p.m - m0 - (int64_t)w * C::A_INST * C::A_RPI;
+    const int64_t r0 = m0 + (int64_t)w * C::A_INST * C::A_RPI;
+    Arows = static_cast<const char*>(p.A) + r0 * (int64_t)K * 2;
+    const int64_t rows = p.m - r0;
+    a_valid = (uint32_t)((rows <= 0 ? 0 : rows >= C::A_INST * C::A_RPI ? C::A_INST * C::A_RPI : rows) * K * 2);
+    Brows = static_cast<const char*>(p.B) + ((int64_t)w * C::B_INST * C::B_RPI * N + n0) * 2;
 #pragma unroll
     for (int par = 0; par < 2; ++par) {
       const int row = par * C::B_RPI + lane / C::B_CHUNKS;
@@ -809,44 +818,45 @@ struct CopyPlan {
       b_lane[par] = (n0 + c * 8 < N) ? (uint32_t)((lane / C::B_CHUNKS) * N * 2 + c * 16) : kOOB;
     }
   }
+  // One descriptor per operand and k-tile. A rows at or past m: the descriptor's range
+  // ends at this wave's last valid row (every valid row's 128 bytes at k0 lie below it,
+  // as k0 + BK <= K), so their offsets read as zero. B columns past n: kOOB lane offsets.
   __device__ __forceinline__ void issue_tile(int kt, int stage) const {
     const int64_t k0 = (int64_t)kt * BK;
-    const uint32_t sA = lds_base + stage * C::STAGE;
-    const uint32_t sB = sA + C::A_BYTES;
+    const uint32_t ka = (uint32_t)(k0 * 2);
+    const i32x4 ra = make_srd(Arows + k0 * 2, a_valid > ka ? a_valid - ka : 0u);
+    const i32x4 rb = make_srd(Brows + k0 * N * 2, 0x7fffffffu);
+    const uint32_t sa = lds_a + stage * C::STAGE, sb = lds_b + stage * C::STAGE;
 #pragma unroll
-    for (int j = 0; j < C::A_INST; ++j) {
-      const int idx = w * C::A_INST + j;
-      const int par = ((C::A_INST % 2 == 0) ? j : idx) & 1;
-      const int64_t left = rows_left - (int64_t)j * C::A_RPI;
-      const uint32_t range = left >= C::A_RPI ? 0x7fffffffu : left > 0 ? (uint32_t)(left * K * 2) : 0u;
-      const char* base = Atile + k0 * 2 + (int64_t)idx * C::A_RPI * K * 2;
-      copy_to_lds_b128(make_srd(base, range), par ? a_lane[1] : a_lane[0], sA + idx * 1024);
-    }
+    for (int j = 0; j < C::A_INST; ++j)
+      copy_to_lds_b128(ra, a_lane[j & 1] + j * a_step, sa + j * 1024);
 #pragma unroll
-    for (int j = 0; j < C::B_INST; ++j) {
-      const int idx = w * C::B_INST + j;
-      const int par = ((C::B_INST % 2 == 0) ? j : idx) & 1;
-      const char* base = Btile + (k0 + (int64_t)idx * C::B_RPI) * N * 2;
-      copy_to_lds_b128(make_srd(base, 0x7fffffffu), par ? b_lane[1] : b_lane[0], sB + idx * 1024);
-    }
+    for (int j = 0; j < C::B_INST; ++j)
+      copy_to_lds_b128(rb, b_lane[j & 1] + j * b_step, sb + j * 1024);
   }
 };
 
 // Copies of the persistent kernel for operands in either storage order (LAY != 0), on the
-// pattern of CopyPlan: per operand two lane offsets (the swizzle repeats with the parity
-// of the copy instruction) and the instruction's row block in the descriptor's base.
+// pattern of CopyPlan: each copy wave copies a contiguous block of INST instructions of
+// RPI stored rows; per k-tile one descriptor per operand, two per-parity lane offsets
+// (the swizzle repeats with the parity of the instruction) plus the instruction's row
+// step. K is a multiple of BK.
 // k-major tile (A as stored, or B given as B^T): MN rows of 2 BK bytes; rows past the
-// operand's extent fall outside the descriptor's range and read as zero.
+// operand's extent fall outside the descriptor's range (which ends at this wave's last
+// valid row; every valid row's 2 BK bytes at k0 lie below it) and read as zero.
 template <int MN, int BK, int INST>
 struct KMajorCopy {
   using G = TileGeom<MN, BK, true>;
   static_assert(G::RPI % 8 == 0 || G::ROWB == 64, "swizzle period");
-  const char* tile;
-  int64_t rows_left;   // rows from this wave's first copied row to the extent
+  static_assert(INST % 2 == 0, "copy parity follows j");
+  const char* rows;    // this wave's first copied row of the current tile, k = 0
+  uint32_t valid;      // bytes of this wave's copied rows inside the extent
+  uint32_t step;       // bytes between consecutive copy instructions (RPI rows)
   int64_t ldb;
   uint32_t lane_off[2];
   __device__ __forceinline__ void init(int K, int lane) {
     ldb = (int64_t)K * 2;
+    step = (uint32_t)(G::RPI * ldb);
 #pragma unroll
     for (int par = 0; par < 2; ++par) {
       const int row = par * G::RPI + lane / G::CHUNKS;
@@ -855,34 +865,36 @@ struct KMajorCopy {
     }
   }
   __device__ __forceinline__ void retarget(const void* X, int64_t mn0, int64_t mndim, int w, int) {
-    tile = static_cast<const char*>(X) + mn0 * ldb;
-    rows_left = mndim - mn0 - (int64_t)w * INST * G::RPI;
+    const int64_t r0 = mn0 + (int64_t)w * INST * G::RPI;
+    rows = static_cast<const char*>(X) + r0 * ldb;
+    const int64_t left = mndim - r0;
+    valid = __builtin_amdgcn_readfirstlane(
+        (int)((left <= 0 ? 0 : left >= INST * G::RPI ? INST * G::RPI : left) * ldb));
   }
   __device__ __forceinline__ void issue(int64_t k0, int w, uint32_t dst) const {
+    const uint32_t kb = (uint32_t)(k0 * 2);
+    const i32x4 srd = make_srd(rows + k0 * 2, valid > kb ? valid - kb : 0u);
+    const uint32_t d = dst + w * INST * 1024;
 #pragma unroll
-    for (int j = 0; j < INST; ++j) {
-      const int idx = w * INST + j;
-      const int par = ((INST % 2 == 0) ? j : idx) & 1;
-      const int64_t left = rows_left - (int64_t)j * G::RPI;
-      const uint32_t range = left >= G::RPI ? 0x7fffffffu : left > 0 ? (uint32_t)(left * ldb) : 0u;
-      const char* base = tile + k0 * 2 + (int64_t)idx * G::RPI * ldb;
-      copy_to_lds_b128(make_srd(base, range), par ? lane_off[1] : lane_off[0], dst + idx * 1024);
-    }
+    for (int j = 0; j < INST; ++j) copy_to_lds_b128(srd, lane_off[j & 1] + j * step, d + j * 1024);
   }
 };
 // mn-major tile (B as stored, or A given as A^T): BK rows of 2 MN bytes; columns past the
-// operand's extent get an out-of-range offset.
+// operand's extent get an out-of-range lane offset.
 template <int MN, int BK, int INST>
 struct MNMajorCopy {
   using G = TileGeom<MN, BK, false>;
   static_assert(G::RPI % 2 == 0, "swizzle period");
-  const char* tile;
+  static_assert(INST % 2 == 0, "copy parity follows j");
+  const char* rows;    // this wave's first copied k-row, column mn0 of the current tile
+  uint32_t step;       // bytes between consecutive copy instructions (RPI k-rows)
   int64_t ldb;
   uint32_t lane_off[2];
   __device__ __forceinline__ void init(int, int) {}
-  __device__ __forceinline__ void retarget(const void* X, int64_t mn0, int64_t mndim, int, int lane) {
+  __device__ __forceinline__ void retarget(const void* X, int64_t mn0, int64_t mndim, int w, int lane) {
     ldb = mndim * 2;
-    tile = static_cast<const char*>(X) + mn0 * 2;
+    step = (uint32_t)(G::RPI * ldb);
+    rows = static_cast<const char*>(X) + mn0 * 2 + (int64_t)w * INST * G::RPI * ldb;
 #pragma unroll
     for (int par = 0; par < 2; ++par) {
       const int row = par * G::RPI + lane / G::CHUNKS;
@@ -891,13 +903,10 @@ struct MNMajorCopy {
     }
   }
   __device__ __forceinline__ void issue(int64_t k0, int w, uint32_t dst) const {
+    const i32x4 srd = make_srd(rows + k0 * ldb, 0x7fffffffu);
+    const uint32_t d = dst + w * INST * 1024;
 #pragma unroll
-    for (int j = 0; j < INST; ++j) {
-      const int idx = w * INST + j;
-      const int par = ((INST % 2 == 0) ? j : idx) & 1;
-      const char* base = tile + (k0 + (int64_t)idx * G::RPI) * ldb;
-      copy_to_lds_b128(make_srd(base, 0x7fffffffu), par ? lane_off[1] : lane_off[0], dst + idx * 1024);
-    }
+    for (int j = 0; j < INST; ++j) copy_to_lds_b128(srd, lane_off[j & 1] + j * step, d + j * 1024);
   }
 };
 

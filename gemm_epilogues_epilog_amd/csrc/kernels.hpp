@@ -174,10 +174,11 @@ template <> struct Tr<F16> {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
                                                   0, 0, 0);
   }
+  // two values rounded to nearest even in one v_cvt_pk_f16_f32 (lo in bits 15:0)
   __device__ static __forceinline__ uint32_t pack2(float lo, float hi) {
-    const uint32_t l = __builtin_bit_cast(uint16_t, (_Float16)lo);
-    const uint32_t h = __builtin_bit_cast(uint16_t, (_Float16)hi);
-    return l | (h << 16);
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{lo, hi}), f16x2_t));
   }
   __device__ static __forceinline__ float widen(uint16_t v) { return (float)__builtin_bit_cast(_Float16, v); }
 };
@@ -189,10 +190,11 @@ template <> struct Tr<BF16> {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
                                                    0, 0, 0);
   }
+  // two values rounded to nearest even in one v_cvt_pk_bf16_f32 (lo in bits 15:0)
   __device__ static __forceinline__ uint32_t pack2(float lo, float hi) {
-    const uint32_t l = __builtin_bit_cast(uint16_t, (__bf16)lo);
-    const uint32_t h = __builtin_bit_cast(uint16_t, (__bf16)hi);
-    return l | (h << 16);
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{lo, hi}), bf16x2_t));
   }
   __device__ static __forceinline__ float widen(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
 };
