@@ -1166,16 +1166,185 @@ constexpr int kDeviceScope = 16;   // cache-policy bit sc1 of a buffer instructi
 // one.
 constexpr uint32_t kSkAbort = 0xffffffffu;   // epochs stay below 2^31
 
-__device__ __forceinline__ bool sk_wait_flag(uint32_t* flag, uint32_t epoch, uint32_t spin_limit) {
-  for (uint32_t spins = 0; spins < spin_limit; ++spins) {
-    if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch) return true;
-    __builtin_amdgcn_s_sleep(8);
+// Wave 0 of an owner waits for flags[0 .. np - 1], one lane per flag, so all the
+// polls of one round trip are in flight together. Returns how many waits ran out
+// (their flags now hold kSkAbort, or were published while the spin ran out).
+__device__ __forceinline__ uint32_t sk_wait_flags(uint32_t* flags, int np, uint32_t epoch, uint32_t spin_limit,
+                                                  int lane) {
+  uint32_t lost = 0u;
+  for (int j0 = 0; j0 < np; j0 += 64) {
+    const int j = j0 + lane;
+    uint32_t* f = flags + j;
+    bool got = j >= np;
+    for (uint32_t spins = 0; spins < spin_limit; ++spins) {
+      if (!got) got = __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch;
+      if (__builtin_amdgcn_ballot_w64(!got) == 0) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+    if (!got) {
+      uint32_t expected = 0u;
+      // abandoned: the late publisher will reset it; else published while the spin ran out
+      if (!__hip_atomic_compare_exchange_strong(f, &expected, kSkAbort, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT))
+        got = expected == epoch;
+    }
+    lost += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(!got));
   }
-  uint32_t expected = 0u;
-  if (__hip_atomic_compare_exchange_strong(flag, &expected, kSkAbort, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT))
-    return false;                 // abandoned: the late publisher will reset it
-  return expected == epoch;       // published while the spin ran out
+  return lost;
+}
+
+// Split runs that cover whole tiles (KT a multiple of the run length): the S runs of
+// tail tile t are t S .. t S + S - 1, run s computing k-tiles [s units, (s + 1) units).
+// The tile is finished in S parts, one per run: wave w's sub-tile belongs to run
+// w % S. Every run stores the sub-tiles of its waves that other runs finish, publishes
+// them, waits until all S runs have published, and its own waves add the other runs'
+// partials of their sub-tiles (own sum first, then the others in run order) and run
+// the epilogue. Each run thus moves (S - 1) / S of a tile each way instead of the
+// owner's S - 1 tiles in one workgroup, and the epilogue is spread over S workgroups.
+//
+// Each tail tile has two counters in the flag region: words 2t (published) and 2t + 1
+// (finished). A run adds 1 to the first once its stores have completed and waits (a
+// bounded spin, p.sk_spin_limit polls) until it reads S; after its loads it adds 1 to
+// the second, and the run that brings it to S sets both back to 0. Every run publishes
+// before it waits and finishes after its wait, so the last to finish finds both
+// complete and nothing touches them after it: the counters are 0 when the kernel ends,
+// lost wait or not, and a replayed graph starts from clean counters. A wait that runs
+// out is counted in the flag region's last word and gives NaN for the run's part.
+template <int DT, int EP, int BM, int BN, int WM, int WN, int BK, int STAGES, bool ILV, int CW>
+__device__ __forceinline__ void sk_reduce_scatter(const Args& p, char* smem, int r, int S, uint32_t& lost_any) {
+  using C = DtlCfg<BM, BN, WM, WN, BK, STAGES>;
+  using PL = PartialLayout<C::MB, C::NB>;
+  constexpr int MB = C::MB, NB = C::NB;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = w % C::WAVES_M, wn = w / C::WAVES_M;
+  const size_t slot_bytes = (size_t)C::NW * PL::WAVE_BYTES;
+  const int t = r / S, s = r - t * S;
+  int tm, tn;
+  raster(p, p.dp_tiles + t, tm, tn);
+
+  f32x16 acc[NB][MB];
+  lockstep_tile<DT, BM, BN, WM, WN, BK, STAGES, ILV, CW>(p, smem, (int64_t)tm * BM, tn * BN, s * p.sk_units,
+                                                        p.sk_units, acc);
+  const bool mine = w % S == s;
+  char* const base = reinterpret_cast<char*>(p.sk_partial);
+  if (!mine) {
+    const __amdgpu_buffer_rsrc_t slot = rsrc(base + (size_t)r * slot_bytes);
+#pragma unroll
+    for (int a = 0; a < NB; ++a)
+#pragma unroll
+      for (int bb = 0; bb < MB; ++bb)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const i32x4 v = {__float_as_int(acc[a][bb][4 * r4]), __float_as_int(acc[a][bb][4 * r4 + 1]),
+                           __float_as_int(acc[a][bb][4 * r4 + 2]), __float_as_int(acc[a][bb][4 * r4 + 3])};
+          __builtin_amdgcn_raw_buffer_store_b128(v, slot, PL::off(w, (a * MB + bb) * 4 + r4, lane), 0, kDeviceScope);
+        }
+  }
+  wait_vmcnt<0>();
+  wait_lgkmcnt<0>();   // also: every wave is done with the LDS stages
+  barrier_only();
+  uint32_t* const cnt = p.sk_flag + 2 * t;   // [published, finished]
+  // the epilogue's bias values (DRELU_BGRAD: mask words) load during the wait
+  const int64_t m0w = (int64_t)tm * BM + wm * WM;
+  const int n0w = tn * BN + wn * WN;
+  uint32_t bbits[MB], mwords[MB][NB];
+  if (mine) {
+#pragma unroll
+    for (int b = 0; b < MB; ++b) {
+      const int64_t row = m0w + 32 * b + (lane & 31);
+      bbits[b] = 0u;
+      if constexpr (EP != NONE && EP != DRELU_BGRAD) {
+        if (row < p.m) bbits[b] = load_vec_bits(p.bias, p.vec_dt, row);
+      }
+#pragma unroll
+      for (int a = 0; a < NB; ++a) {
+        mwords[b][a] = 0u;
+        if constexpr (EP == DRELU_BGRAD) {
+          const int64_t grp = (m0w + 32 * b) >> 5;
+          const int ncol = n0w + 32 * a + (lane & 31);
+          if (grp * 32 < p.m && ncol < p.n) mwords[b][a] = p.aux[grp * p.n + ncol];
+        }
+      }
+    }
+  }
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    bool all = false;
+    for (uint32_t spins = 0; spins < p.sk_spin_limit && !all; ++spins) {
+      all = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)S;
+      if (!all) __builtin_amdgcn_s_sleep(2);
+    }
+    if (!all) all = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)S;
+    if (!all) __hip_atomic_fetch_add(p.sk_flag + kSkLostWord, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    lost_any = all ? 0u : 1u;
+  }
+  wait_lgkmcnt<0>();
+  barrier_only();
+  const bool lost = lost_any != 0u;
+  if (mine) {
+    if (!lost) {
+      // the other runs' partials of this sub-tile, read at device scope: LOADS loads in
+      // flight at a time, QB 4-float groups of each of PB runs
+      constexpr int LOADS = MB * NB <= 2 ? 24 : 16;
+      constexpr int QB = PL::QUADS < LOADS ? PL::QUADS : LOADS;
+      constexpr int PB = LOADS / QB;
+      static_assert(PL::QUADS % QB == 0, "load batches");
+      for (int o0 = 0; o0 < S; o0 += PB) {
+#pragma unroll
+        for (int q0 = 0; q0 < PL::QUADS; q0 += QB) {
+          i32x4 v[PB][QB];
+#pragma unroll
+          for (int i = 0; i < PB; ++i)
+            if (o0 + i < S && o0 + i != s) {
+              const __amdgpu_buffer_rsrc_t slot = rsrc(base + (size_t)(t * S + o0 + i) * slot_bytes);
+#pragma unroll
+              for (int j = 0; j < QB; ++j)
+                v[i][j] = __builtin_amdgcn_raw_buffer_load_b128(slot, PL::off(w, q0 + j, lane), 0, kDeviceScope);
+            }
+#pragma unroll
+          for (int i = 0; i < PB; ++i)
+            if (o0 + i < S && o0 + i != s) {
+#pragma unroll
+              for (int j = 0; j < QB; ++j) {
+                const int q = q0 + j, a = q / (4 * MB), bb = (q / 4) % MB, r4 = q % 4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[a][bb][4 * r4 + e] += __int_as_float(v[i][j][e]);
+              }
+            }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int a = 0; a < NB; ++a)
+#pragma unroll
+        for (int bb = 0; bb < MB; ++bb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[a][bb][e] = __builtin_nanf("");
+    }
+  }
+  // every wave's loads have completed before the run counts itself finished
+  wait_vmcnt<0>();
+  barrier_only();
+  if (threadIdx.x == 0) {
+    if (__hip_atomic_fetch_add(cnt + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(S - 1)) {
+      __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(cnt + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  if (mine) {
+#pragma unroll
+    for (int b = 0; b < MB; ++b)
+      epilogue_block<DT, EP, MB, NB, WN>(p, acc, b, vec_value(bbits[b], p.vec_dt), mwords[b], m0w, n0w, lane,
+                                         smem + w * C::SCRATCH);
+    // a lost wait: the activation may have turned the NaN accumulators into zeros, so
+    // the sub-tile of D is written again with them as they are
+    if (lost) {
+#pragma unroll
+      for (int b = 0; b < MB; ++b)
+        epilogue_block<DT, NONE, MB, NB, WN>(p, acc, b, 0.0f, mwords[b], m0w, n0w, lane, smem + w * C::SCRATCH);
+    }
+  }
 }
 
 template <int DT, int EP, int BM, int BN, int WM, int WN, int BK, int STAGES, bool ILV, int CW>
@@ -1205,6 +1374,12 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_sk_kernel(
     nt = run.own_nt;
   }
   const int pa_t = run.pa_t, pa_kb = run.pa_kb, pa_nt = run.pa_nt;
+  __shared__ uint32_t lost_any;
+
+  if (split && KT % p.sk_units == 0) {
+    sk_reduce_scatter<DT, EP, BM, BN, WM, WN, BK, STAGES, ILV, CW>(p, smem, r, KT / p.sk_units, lost_any);
+    return;
+  }
 
   f32x16 acc[NB][MB];
   bool lost = false;   // the owner: a partner's partial did not arrive in time
@@ -1241,14 +1416,14 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_sk_kernel(
   raster(p, pos, tm, tn);
   lockstep_tile<DT, BM, BN, WM, WN, BK, STAGES, ILV, CW>(p, smem, (int64_t)tm * BM, tn * BN, 0, nt, acc);
   if (split) {
-    // the owner: one thread waits for the partials of runs r+1 .. last, which hold the
-    // rest of the tile, and tells the workgroup through LDS whether all arrived
-    __shared__ uint32_t lost_any;
-    if (threadIdx.x == 0) {
-      uint32_t lost = 0u;
-      for (int o = r + 1; o <= run.last; ++o) lost += sk_wait_flag(p.sk_flag + o, p.epoch, p.sk_spin_limit) ? 0u : 1u;
-      if (lost) __hip_atomic_fetch_add(p.sk_flag + kSkLostWord, lost, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      lost_any = lost;
+    // the owner: wave 0 waits for the partials of runs r+1 .. last, which hold the rest
+    // of the tile, and tells the workgroup through LDS whether all arrived
+    if (w == 0) {
+      const uint32_t lost = sk_wait_flags(p.sk_flag + r + 1, run.last - r, p.epoch, p.sk_spin_limit, lane);
+      if (lane == 0) {
+        if (lost) __hip_atomic_fetch_add(p.sk_flag + kSkLostWord, lost, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        lost_any = lost;
+      }
     }
     wait_lgkmcnt<0>();
     barrier_only();
@@ -1256,23 +1431,35 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_sk_kernel(
     // side (device scope)
     lost = lost_any != 0u;
     if (!lost) {
-      for (int o = r + 1; o <= run.last; ++o) {
-        const __amdgpu_buffer_rsrc_t slot = rsrc(reinterpret_cast<char*>(p.sk_partial) + (size_t)o * slot_bytes);
-        // sixteen loads in flight at a time, then the adds
-        constexpr int BATCH = PL::QUADS < 16 ? PL::QUADS : 16;
-        static_assert(PL::QUADS % BATCH == 0, "load batches");
+      // LOADS loads in flight at a time: QB 4-float groups of each of PB partials, then
+      // the adds, partials in run order (the order of the sums does not depend on PB)
+      constexpr int LOADS = MB * NB <= 2 ? 24 : 16;
+      constexpr int QB = PL::QUADS < LOADS ? PL::QUADS : LOADS;
+      constexpr int PB = LOADS / QB;
+      static_assert(PL::QUADS % QB == 0, "load batches");
+      char* const base = reinterpret_cast<char*>(p.sk_partial);
+      for (int o0 = r + 1; o0 <= run.last; o0 += PB) {
 #pragma unroll
-        for (int q0 = 0; q0 < PL::QUADS; q0 += BATCH) {
-          i32x4 v[BATCH];
+        for (int q0 = 0; q0 < PL::QUADS; q0 += QB) {
+          i32x4 v[PB][QB];
 #pragma unroll
-          for (int j = 0; j < BATCH; ++j)
-            v[j] = __builtin_amdgcn_raw_buffer_load_b128(slot, PL::off(w, q0 + j, lane), 0, kDeviceScope);
+          for (int i = 0; i < PB; ++i)
+            if (o0 + i <= run.last) {
+              const __amdgpu_buffer_rsrc_t slot = rsrc(base + (size_t)(o0 + i) * slot_bytes);
 #pragma unroll
-          for (int j = 0; j < BATCH; ++j) {
-            const int q = q0 + j, a = q / (4 * MB), bb = (q / 4) % MB, r4 = q % 4;
+              for (int j = 0; j < QB; ++j)
+                v[i][j] = __builtin_amdgcn_raw_buffer_load_b128(slot, PL::off(w, q0 + j, lane), 0, kDeviceScope);
+            }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[a][bb][4 * r4 + e] += __int_as_float(v[j][e]);
-          }
+          for (int i = 0; i < PB; ++i)
+            if (o0 + i <= run.last) {
+#pragma unroll
+              for (int j = 0; j < QB; ++j) {
+                const int q = q0 + j, a = q / (4 * MB), bb = (q / 4) % MB, r4 = q % 4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[a][bb][4 * r4 + e] += __int_as_float(v[i][j][e]);
+              }
+            }
         }
       }
     } else {
@@ -1288,10 +1475,10 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_sk_kernel(
   wait_vmcnt<0>();
   wait_lgkmcnt<0>();
   barrier_only();
-  if (split && threadIdx.x == 0) {
-    // every wave has read the partials: set the consumed flags (epoch) back to 0; an
-    // abandoned flag (kSkAbort) is reset by its late publisher
-    for (int o = r + 1; o <= run.last; ++o) {
+  if (split && w == 0) {
+    // every wave has read the partials: set the consumed flags (epoch) back to 0, one
+    // lane per flag; an abandoned flag (kSkAbort) is reset by its late publisher
+    for (int o = r + 1 + lane; o <= run.last; o += 64) {
       uint32_t expected = p.epoch;
       __hip_atomic_compare_exchange_strong(p.sk_flag + o, &expected, 0u, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT);

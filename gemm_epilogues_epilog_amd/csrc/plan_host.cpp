@@ -177,6 +177,7 @@ ge_status_t make_layout(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt, ge_epil
         L.dp_tiles = (int)(tiles - rem);
         L.sk_units = (int)per;
         L.sk_wgs = (int)cdiv(units, per);
+        L.sk_parts = kt % per == 0 ? (int)(kt / per) : 0;
       }
     }
   }
@@ -225,7 +226,8 @@ std::string describe(ge_dtypes_t dt, ge_epilog_t ep, const Layout& L) {
   if (L.persist_grid) s += " on " + std::to_string(L.persist_grid) + " persistent workgroups";
   if (L.sk_wgs)
     s += " (" + std::to_string(L.dp_tiles) + " whole + " + std::to_string(tiles - L.dp_tiles) + " split over " +
-         std::to_string(L.sk_wgs) + "x" + std::to_string(L.sk_units) + " k-tiles)";
+         std::to_string(L.sk_wgs) + "x" + std::to_string(L.sk_units) + " k-tiles" +
+         (L.sk_parts ? ", " + std::to_string(L.sk_parts) + " parts per tile)" : ")");
   return s;
 }
 

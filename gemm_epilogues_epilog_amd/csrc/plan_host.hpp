@@ -27,6 +27,7 @@ struct Layout {
   int dp_tiles = 0;       // tiles computed whole (all tiles when the grid is not split)
   int sk_units = 0;       // split tail: k-tiles per split workgroup
   int sk_wgs = 0;         // split tail: split workgroups
+  int sk_parts = 0;       // split tail: runs per tile when they cover whole tiles (each finishes a part), else 0
   int persist_grid = 0;   // persistent workgroups (0: one workgroup per tile)
   int partial_cols = 0;   // DRELU_BGRAD: partial row sums per row (one per wave column)
   // Workspace: [split flags][DRELU_BGRAD partials | unfused T1, T2][split partials];

@@ -15,13 +15,17 @@ GUARD = 256   # guard elements (multiple of 16 bytes for every dtype)
 @contextmanager
 def tile_env(tile):
     """Force a tile configuration for the plans made inside. A "-nosk" suffix also turns
-    off the split tail (GE_STREAMK=0)."""
-    saved = {k: os.environ.get(k) for k in ("GE_TILE", "GE_STREAMK")}
+    off the split tail (GE_STREAMK=0); "-runN" forces split runs of N k-tiles
+    (GE_SK_RUN), so runs that do not divide a tile's k loop take the owner-adds-partials
+    protocol."""
+    saved = {k: os.environ.get(k) for k in ("GE_TILE", "GE_STREAMK", "GE_SK_RUN")}
     if tile:
         name, _, opt = tile.partition("-")
         os.environ["GE_TILE"] = name
         if opt == "nosk":
             os.environ["GE_STREAMK"] = "0"
+        elif opt.startswith("run"):
+            os.environ["GE_SK_RUN"] = opt[3:]
     try:
         yield
     finally:

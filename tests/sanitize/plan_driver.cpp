@@ -122,6 +122,23 @@ void check_split(const geh::Layout& L, int kt, int cus, long long m, long long n
   for (int r = 0; r < L.sk_wgs; ++r)
     check(waited[(size_t)r] == (partial_tile[(size_t)r] >= 0 ? 1 : 0), "each published partial has one waiter", m, n,
           k, L.cfg);
+  // runs that cover whole tiles: the kernel takes run r as part r % S of tail tile r / S
+  // and counts each tile's publications in flag words 2t and 2t + 1
+  check((L.sk_parts != 0) == (kt % L.sk_units == 0), "parts exactly when runs divide the tile", m, n, k, L.cfg);
+  if (L.sk_parts) {
+    const int S = L.sk_parts;
+    check(S >= 2 && S * L.sk_units == kt && L.sk_wgs == tail * S, "parts cover each tile", m, n, k, L.cfg);
+    check(2 * tail <= gek::kSkLostWord, "tile counters below the lost-wait word", m, n, k, L.cfg);
+    for (int r = 0; r < L.sk_wgs; ++r) {
+      const gek::SkRun s = gek::sk_run(r, L.sk_units, kt, tail, L.sk_wgs);
+      const int t = r / S, part = r % S;
+      if (part == 0)
+        check(s.pa_nt == 0 && s.own_t == t && s.own_nt == L.sk_units, "part 0 starts its tile", m, n, k, L.cfg);
+      else
+        check(s.own_nt == 0 && s.pa_t == t && s.pa_kb == part * L.sk_units && s.pa_nt == L.sk_units,
+              "part s covers k-tiles [s units, (s + 1) units)", m, n, k, L.cfg);
+    }
+  }
 }
 
 void check_layout(long long m, long long n, long long k, ge_dtype_t t, ge_epilog_t ep, int cus) {

@@ -1,12 +1,15 @@
 """The split tail's bounded wait, forced to run out from the host: a plan made with
-GE_SK_SPIN=0 lets each owner poll its partners' flags zero times before it gives up, so
-whether a partial is taken depends on the race with its publisher. Every kernel still
-ends normally. Each tile of D must then be either exactly the result of a normal plan
-or all NaN (a lost wait), never a wrong finite value; gemm_epilog_lost_waits counts at
-least one lost wait per NaN tile. Replays of a captured graph repeat the epoch of the
-capture, so a flag left set by a late publisher would hand a later replay the previous
-replay's partial: the replays below run on new operand values each time and would show
-that as a wrong finite tile."""
+GE_SK_SPIN=0 lets each waiting workgroup poll zero times before it gives up, so whether
+a partial is taken depends on the race with its publisher. Every kernel still ends
+normally. Two protocols are covered: runs that cover whole tiles (each run finishes the
+sub-tiles of some of its waves, counting publications per tile) and runs of any other
+length (forced with GE_SK_RUN: an owner run adds its partners' partials, one flag per
+partial). Each wave sub-tile of D must then be either exactly the result of a normal
+plan or all NaN (a lost wait), never a wrong finite value; gemm_epilog_lost_waits counts
+the lost waits, each of which accounts for at most one workgroup's eight sub-tiles.
+Replays of a captured graph repeat the epoch of the capture, so a flag or counter left
+set would hand a later replay the previous replay's partial: the replays below run on
+new operand values each time and would show that as a wrong finite sub-tile."""
 import os
 
 import numpy as np
@@ -20,7 +23,7 @@ pytestmark = pytest.mark.gpu
 
 
 def tile_states(D, ref, bm, bn):
-    """Per output tile: 'ok' (bits equal to ref), 'nan' (all NaN) or 'bad'."""
+    """Per bm x bn block of D: 'ok' (bits equal to ref), 'nan' (all NaN) or 'bad'."""
     m, n = D.shape
     out = []
     for i in range(0, m, bm):
@@ -35,22 +38,31 @@ def tile_states(D, ref, bm, bn):
     return out
 
 
-@pytest.mark.parametrize("shape,tile", [((1024, 512, 2048), 128), ((4352, 4096, 1024), 256)])
-def test_lost_waits_leave_clean_flags(gpu, shape, tile):
+# (shape, wave sub-tile, forced run length, whether the runs cover whole tiles)
+CASES = [((1024, 512, 2048), (32, 64), None, True),      # 128 x 128 tiles, 4 parts per tile
+         ((4352, 4096, 1024), (128, 64), None, True),    # 256 x 256 tiles, 4 parts per tile
+         ((1024, 512, 2048), (32, 64), "12", False)]     # runs of 12 of a tile's 32 k-tiles
+
+
+@pytest.mark.parametrize("shape,sub,run_len,parts", CASES)
+def test_lost_waits_leave_clean_flags(gpu, shape, sub, run_len, parts):
     ge = gpu
     m, n, k = shape
     dt = "f16"
-    print(f"[case] lost waits m={m} n={n} k={k}", flush=True)
+    print(f"[case] lost waits m={m} n={n} k={k} run={run_len}", flush=True)
     A, B, bias, _, _ = inputs.small_case(m, n, k, dt, std=k ** -0.5, std_bias=0.5)
     Ad, Bd, bd = A.cuda(), B.cuda(), bias.cuda()
     D = torch.empty(m, n, dtype=torch.float16, device="cuda")
     ref = torch.empty_like(D)
-    h0 = ge.gemm_epilog_plan(m, n, k, (dt, dt, dt), "RELU_BIAS")
-    with R.env({"GE_SK_SPIN": "0"}):
+    env = {"GE_SK_RUN": run_len} if run_len else {}
+    with R.env(env):
+        h0 = ge.gemm_epilog_plan(m, n, k, (dt, dt, dt), "RELU_BIAS")
+    with R.env({**env, "GE_SK_SPIN": "0"}):
         h1 = ge.gemm_epilog_plan(m, n, k, (dt, dt, dt), "RELU_BIAS")
     try:
-        assert "split" in ge.gemm_epilog_describe(h1), ge.gemm_epilog_describe(h1)
-        assert ge.gemm_epilog_describe(h0) == ge.gemm_epilog_describe(h1)
+        desc = ge.gemm_epilog_describe(h1)
+        assert "split" in desc and ("parts per tile" in desc) == parts, desc
+        assert ge.gemm_epilog_describe(h0) == desc
         run = lambda: ge.gemm_epilog_execute(h1, Ad, Bd, bd, D)
         run()
         torch.cuda.synchronize()
@@ -70,12 +82,12 @@ def test_lost_waits_leave_clean_flags(gpu, shape, tile):
             else:
                 run()                                            # eager, new epoch
             torch.cuda.synchronize()
-            st = tile_states(D, ref, tile, tile)
-            assert "bad" not in st, f"round {i}: a tile holds wrong finite values"
+            st = tile_states(D, ref, *sub)
+            assert "bad" not in st, f"round {i}: a sub-tile holds wrong finite values"
             nan_tiles += st.count("nan")
         lost = ge.gemm_epilog_lost_waits(h1)
-        print(f"[case] lost waits: {lost} (+{lost_before} at capture), NaN tiles {nan_tiles}", flush=True)
-        assert lost >= nan_tiles
+        print(f"[case] lost waits: {lost} (+{lost_before} at capture), NaN sub-tiles {nan_tiles}", flush=True)
+        assert 8 * lost >= nan_tiles
         assert ge.gemm_epilog_lost_waits(h1) == 0            # the count was reset
         assert ge.gemm_epilog_lost_waits(h0) == 0            # the normal plan never lost a wait
         del graph
