@@ -305,6 +305,7 @@ def mfma_probe(ge, iters: int = 20000, workgroups: int = 512, only=None):
     under the power limit. Each case: one warm-up launch, then 5 timed with HIP events.
     `only`: names of the cases to run (all by default)."""
     import torch
+    from gemm_epilogues_epilog_amd import probe as gprobe
     g = torch.Generator(device="cuda").manual_seed(0)
     n = 1 << 19   # 1 MiB of fp16/bf16 values
     makers = {
@@ -321,13 +322,13 @@ def mfma_probe(ge, iters: int = 20000, workgroups: int = 512, only=None):
         if only is not None and name not in only:
             continue
         ops = make().to(torch.float16 if dt == "f16" else torch.bfloat16)
-        ge.gemm_epilog_mfma_probe(ops, dt, iters, workgroups, out)
+        gprobe.gemm_epilog_mfma_probe(ops, dt, iters, workgroups, out)
         torch.cuda.synchronize()
         times = []
         for _ in range(5):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-            ge.gemm_epilog_mfma_probe(ops, dt, iters, workgroups, out)
+            gprobe.gemm_epilog_mfma_probe(ops, dt, iters, workgroups, out)
             e1.record()
             torch.cuda.synchronize()
             times.append(e0.elapsed_time(e1))

@@ -36,7 +36,7 @@ STATUS = {0: "GE_OK", 1: "GE_ERR_INVALID_VALUE", 2: "GE_ERR_NOT_SUPPORTED", 3: "
 NOALLOC_SCRATCH_BYTES = 64 << 20
 EXPORTS = ("gemm_epilog_plan", "gemm_epilog_plan_ex", "gemm_epilog_plan_info", "gemm_epilog_execute",
            "gemm_epilog_execute_noalloc",
-           "gemm_epilog_autotune", "gemm_epilog_mfma_probe", "gemm_epilog_lost_waits", "gemm_epilog_free",
+           "gemm_epilog_autotune", "gemm_epilog_lost_waits", "gemm_epilog_free",
            "gemm_epilog_aux_bytes", "gemm_epilog_workspace_bytes", "gemm_epilog_describe",
            "gemm_epilog_status_string")
 OP_N, OP_T = 0, 1
@@ -86,8 +86,6 @@ def load() -> ctypes.CDLL:
     L.gemm_epilog_execute_noalloc.restype = c_int
     L.gemm_epilog_autotune.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, c_int, ctypes.POINTER(ctypes.c_float)]
     L.gemm_epilog_autotune.restype = c_int
-    L.gemm_epilog_mfma_probe.argtypes = [vp, ctypes.c_size_t, c_int, c_int, c_int, vp, vp]
-    L.gemm_epilog_mfma_probe.restype = c_int
     L.gemm_epilog_lost_waits.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_uint32)]
     L.gemm_epilog_lost_waits.restype = c_int
     L.gemm_epilog_free.argtypes = [vp]
@@ -224,23 +222,6 @@ def gemm_epilog_autotune(handle, A, B, bias=None, D=None, aux=None, bgrad=None, 
     if st != 0:
         raise GemmEpilogError(st, "gemm_epilog_autotune")
     return ms.value
-
-
-def gemm_epilog_mfma_probe(operands, dtype, iters: int, workgroups: int, out, stream=None, check: bool = True):
-    """Enqueue the MFMA-rate probe (include/gemm_epilog_probe.h) on fp16/bf16 operand
-    values: `operands` a device tensor (its bytes are used), `out` a float32 device
-    tensor of workgroups * 256 elements. Flop: workgroups * 16 * iters * 32768."""
-    if stream is None:
-        import torch
-        stream = torch.cuda.current_stream().cuda_stream
-    elif not isinstance(stream, int):
-        stream = stream.cuda_stream
-    nbytes = operands.numel() * operands.element_size()
-    st = load().gemm_epilog_mfma_probe(_ptr(operands), nbytes, _dt(dtype), int(iters), int(workgroups), _ptr(out),
-                                       stream)
-    if check and st != 0:
-        raise GemmEpilogError(st, "gemm_epilog_mfma_probe")
-    return st
 
 
 def gemm_epilog_lost_waits(handle, stream=None) -> int:

@@ -1,8 +1,10 @@
-"""Compile the HIP library libgemm_epilog.so for gfx950 (in-tree, next to this file).
+"""Compile the HIP libraries for gfx950 (in-tree, next to this file).
 
-Each translation unit is compiled in parallel (the HIP units by hipcc, the host-only
-plan arithmetic by g++), then linked into one shared library that exports the C ABI of
-include/gemm_epilog.h.
+libgemm_epilog.so is the epilogue library: each translation unit is compiled in
+parallel (the HIP units by hipcc, the host-only plan arithmetic by g++), then linked
+into one shared library that exports the C ABI of include/gemm_epilog.h.
+libgemm_epilog_probe.so is a measurement aid kept apart from it: the MFMA-rate probe of
+include/gemm_epilog_probe.h, which the benchmark loads.
 """
 import os
 import subprocess
@@ -15,9 +17,10 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libgemm_epilog.so")
+PROBE_LIB = os.path.join(HERE, "libgemm_epilog_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.hip", "probe.hip", "inst_f32.hip", "inst_f16.hip", "inst_bf16.hip",
+SOURCES = ["api.hip", "inst_f32.hip", "inst_f16.hip", "inst_bf16.hip",
            "inst_f16_lay1.hip", "inst_f16_lay2.hip", "inst_f16_lay3.hip",
            "inst_bf16_lay1.hip", "inst_bf16_lay2.hip", "inst_bf16_lay3.hip"]
 
@@ -28,6 +31,8 @@ FLAGS = [
     "-I", INCLUDE, "-I", CSRC,
 ]
 
+
+PROBE_SOURCES = ["probe.hip"]
 
 # Host-only C++ (the plan arithmetic): plain g++, no HIP.
 HOST_SOURCES = ["plan_host.cpp"]
@@ -49,15 +54,22 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
-    os.makedirs(OBJ, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), HOST_SOURCES + SOURCES))
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", LIB + ".tmp"]
+def _link(objs, lib: str, verbose: bool) -> None:
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", lib + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
+    os.replace(lib + ".tmp", lib)
+
+
+def build(verbose: bool = False, jobs: int = 8) -> str:
+    """Build both libraries; return the epilogue library's path."""
+    os.makedirs(OBJ, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), HOST_SOURCES + SOURCES + PROBE_SOURCES))
+    n = len(HOST_SOURCES) + len(SOURCES)
+    _link(objs[:n], LIB, verbose)
+    _link(objs[n:], PROBE_LIB, verbose)
     return LIB
 
 

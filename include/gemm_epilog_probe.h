@@ -1,8 +1,9 @@
 /*
- * gemm_epilog_probe.h - measurement aid of the fused GEMM + epilogue library (gfx950):
+ * gemm_epilog_probe.h - measurement aid for the fused GEMM + epilogue library (gfx950):
  * the rate the matrix cores sustain on given operand values.
  *
- * Not part of the epilogue path. The fused kernels report their throughput as a
+ * Not part of the epilogue path: exported by its own library, libgemm_epilog_probe.so,
+ * which only the benchmark and its tests load. The fused kernels report their throughput as a
  * fraction of the dense fp16/bf16 MFMA peak (256 compute units x 2.4 GHz x 4096 flop
  * per clock). Under the power limit the clock, and so the reachable rate, depends on
  * the operand values. This probe issues nothing but MFMAs on the values it is given,

@@ -8,13 +8,14 @@ import re
 import pytest
 
 import gemm_epilogues_epilog_amd as ge
+from gemm_epilogues_epilog_amd import probe as gprobe
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def declared_functions():
+def declared_functions(header="*.h"):
     names = set()
-    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+    for h in glob.glob(os.path.join(ROOT, "include", header)):
         text = open(h).read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
         for m in re.finditer(r"^[A-Za-z_][\w\s\*]*?\b(gemm_epilog_\w+)\s*\(", text, flags=re.M):
@@ -23,16 +24,23 @@ def declared_functions():
 
 
 def test_header_declares_the_boundary():
-    names = declared_functions()
+    names = declared_functions("gemm_epilog.h")
     for required in ("gemm_epilog_plan", "gemm_epilog_execute", "gemm_epilog_free"):
         assert required in names
     assert set(names) == set(ge.EXPORTS)
+    assert set(declared_functions("gemm_epilog_probe.h")) == set(gprobe.EXPORTS)
+    assert set(declared_functions()) == set(ge.EXPORTS) | set(gprobe.EXPORTS)
 
 
 def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(ge.LIB_PATH)
-    for name in declared_functions():
-        assert hasattr(lib, name), f"{name} is declared in include/ but not exported"
+    for name in declared_functions("gemm_epilog.h"):
+        assert hasattr(lib, name), f"{name} is declared in include/gemm_epilog.h but not exported"
+    # the measurement probe lives in its own library, not in the epilogue library
+    assert not hasattr(lib, "gemm_epilog_mfma_probe")
+    plib = ctypes.CDLL(gprobe.LIB_PATH)
+    for name in declared_functions("gemm_epilog_probe.h"):
+        assert hasattr(plib, name), f"{name} is declared in include/gemm_epilog_probe.h but not exported"
 
 
 def test_aux_bytes():
@@ -146,7 +154,7 @@ def test_product_path_does_not_import_the_oracle():
 
 
 def test_mfma_probe_rejects_bad_arguments_on_host():
-    lib = ge.load()
+    lib = gprobe.load()
     assert lib.gemm_epilog_mfma_probe(None, 64, 1, 10, 1, 16, None) == 3          # NULL operands
     assert lib.gemm_epilog_mfma_probe(16, 64, 1, 10, 1, None, None) == 3          # NULL out
     assert lib.gemm_epilog_mfma_probe(16, 64, 0, 10, 1, 16, None) == 2            # fp32 operands

@@ -4,21 +4,22 @@ finite); its argument errors come back before any launch."""
 import pytest
 import torch
 
+from gemm_epilogues_epilog_amd import probe as gprobe
+
 pytestmark = pytest.mark.gpu
 
 
 def test_mfma_probe_runs_and_writes_every_output(gpu):
-    ge = gpu
     wgs, iters = 8, 16
     out = torch.full((wgs * 256,), float("nan"), dtype=torch.float32, device="cuda")
     zeros = torch.zeros(4096, dtype=torch.float16, device="cuda")
-    ge.gemm_epilog_mfma_probe(zeros, "f16", iters, wgs, out)
+    gprobe.gemm_epilog_mfma_probe(zeros, "f16", iters, wgs, out)
     torch.cuda.synchronize()
     assert bool((out == 0).all())
     g = torch.Generator(device="cuda").manual_seed(0)
     vals = (torch.randn(4096, device="cuda", generator=g) / 64).to(torch.bfloat16)
     out.fill_(float("nan"))
-    ge.gemm_epilog_mfma_probe(vals, "bf16", iters, wgs, out)
+    gprobe.gemm_epilog_mfma_probe(vals, "bf16", iters, wgs, out)
     torch.cuda.synchronize()
     assert bool(torch.isfinite(out).all()) and bool((out != 0).any())
-    assert ge.gemm_epilog_mfma_probe(vals, "f32", iters, wgs, out, check=False) == 2
+    assert gprobe.gemm_epilog_mfma_probe(vals, "f32", iters, wgs, out, check=False) == 2
