@@ -1195,6 +1195,15 @@ __device__ __forceinline__ uint32_t sk_wait_flags(uint32_t* flags, int np, uint3
 
 // Split runs that cover whole tiles (KT a multiple of the run length): the S runs of
 // tail tile t are t S .. t S + S - 1, run s computing k-tiles [s units, (s + 1) units).
+// Workgroup q (each XCD takes a contiguous range of q) runs:
+//   256 x 256 tiles, part-major: q = s T + t over the T tail tiles, so the runs that
+//   share an XCD read A and B over the same k range, and tiles of one m-tile (n-tile)
+//   share their A rows (B columns) in that XCD's L2 (2048 x 2048 x 8192: 3-5% faster
+//   than tile-major);
+//   128 x 128 tiles, tile-major: q = t S + s, so the S runs of a tile share an XCD. The
+//   XCDs start a launch's workgroups up to about 2.5 us apart, and a tile whose runs
+//   sit on several XCDs waits for the latest (1024 x 512 x 2048: 11.6 us tile-major,
+//   14.3 part-major).
 // The tile is finished in S parts, one per run: wave w's sub-tile belongs to run
 // w % S. Every run stores the sub-tiles of its waves that other runs finish, publishes
 // them, waits until all S runs have published, and its own waves add the other runs'
@@ -1211,7 +1220,7 @@ __device__ __forceinline__ uint32_t sk_wait_flags(uint32_t* flags, int np, uint3
 // lost wait or not, and a replayed graph starts from clean counters. A wait that runs
 // out is counted in the flag region's last word and gives NaN for the run's part.
 template <int DT, int EP, int BM, int BN, int WM, int WN, int BK, int STAGES, bool ILV, int CW>
-__device__ __forceinline__ void sk_reduce_scatter(const Args& p, char* smem, int r, int S, uint32_t& lost_any) {
+__device__ __forceinline__ void sk_reduce_scatter(const Args& p, char* smem, int q, int S, uint32_t& lost_any) {
   using C = DtlCfg<BM, BN, WM, WN, BK, STAGES>;
   using PL = PartialLayout<C::MB, C::NB>;
   constexpr int MB = C::MB, NB = C::NB;
@@ -1219,7 +1228,11 @@ __device__ __forceinline__ void sk_reduce_scatter(const Args& p, char* smem, int
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = w % C::WAVES_M, wn = w / C::WAVES_M;
   const size_t slot_bytes = (size_t)C::NW * PL::WAVE_BYTES;
-  const int t = r / S, s = r - t * S;
+  const int T = p.sk_wgs / S;
+  constexpr bool PART_MAJOR = BM >= 256;
+  const int s = PART_MAJOR ? q / T : q % S;
+  const int t = PART_MAJOR ? q - s * T : q / S;
+  const int r = t * S + s;   // the run: its partial slot
   int tm, tn;
   raster(p, p.dp_tiles + t, tm, tn);
 
