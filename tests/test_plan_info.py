@@ -49,6 +49,13 @@ def test_group_of_m_tiles_follows_the_size_of_A():
     assert info(65536, 8192, 16384)["group_m"] == 4   # A of 2 GiB outgrows the 256 MB MALL
 
 
+def test_split_plans_take_groups_of_4():
+    # split runs of one XCD cover fewer tiles: groups of 4 m-tiles share more panels
+    for shape in ((1024, 512, 2048), (1024, 1024, 4096), (2048, 2048, 8192), (8192, 1024, 8192)):
+        r = info(*shape)
+        assert r["split_workgroups"] > 0 and r["group_m"] == 4, (shape, r)
+
+
 def test_workspace():
     assert info(4096, 11008, 4096)["workspace_bytes"] == 0
     # DRELU_BGRAD: one fp32 row sum per row and 64-column wave tile

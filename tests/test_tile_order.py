@@ -4,9 +4,9 @@ Workgroup ids are renumbered so that each of the 8 XCDs walks a contiguous range
 positions (xcd_remap), and positions are laid out in groups of group_m m-tiles, m
 fastest inside a group (raster). The persistent kernel's workgroup w takes ids
 w, w + G, w + 2G, ... This model restates that arithmetic and checks that every
-tile is computed exactly once for every grid the plan can launch, that the tiles
-an XCD runs together form compact blocks (so they share A and B panels in its L2),
-and the plan's choice of group size."""
+tile is computed exactly once for every grid the plan can launch and that the tiles
+an XCD runs together form compact blocks (so they share A and B panels in its L2);
+the plan's choice of group size is read from the plan itself (gemm_epilog_plan_info)."""
 import itertools
 
 import pytest
@@ -24,10 +24,6 @@ def raster(pos, tiles_m, tiles_n, group_m):
     rows = min(tiles_m - first_m, group_m)
     inner = pos - g * gsz
     return first_m + inner % rows, inner // rows
-
-
-def group_m_for(m, k, elem):
-    return 4 if m * k * elem >= 256 * 1024 * 1024 else 8
 
 
 @pytest.mark.parametrize("tiles_m,tiles_n", [(1, 1), (1, 43), (16, 43), (17, 16), (32, 32), (256, 32), (3, 5),
@@ -63,8 +59,17 @@ def test_concurrent_tiles_of_an_xcd_share_panels():
         assert len(ms) <= 8 and len(ns) <= 5, (x, j, ms, ns)
 
 
+def plan_group(m, n, k):
+    """The group size the plan itself chooses (host code of the library, no GPU)."""
+    import gemm_epilogues_epilog_amd as ge
+    return ge.gemm_epilog_plan_info(m, n, k, ("f16", "f16", "f16"), "RELU_BIAS")["group_m"]
+
+
 def test_group_size_rule():
-    assert group_m_for(4096, 4096, 2) == 8          # headline: A is 32 MiB
-    assert group_m_for(8192, 8192, 2) == 8          # 8192 x 8192 x 8192: A is 128 MiB
-    assert group_m_for(65536, 16384, 2) == 4        # 65536 x 8192 x 16384: A is 2 GiB
-    assert group_m_for(16383, 8192, 2) == 8 and group_m_for(16384, 8192, 2) == 4   # A of 256 MiB
+    # whole-tile plans: groups of 8 m-tiles, or 4 once A outgrows the 256 MB MALL
+    assert plan_group(4096, 11008, 4096) == 8       # headline: A is 32 MiB
+    assert plan_group(8192, 8192, 8192) == 8        # A is 128 MiB
+    assert plan_group(65536, 8192, 16384) == 4      # A is 2 GiB
+    assert plan_group(16376, 8192, 8192) == 8 and plan_group(16384, 8192, 8192) == 4   # A of 256 MiB
+    # split plans: groups of 4
+    assert plan_group(1024, 1024, 4096) == 4
