@@ -42,6 +42,9 @@ VARIANTS = {
     "ffn_bias_f16": (None, "BIAS", "f16", False),
     "ffn_none_f16": (None, "NONE", "f16", False),
     "ffn_gelu_bf16": ("ffn_gelu_bf16_4096x11008x4096", "GELU_BIAS", "bf16", False),
+    # the same fused product with B held as its (n, k) transpose (a linear layer's weight
+    # as stored, out x in): every B fragment is then one ds_read_b128
+    "ffn_relu_bias_f16_bt": (None, "RELU_BIAS", "f16", False, "NT"),
     "mlp8192_fwd_aux_bf16": ("mlp_bf16_8192", "RELU_AUX_BIAS", "bf16", True),
     "mlp8192_bwd_drelu_bgrad_bf16": ("mlp_bf16_8192", "DRELU_BGRAD", "bf16", True),
     "large_relu_bias_f16": ("large_f16_65536x8192x16384", "RELU_BIAS", "f16", True),
