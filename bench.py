@@ -528,7 +528,10 @@ def main():
         return
     prop = torch.cuda.get_device_properties(0)
     W = inputs.WORKLOADS[inputs.HEADLINE]
-    log(f"[bench] device {prop.name} {getattr(prop, 'gcnArchName', '')} CUs {prop.multi_processor_count}")
+    from gemm_epilogues_epilog_amd import probe as gprobe
+    dev_cus, dev_mhz = gprobe.gemm_epilog_device_info()
+    log(f"[bench] device {prop.name} {getattr(prop, 'gcnArchName', '')} CUs {prop.multi_processor_count} "
+        f"(runtime: {dev_cus} CUs, peak clock {dev_mhz} MHz)")
     log(f"[bench] headline {W.name}: generating inputs")
     A, B, bias = device_inputs(W, device_rng=False)
     D = torch.empty(W.m, W.n, dtype=A.dtype, device="cuda")
@@ -612,7 +615,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": W.name, "m": W.m, "n": W.n, "k": W.k, "epilog": W.epilog,
                    "accumulate": "f32", "kernel": kernel_desc, "plan_ms": round(plan_ms, 3),
-                   "cus": prop.multi_processor_count, "frac_of_peak": round(value / PEAK_F16_TFLOPS, 4)},
+                   "cus": prop.multi_processor_count, "device_cus": dev_cus, "device_peak_clock_mhz": dev_mhz,
+                   "peak_derivation": "256 CUs x 2.4 GHz x 4096 flop/clk (dense fp16/bf16 MFMA)",
+                   "frac_of_peak": round(value / PEAK_F16_TFLOPS, 4)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_F16_TFLOPS, 4), "traffic": traffic,
                      "kernel_ms_mean": round(r["region_ms_per_launch"], 4), "kernel_launches_timed": args.steps,

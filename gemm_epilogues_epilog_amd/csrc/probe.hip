@@ -65,3 +65,15 @@ extern "C" ge_status_t gemm_epilog_mfma_probe(const void* operands, size_t opera
              ? GE_OK
              : GE_ERR_HIP;
 }
+
+extern "C" ge_status_t gemm_epilog_device_info(int* compute_units, int* clock_khz) {
+  if (!compute_units || !clock_khz) return GE_ERR_NULL_POINTER;
+  int dev = 0, cus = 0, khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipDeviceGetAttribute(&khz, hipDeviceAttributeClockRate, dev) != hipSuccess)
+    return GE_ERR_HIP;
+  *compute_units = cus;
+  *clock_khz = khz;
+  return GE_OK;
+}

@@ -11,7 +11,7 @@ import os
 from . import GemmEpilogError, _dt, _ptr
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgemm_epilog_probe.so")
-EXPORTS = ("gemm_epilog_mfma_probe",)
+EXPORTS = ("gemm_epilog_mfma_probe", "gemm_epilog_device_info")
 
 _lib = None
 
@@ -27,6 +27,8 @@ def load() -> ctypes.CDLL:
     vp, c_int = ctypes.c_void_p, ctypes.c_int
     L.gemm_epilog_mfma_probe.argtypes = [vp, ctypes.c_size_t, c_int, c_int, c_int, vp, vp]
     L.gemm_epilog_mfma_probe.restype = c_int
+    L.gemm_epilog_device_info.argtypes = [ctypes.POINTER(c_int), ctypes.POINTER(c_int)]
+    L.gemm_epilog_device_info.restype = c_int
     _lib = L
     return L
 
@@ -46,3 +48,12 @@ def gemm_epilog_mfma_probe(operands, dtype, iters: int, workgroups: int, out, st
     if check and st != 0:
         raise GemmEpilogError(st, "gemm_epilog_mfma_probe")
     return st
+
+
+def gemm_epilog_device_info():
+    """(compute units, peak shader clock in MHz) of the current device."""
+    cus, khz = ctypes.c_int(0), ctypes.c_int(0)
+    st = load().gemm_epilog_device_info(ctypes.byref(cus), ctypes.byref(khz))
+    if st != 0:
+        raise GemmEpilogError(st, "gemm_epilog_device_info")
+    return cus.value, khz.value / 1000.0

@@ -40,6 +40,15 @@ extern "C" {
 ge_status_t gemm_epilog_mfma_probe(const void* operands, size_t operand_bytes, ge_dtype_t dt, int iters,
                                    int workgroups, float* out, void* stream);
 
+/*
+ * gemm_epilog_device_info - what the current HIP device reports, for stating the peak
+ * the measurements are read against: its compute units and its peak shader clock (kHz;
+ * the clock the dense MFMA peak assumes, not the clock under load).
+ *   compute_units, clock_khz : host pointers, written on success.
+ * Returns GE_ERR_NULL_POINTER for a NULL pointer, GE_ERR_HIP if the runtime cannot answer.
+ */
+ge_status_t gemm_epilog_device_info(int* compute_units, int* clock_khz);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,3 +23,9 @@ def test_mfma_probe_runs_and_writes_every_output(gpu):
     torch.cuda.synchronize()
     assert bool(torch.isfinite(out).all()) and bool((out != 0).any())
     assert gprobe.gemm_epilog_mfma_probe(vals, "f32", iters, wgs, out, check=False) == 2
+
+
+def test_device_info_matches_torch(gpu):
+    cus, mhz = gprobe.gemm_epilog_device_info()
+    assert cus == torch.cuda.get_device_properties(0).multi_processor_count
+    assert 500.0 <= mhz <= 5000.0
