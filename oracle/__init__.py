@@ -20,7 +20,7 @@ _lib = None
 
 DT = {"f32": 0, "f16": 1, "bf16": 2}
 EPILOG = {"NONE": 0, "RELU_BIAS": 1, "GELU_BIAS": 2, "RELU_AUX_BIAS": 3, "DRELU_BGRAD": 4,
-          "BIAS": 5, "RELU_BIAS_UNFUSED": 100}
+          "BIAS": 5, "RELU_BIAS_UNFUSED": 100, "DRELU_BGRAD_UNFUSED": 101}
 _NP = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}
 
 
@@ -37,6 +37,9 @@ def lib():
         L.oracle_gemm_epilog_t.argtypes = [i64, i64, i64, c_int, c_int, c_int, c_int, c_int, c_int,
                                            vp, vp, vp, vp, vp, vp, vp, vp, c_int]
         L.oracle_gemm_epilog_t.restype = c_int
+        L.oracle_gemm_epilog_act_t.argtypes = [i64, i64, i64, c_int, c_int, c_int, c_int, c_int, c_int,
+                                               vp, vp, vp, vp, vp, vp, vp, vp, vp, c_int]
+        L.oracle_gemm_epilog_act_t.restype = c_int
         L.oracle_f16_to_f32.argtypes = [ctypes.c_uint16]
         L.oracle_f16_to_f32.restype = ctypes.c_float
         L.oracle_f32_to_f16.argtypes = [ctypes.c_float]
@@ -105,14 +108,15 @@ def to_f32(a: np.ndarray, dt: str) -> np.ndarray:
 
 
 def gemm_epilog(A, B, epilog, bias=None, mask=None, ab="f16", d=None, vec=None,
-                want_pre=False, nthreads=0, trans_a=False, trans_b=False):
+                want_pre=False, nthreads=0, trans_a=False, trans_b=False, act=None):
     """Compute one epilogue on the CPU.
 
     A: (m,k), B: (k,n) arrays in dtype `ab` (A given as its (k,m) transpose with
     trans_a, B as its (n,k) transpose with trans_b); bias: (m,) in `vec` (forward
-    epilogs); mask: uint32 (ceil(m/32), n) words, read by DRELU_BGRAD.
+    epilogs); mask: uint32 (ceil(m/32), n) words, read by DRELU_BGRAD; act: the
+    (m,n) forward activation in `d`, read by DRELU_BGRAD_UNFUSED.
     Returns a dict with "D" (m,n) in `d`, and as applicable "mask", "bgrad",
-    "pre" (fp32 pre-activation, or dz for DRELU_BGRAD) and "absum" (sum_j |dz|).
+    "pre" (fp32 pre-activation, or dz for the backward) and "absum" (sum_j |dz|).
     """
     d = d or ab
     vec = vec or d
@@ -136,9 +140,14 @@ def gemm_epilog(A, B, epilog, bias=None, mask=None, ab="f16", d=None, vec=None,
     elif epilog == "DRELU_BGRAD":
         aux = np.ascontiguousarray(mask, dtype=np.uint32)
         assert aux.shape == ((m + 31) // 32, n), "mask shape must be (ceil(m/32), n)"
+    if epilog == "DRELU_BGRAD_UNFUSED":
+        act = np.ascontiguousarray(act, dtype=_NP[d])
+        assert act.shape == (m, n), "the activation must be (m, n)"
+    else:
+        act = None
     bgrad = None
     absum = None
-    if epilog == "DRELU_BGRAD":
+    if epilog in ("DRELU_BGRAD", "DRELU_BGRAD_UNFUSED"):
         bgrad = np.empty(m, _NP[vec])
         absum = np.empty(m, np.float64)
         out["bgrad"] = bgrad
@@ -146,9 +155,9 @@ def gemm_epilog(A, B, epilog, bias=None, mask=None, ab="f16", d=None, vec=None,
     pre = np.empty((m, n), np.float32) if want_pre else None
     if want_pre:
         out["pre"] = pre
-    rc = lib().oracle_gemm_epilog_t(m, n, k, DT[ab], DT[d], DT[vec], ep, int(bool(trans_a)), int(bool(trans_b)),
-                                    _ptr(A), _ptr(B), _ptr(bias), _ptr(D), _ptr(aux), _ptr(bgrad), _ptr(pre),
-                                    _ptr(absum), int(nthreads))
+    rc = lib().oracle_gemm_epilog_act_t(m, n, k, DT[ab], DT[d], DT[vec], ep, int(bool(trans_a)),
+                                        int(bool(trans_b)), _ptr(A), _ptr(B), _ptr(bias), _ptr(act), _ptr(D),
+                                        _ptr(aux), _ptr(bgrad), _ptr(pre), _ptr(absum), int(nthreads))
     if rc != 0:
         raise ValueError("oracle rejected the arguments")
     return out

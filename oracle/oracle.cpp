@@ -26,8 +26,9 @@
 //    the columns of every row.
 //  * "Operator fusion in AI inference compilers: implementation and trade-offs"
 //    (mqxn.cn), section 2.2 diagram: the unfused chain MatMul -> T1 -> BiasAdd ->
-//    T2 -> ReLU; section 2.3 / 4.3: fusion must give the same result up to the
-//    order of the floating-point reduction, with FP32 accumulation.
+//    T2 -> ReLU, each operator its own kernel with its output written to memory;
+//    section 2.3 / 4.3: fusion must give the same result up to the order of the
+//    floating-point reduction, with FP32 accumulation.
 //
 // Readings where the pages are silent (each is also listed with the design notes):
 //  * mask layout: uint32 words [ceil(m/32)][n]; bit (i % 32) of word (i/32, j) is
@@ -39,6 +40,11 @@
 //  * DRELU_BGRAD: dz = bit ? acc : +0; D = round(dz); bgrad[i] = round_vec(sum_j
 //    dz[i,j]) with the sum taken in double over ascending j.
 //  * unfused chain: T1 = round_d(acc); T2 = round_d(T1 + bias); D = max(T2, 0).
+//  * unfused backward chain (the three steps DRELU_BGRAD does in one call, each as its
+//    own kernel as in the diagram above): T1 = round_d(acc); D = act > 0 ? T1 : +0,
+//    where act is the forward pass's stored activation (D's type; the unfused forward
+//    keeps its ReLU output, not a bit mask); bgrad[i] = round_vec(sum_j D[i,j]) with
+//    the sum of the stored D values taken in double over ascending j.
 //
 // Operand storage order ("Fusing epilogs with matrix multiplication using
 // nvmath-python", section on the DRELU_BGRAD path, second paragraph: the backward's
@@ -65,7 +71,7 @@ namespace {
 enum { ODT_F32 = 0, ODT_F16 = 1, ODT_BF16 = 2 };
 // epilogue codes of this file's C interface (chosen to match the library's public enum).
 enum { OEP_NONE = 0, OEP_RELU_BIAS = 1, OEP_GELU_BIAS = 2, OEP_RELU_AUX_BIAS = 3,
-       OEP_DRELU_BGRAD = 4, OEP_BIAS = 5, OEP_RELU_BIAS_UNFUSED = 100 };
+       OEP_DRELU_BGRAD = 4, OEP_BIAS = 5, OEP_RELU_BIAS_UNFUSED = 100, OEP_DRELU_BGRAD_UNFUSED = 101 };
 
 inline uint32_t f32_bits(float x) { uint32_t u; std::memcpy(&u, &x, 4); return u; }
 inline float bits_f32(uint32_t u) { float x; std::memcpy(&x, &u, 4); return x; }
@@ -155,9 +161,10 @@ struct Problem {
   const void* bias;       // m values in vec_dt (forward epilogs with a bias)
   void* D;                // m x n in d_dt
   uint32_t* aux;          // mask words: written for RELU_AUX_BIAS, read for DRELU_BGRAD
-  void* bgrad;            // m values in vec_dt (DRELU_BGRAD)
-  float* pre_out;         // optional m x n: pre-activation (or dz for DRELU_BGRAD)
-  double* absum_out;      // optional m: sum_j |dz[i,j]| (DRELU_BGRAD)
+  void* bgrad;            // m values in vec_dt (DRELU_BGRAD, DRELU_BGRAD_UNFUSED)
+  const void* act;        // m x n in d_dt: the forward activation (DRELU_BGRAD_UNFUSED)
+  float* pre_out;         // optional m x n: pre-activation (or dz for the backward)
+  double* absum_out;      // optional m: sum_j |dz[i,j]| (the backward)
 };
 
 // Rows [r0, r1) of the result. r0 is a multiple of 32 so mask words are owned by
@@ -196,8 +203,8 @@ void compute_rows(const Problem& P, int64_t r0, int64_t r1) {
       // epilogue, element by element
       for (int64_t ii = 0; ii < ib; ++ii) {
         const int64_t i = i0 + ii;
-        const float bias_i =
-            (P.epilog == OEP_NONE || P.epilog == OEP_DRELU_BGRAD) ? 0.0f : load_elem(P.bias, P.vec_dt, i);
+        const bool backward = P.epilog == OEP_DRELU_BGRAD || P.epilog == OEP_DRELU_BGRAD_UNFUSED;
+        const float bias_i = (P.epilog == OEP_NONE || backward) ? 0.0f : load_elem(P.bias, P.vec_dt, i);
         for (int64_t jj = 0; jj < jb; ++jj) {
           const int64_t j = j0 + jj;
           const float a = acc[(size_t)(ii * JB + jj)];
@@ -246,11 +253,22 @@ void compute_rows(const Problem& P, int64_t r0, int64_t r1) {
               if (P.pre_out) P.pre_out[o] = t2;
               break;
             }
+            case OEP_DRELU_BGRAD_UNFUSED: {
+              // GEMM -> T1 (rounded to D's type), then T1 kept where the stored forward
+              // activation is positive; the row sums read those stored values
+              const float t1 = round_through(P.d_dt, a);
+              const float dz = load_elem(P.act, P.d_dt, o) > 0.0f ? t1 : 0.0f;
+              store_elem(P.D, P.d_dt, o, dz);
+              if (P.pre_out) P.pre_out[o] = dz;
+              rowsum[(size_t)ii] += (double)dz;
+              rowabs[(size_t)ii] += std::fabs((double)dz);
+              break;
+            }
           }
         }
       }
     }
-    if (P.epilog == OEP_DRELU_BGRAD) {
+    if (P.epilog == OEP_DRELU_BGRAD || P.epilog == OEP_DRELU_BGRAD_UNFUSED) {
       for (int64_t ii = 0; ii < ib; ++ii) {
         store_elem(P.bgrad, P.vec_dt, i0 + ii, (float)rowsum[(size_t)ii]);
         if (P.absum_out) P.absum_out[i0 + ii] = rowabs[(size_t)ii];
@@ -285,20 +303,24 @@ void oracle_bf16_to_f32_n(const uint16_t* x, float* y, int64_t n) { for (int64_t
 
 // Full computation on host memory. A (m,k) (or (k,m) with trans_a), B (k,n) (or
 // (n,k) with trans_b), D (m,n), all row-major; bias and bgrad hold m values; aux
-// holds ceil(m/32)*n words. Returns 0 on success, -1 on an invalid argument.
+// holds ceil(m/32)*n words; act holds the (m,n) forward activation in d_dt, read by
+// DRELU_BGRAD_UNFUSED only. Returns 0 on success, -1 on an invalid argument.
 // nthreads <= 0 picks min(hardware threads, 16) or $ORACLE_THREADS.
-int oracle_gemm_epilog_t(int64_t m, int64_t n, int64_t k, int ab_dt, int d_dt, int vec_dt, int epilog,
-                         int trans_a, int trans_b, const void* A, const void* B, const void* bias, void* D,
-                         uint32_t* aux, void* bgrad, float* pre_out, double* absum_out, int nthreads) {
+int oracle_gemm_epilog_act_t(int64_t m, int64_t n, int64_t k, int ab_dt, int d_dt, int vec_dt, int epilog,
+                             int trans_a, int trans_b, const void* A, const void* B, const void* bias,
+                             const void* act, void* D, uint32_t* aux, void* bgrad, float* pre_out,
+                             double* absum_out, int nthreads) {
   if (m < 1 || n < 1 || k < 1) return -1;
   if (ab_dt < 0 || ab_dt > 2 || d_dt < 0 || d_dt > 2 || vec_dt < 0 || vec_dt > 2) return -1;
   const bool uses_bias = epilog == OEP_BIAS || epilog == OEP_RELU_BIAS || epilog == OEP_GELU_BIAS ||
                          epilog == OEP_RELU_AUX_BIAS || epilog == OEP_RELU_BIAS_UNFUSED;
-  if (!(uses_bias || epilog == OEP_NONE || epilog == OEP_DRELU_BGRAD)) return -1;
+  if (!(uses_bias || epilog == OEP_NONE || epilog == OEP_DRELU_BGRAD || epilog == OEP_DRELU_BGRAD_UNFUSED))
+    return -1;
   if (!A || !B || !D) return -1;
   if (uses_bias && !bias) return -1;
   if ((epilog == OEP_RELU_AUX_BIAS || epilog == OEP_DRELU_BGRAD) && !aux) return -1;
-  if (epilog == OEP_DRELU_BGRAD && !bgrad) return -1;
+  if ((epilog == OEP_DRELU_BGRAD || epilog == OEP_DRELU_BGRAD_UNFUSED) && !bgrad) return -1;
+  if (epilog == OEP_DRELU_BGRAD_UNFUSED && !act) return -1;
 
   // O0: widen the operands exactly, into a (m,k) and b (k,n)
   std::vector<float> Aw((size_t)(m * k)), Bw((size_t)(k * n));
@@ -309,7 +331,7 @@ int oracle_gemm_epilog_t(int64_t m, int64_t n, int64_t k, int ab_dt, int d_dt, i
     for (int64_t j = 0; j < n; ++j)
       Bw[(size_t)(kk * n + j)] = load_elem(B, ab_dt, trans_b ? j * k + kk : kk * n + j);
 
-  Problem P{m, n, k, ab_dt, d_dt, vec_dt, epilog, Aw.data(), Bw.data(), bias, D, aux, bgrad, pre_out, absum_out};
+  Problem P{m, n, k, ab_dt, d_dt, vec_dt, epilog, Aw.data(), Bw.data(), bias, D, aux, bgrad, act, pre_out, absum_out};
   if (epilog == OEP_RELU_AUX_BIAS && (m % 32) != 0) {
     // pad bits of the last group are zero: clear that group up front
     std::fill(aux + (m / 32) * n, aux + (m / 32 + 1) * n, 0u);
@@ -327,6 +349,14 @@ int oracle_gemm_epilog_t(int64_t m, int64_t n, int64_t k, int ab_dt, int d_dt, i
   }
   for (auto& th : pool) th.join();
   return 0;
+}
+
+// Without the activation argument (every epilogue but DRELU_BGRAD_UNFUSED).
+int oracle_gemm_epilog_t(int64_t m, int64_t n, int64_t k, int ab_dt, int d_dt, int vec_dt, int epilog,
+                         int trans_a, int trans_b, const void* A, const void* B, const void* bias, void* D,
+                         uint32_t* aux, void* bgrad, float* pre_out, double* absum_out, int nthreads) {
+  return oracle_gemm_epilog_act_t(m, n, k, ab_dt, d_dt, vec_dt, epilog, trans_a, trans_b, A, B, bias, nullptr, D,
+                                  aux, bgrad, pre_out, absum_out, nthreads);
 }
 
 // Both operands stored as in the product: A (m,k), B (k,n).

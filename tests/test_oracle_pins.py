@@ -196,6 +196,37 @@ def test_unfused_chain_rounds_its_intermediate(dt):
         assert not np.array_equal(f["D"].view(np.uint16), u["D"].view(np.uint16))
 
 
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+def test_unfused_backward_rounds_its_intermediate(dt):
+    """The unfused backward chain rounds the product to D's type before the mask is
+    applied and sums the stored values; the fused DRELU_BGRAD sums the fp32 product.
+    Hand-worked values in tests/golden/unfused_backward_rounding.json: with an fp32
+    bias type the two bias gradients differ in the 16-bit types by 2 e^2 per row.
+    Dropping T1's rounding, or summing before it, gives the fused value and fails."""
+    fx = json.load(open(os.path.join(GOLDEN, "unfused_backward_rounding.json")))
+    case = fx["cases"][dt]
+    m, n, k = fx["m"], fx["n"], fx["k"]
+    cast = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dt]
+    x = torch.tensor(case["x"], dtype=torch.float64).to(cast)
+    if dt != "f32":
+        assert int(x.view(torch.int16)) == case["x_bits"]
+    A = np_of(x.repeat(m, k), dt)
+    B = np_of(x.repeat(k, n), dt)
+    act = np_of(torch.tensor(fx["act"], dtype=torch.float64).to(cast), dt)
+    u = oracle.gemm_epilog(A, B, "DRELU_BGRAD_UNFUSED", act=act, ab=dt, vec="f32")
+    mask = pack_mask_np(np.array(fx["act"]) > 0)
+    f = oracle.gemm_epilog(A, B, "DRELU_BGRAD", mask=mask, ab=dt, vec="f32")
+    assert np.array_equal(u["bgrad"], np.array(case["unfused_bgrad_f32"], np.float32))
+    assert np.array_equal(f["bgrad"], np.array(case["fused_bgrad_f32"], np.float32))
+    if dt == "f32":
+        assert np.array_equal(u["D"], np.array(case["D"], np.float32))
+    else:
+        assert np.array_equal(u["D"].view(np.uint16), np.array(case["D_bits"], np.uint16))
+        assert np.array_equal(f["D"].view(np.uint16), u["D"].view(np.uint16))
+        assert not np.array_equal(u["bgrad"], f["bgrad"])
+    assert not np.signbit(oracle.to_f32(u["D"], dt)).any()
+
+
 def test_mask_layout_fixture():
     fx = json.load(open(os.path.join(GOLDEN, "mask_layout_40x3.json")))
     m, n, k = fx["m"], fx["n"], fx["k"]
@@ -245,6 +276,45 @@ def test_integer_exact_backward(dt, shape):
     assert np.array_equal(w(o["D"]), dz)
     assert np.array_equal(w(o["bgrad"]), dz.sum(axis=1))      # sum over n: one value per row
     assert np.array_equal(o["absum"], np.abs(dz).sum(axis=1))
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("shape", SHAPES)
+def test_integer_exact_backward_unfused(dt, shape):
+    """Integer operands and the forward's ReLU output as the activation: every value is
+    exact, so D = (act > 0) ? A2 B2 : 0 and bgrad = its row sums, both in float64."""
+    m, n, k = shape
+    A, B, bias, A2, B2 = inputs.integer_case(m, n, k, dt)
+    pre = A.double().numpy() @ B.double().numpy() + bias.double().numpy()[:, None]
+    act64 = np.maximum(pre, 0.0)
+    cast = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dt]
+    act = np_of(torch.from_numpy(act64).to(cast), dt)
+    prod = A2.double().numpy() @ B2.double().numpy()
+    dz = np.where(act64 > 0, prod, 0.0)
+    o = oracle.gemm_epilog(np_of(A2, dt), np_of(B2, dt), "DRELU_BGRAD_UNFUSED", act=act, ab=dt)
+    w = lambda a: oracle.to_f32(a, dt).astype(np.float64)
+    assert np.array_equal(w(o["D"]), dz)
+    assert np.array_equal(w(o["bgrad"]), dz.sum(axis=1))
+    assert np.array_equal(o["absum"], np.abs(dz).sum(axis=1))
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_unfused_backward_sums_the_stored_values(dt):
+    """Random operands: D equals the fused DRELU_BGRAD's D under the mask packed from
+    act > 0 (rounding the kept product once either way), and the fp32 bias gradient is
+    the float64 row sum of the stored D, which is exact for 16-bit values at this n."""
+    m, n, k = 72, 48, 40
+    A, B, bias, A2, B2 = inputs.small_case(m, n, k, dt)
+    fw = oracle.gemm_epilog(np_of(A, dt), np_of(B, dt), "RELU_BIAS", bias=np_of(bias, dt), ab=dt)
+    act = fw["D"]
+    pos = oracle.to_f32(act, dt) > 0
+    assert 0 < pos.mean() < 1
+    u = oracle.gemm_epilog(np_of(A2, dt), np_of(B2, dt), "DRELU_BGRAD_UNFUSED", act=act, ab=dt, vec="f32")
+    f = oracle.gemm_epilog(np_of(A2, dt), np_of(B2, dt), "DRELU_BGRAD", mask=pack_mask_np(pos), ab=dt, vec="f32")
+    assert np.array_equal(u["D"].view(np.uint16), f["D"].view(np.uint16))
+    ref = oracle.to_f32(u["D"], dt).astype(np.float64).sum(axis=1).astype(np.float32)
+    assert np.array_equal(u["bgrad"], ref)
+    assert not np.array_equal(u["bgrad"], f["bgrad"])
 
 
 @pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
