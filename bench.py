@@ -47,6 +47,9 @@ VARIANTS = {
     "ffn_relu_bias_f16_bt": (None, "RELU_BIAS", "f16", False, "NT"),
     "mlp8192_fwd_aux_bf16": ("mlp_bf16_8192", "RELU_AUX_BIAS", "bf16", True),
     "mlp8192_bwd_drelu_bgrad_bf16": ("mlp_bf16_8192", "DRELU_BGRAD", "bf16", True),
+    # its unfused baseline: GEMM -> T1, ReLU backward against the forward activation,
+    # row sums for bgrad, each a kernel of its own
+    "mlp8192_bwd_unfused_bf16": ("mlp_bf16_8192", "DRELU_BGRAD_UNFUSED", "bf16", True),
     "large_relu_bias_f16": ("large_f16_65536x8192x16384", "RELU_BIAS", "f16", True),
     "large_aux_f16": ("large_f16_65536x8192x16384", "RELU_AUX_BIAS", "f16", True),
     "small_relu_bias_f16": ("relu_bias_f16_1024x512x2048", "RELU_BIAS", "f16", False),
@@ -243,6 +246,15 @@ def run_variant(ge, W, epilog, dtype, steps, warmup, device_rng, layout="NN", co
         torch.cuda.synchronize()
         ge.gemm_epilog_free(hf)
         bias = None
+    if epilog == "DRELU_BGRAD_UNFUSED":
+        bg = torch.empty(m, dtype=A.dtype, device="cuda")
+        # a realistic activation: the unfused forward pass of the same inputs
+        aux = torch.empty(m, n, dtype=A.dtype, device="cuda")
+        hf = ge.gemm_epilog_plan(m, n, k, (dtype, dtype, dtype), "RELU_BIAS_UNFUSED")
+        ge.gemm_epilog_execute(hf, A, B, bias, aux, None, None)
+        torch.cuda.synchronize()
+        ge.gemm_epilog_free(hf)
+        bias = None
     if ta:   # the same operands in the storage order the plan takes
         A = A.t().contiguous()
     if tb:
@@ -269,14 +281,15 @@ def run_variant(ge, W, epilog, dtype, steps, warmup, device_rng, layout="NN", co
 
 def algorithmic_bytes(m, n, k, dtype, epilog):
     """HBM bytes one execute must move at least: A, B and D once, the bias (or, for
-    DRELU_BGRAD, the mask read and bgrad written), the mask written by RELU_AUX_BIAS, and
-    for the unfused chain its two elementwise kernels' reads and writes of T1 and T2."""
+    DRELU_BGRAD, the mask read and bgrad written), the mask written by RELU_AUX_BIAS, for
+    the unfused chain its two elementwise kernels' reads and writes of T1 and T2, and for
+    the unfused backward T1 written and read, the activation read and D read again."""
     es = 2 if dtype in ("f16", "bf16") else 4
     mask = 4 * ((m + 31) // 32) * n
     byts = es * (m * k + k * n + m * n + m)
     if epilog in ("RELU_AUX_BIAS", "DRELU_BGRAD"):
         byts += mask
-    if epilog == "RELU_BIAS_UNFUSED":
+    if epilog in ("RELU_BIAS_UNFUSED", "DRELU_BGRAD_UNFUSED"):
         byts += 4 * m * n * es
     return byts
 
@@ -373,11 +386,12 @@ def run_autotune(ge, W, steps: int, warmup: int, repeats: int = 20):
             "search_best_ms": round(best, 4), "search_wall_ms": round(search_ms, 1), "repeats": repeats}
 
 
-def run_mlp_step(steps: int, warmup: int, size: int = 8192, dtype: str = "bf16"):
+def run_mlp_step(steps: int, warmup: int, size: int = 8192, dtype: str = "bf16", fused: bool = True):
     """One training step of the two-layer perceptron (batch, input, hidden and output
     all `size`): RELU_AUX_BIAS and NONE forward, then dW2 = dY H^T, the DRELU_BGRAD
     product W2^T dY with db1, and dW1 = dZ1 X^T, five executes per step. Inputs drawn
-    on the device with the distributions of gemm_epilogues_epilog_amd.inputs.mlp_case."""
+    on the device with the distributions of gemm_epilogues_epilog_amd.inputs.mlp_case.
+    fused=False runs the unfused baselines in place of RELU_AUX_BIAS and DRELU_BGRAD."""
     import torch
     from gemm_epilogues_epilog_amd import inputs
     from gemm_epilogues_epilog_amd.mlp import MLP2Step
@@ -390,7 +404,7 @@ def run_mlp_step(steps: int, warmup: int, size: int = 8192, dtype: str = "bf16")
     W2 = (torch.randn(n, n, device="cuda", generator=g) * n ** -0.5).to(t)
     dY = torch.randn(n, n, device="cuda", generator=g).to(t)
     t0 = time.perf_counter()
-    st = MLP2Step(n, n, n, n, dtype)
+    st = MLP2Step(n, n, n, n, dtype, fused=fused)
     plan_ms = (time.perf_counter() - t0) * 1e3
     for _ in range(warmup):
         st.step(X, W1, b1, W2, dY)
@@ -414,8 +428,9 @@ def run_mlp_step(steps: int, warmup: int, size: int = 8192, dtype: str = "bf16")
     del X, W1, b1, W2, dY, st
     torch.cuda.empty_cache()
     med = per[len(per) // 2]
+    fwd, bwd = ("RELU_AUX_BIAS", "DRELU_BGRAD") if fused else ("RELU_BIAS_UNFUSED", "DRELU_BGRAD_UNFUSED")
     return {"what": f"2-layer MLP training step, batch = input = hidden = output = {n}, {dtype}: "
-                    "RELU_AUX_BIAS, NONE; dW2 (B^T), DRELU_BGRAD + db1 (A^T), dW1 (B^T)",
+                    f"{fwd}, NONE; dW2 (B^T), {bwd} + db1 (A^T), dW1 (B^T)",
             "plan_ms": round(plan_ms, 3), "wall_ms_per_step": round(wall_ms, 4), "median_ms": round(med, 4),
             "p10_ms": round(per[len(per) // 10], 4), "p90_ms": round(per[(len(per) * 9) // 10], 4),
             "tflops": round(flops / (wall_ms * 1e-3) / 1e12, 1), "kernels": kernels}
@@ -493,7 +508,8 @@ def main():
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run the 1 GiB copy that calibrates the HBM byte counters")
     ap.add_argument("--only", choices=sorted(VARIANTS) + sorted(COLD_VARIANTS) +
-                    ["mlp8192_train_step_bf16", "autotune_small", "autotune_headline", "launch_floor"],
+                    ["mlp8192_train_step_bf16", "mlp8192_train_step_bf16_unfused", "autotune_small",
+                     "autotune_headline", "launch_floor"],
                     help="time one variant alone (--steps executes after --warmup) and print its line; "
                          "for profiling runs")
     args = ap.parse_args()
@@ -522,8 +538,9 @@ def main():
     if args.only == "launch_floor":
         print(json.dumps({"variant": args.only, **launch_floor()}), flush=True)
         return
-    if args.only == "mlp8192_train_step_bf16":
-        print(json.dumps({"variant": args.only, **run_mlp_step(args.steps, args.warmup)}), flush=True)
+    if args.only in ("mlp8192_train_step_bf16", "mlp8192_train_step_bf16_unfused"):
+        r = run_mlp_step(args.steps, args.warmup, fused=not args.only.endswith("_unfused"))
+        print(json.dumps({"variant": args.only, **r}), flush=True)
         return
     if args.only:
         cold = args.only in COLD_VARIANTS
@@ -580,6 +597,10 @@ def main():
         sq_f, sq_u = variants["square4096_relu_bias_f16"]["median_ms"], variants["square4096_unfused_f16"]["median_ms"]
         variants["square4096_fusion_saving"] = {"fused_ms": sq_f, "unfused_ms": sq_u,
                                                 "saving_frac": round(1 - sq_f / sq_u, 4)}
+        bw_f = variants["mlp8192_bwd_drelu_bgrad_bf16"]["median_ms"]
+        bw_u = variants["mlp8192_bwd_unfused_bf16"]["median_ms"]
+        variants["mlp8192_bwd_fusion_saving"] = {"fused_ms": bw_f, "unfused_ms": bw_u,
+                                                 "saving_frac": round(1 - bw_f / bw_u, 4)}
         for name, base in COLD_VARIANTS.items():
             wname, ep, dt, dev_rng, *lay = VARIANTS[base]
             Wv = inputs.WORKLOADS[inputs.HEADLINE if wname is None else wname]
@@ -592,9 +613,14 @@ def main():
             log(f"[bench]   {variants[f'autotune_{wname}']}")
         variants["launch_floor"] = launch_floor()
         log(f"[bench] launch floor {variants['launch_floor']}")
-        log("[bench] variant mlp8192_train_step_bf16")
-        variants["mlp8192_train_step_bf16"] = run_mlp_step(vsteps, vwarm)
-        log(f"[bench]   {variants['mlp8192_train_step_bf16']}")
+        for name, fused in (("mlp8192_train_step_bf16", True), ("mlp8192_train_step_bf16_unfused", False)):
+            log(f"[bench] variant {name}")
+            variants[name] = run_mlp_step(vsteps, vwarm, fused=fused)
+            log(f"[bench]   {variants[name]}")
+        st_f = variants["mlp8192_train_step_bf16"]["median_ms"]
+        st_u = variants["mlp8192_train_step_bf16_unfused"]["median_ms"]
+        variants["mlp8192_step_fusion_saving"] = {"fused_ms": st_f, "unfused_ms": st_u,
+                                                  "saving_frac": round(1 - st_f / st_u, 4)}
 
     del A, B, D
     torch.cuda.empty_cache()

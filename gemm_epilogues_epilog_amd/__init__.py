@@ -16,7 +16,8 @@ manager that the nvmath-python pages describe ("Fusing bias addition via the
 nvmath-python epilog mechanism", paragraph 4, lifecycle item; "Dissecting
 nvmath-python", paragraph on the plan-execute-free lifecycle). Its execute returns
 D, (D, {"relu_aux": mask}) for RELU_AUX_BIAS, or (D, {"drelu_bgrad": bgrad}) for
-DRELU_BGRAD, as the pages' auxiliary outputs ("Fusing epilogs with matrix
+DRELU_BGRAD (and its unfused baseline, which takes the forward activation as `act`),
+as the pages' auxiliary outputs ("Fusing epilogs with matrix
 multiplication using nvmath-python", sections on the forward epilogs and on the
 DRELU_BGRAD path).
 """
@@ -30,7 +31,7 @@ LIB_PATH = os.path.join(_HERE, "libgemm_epilog.so")
 F32, F16, BF16 = 0, 1, 2
 DTYPES = {"f32": F32, "f16": F16, "bf16": BF16}
 EPILOG = {"NONE": 0, "RELU_BIAS": 1, "GELU_BIAS": 2, "RELU_AUX_BIAS": 3, "DRELU_BGRAD": 4, "BIAS": 5,
-          "RELU_BIAS_UNFUSED": 100}
+          "RELU_BIAS_UNFUSED": 100, "DRELU_BGRAD_UNFUSED": 101}
 STATUS = {0: "GE_OK", 1: "GE_ERR_INVALID_VALUE", 2: "GE_ERR_NOT_SUPPORTED", 3: "GE_ERR_NULL_POINTER",
           4: "GE_ERR_MISALIGNED", 5: "GE_ERR_ALLOC", 6: "GE_ERR_HIP", 7: "GE_ERR_SCRATCH"}
 NOALLOC_SCRATCH_BYTES = 64 << 20
@@ -279,6 +280,7 @@ class Matmul:
     mm = Matmul(m, n, k, "f16", "RELU_BIAS"); mm.plan(); D = mm.execute(A, B, bias); mm.free()
     or `with Matmul(...) as mm:` which plans on entry and frees on exit.
     trans_a=True takes A as its (k, m) transpose, trans_b=True B as its (n, k) transpose.
+    DRELU_BGRAD_UNFUSED takes the forward pass's (m, n) activation as `act`.
     """
 
     def __init__(self, m: int, n: int, k: int, dtype: str, epilog: str, vec_dtype: Optional[str] = None,
@@ -302,7 +304,7 @@ class Matmul:
     def describe(self) -> str:
         return gemm_epilog_describe(self.handle) if self.handle is not None else ""
 
-    def _outputs(self, A, B, bias, relu_aux, out, bgrad):
+    def _outputs(self, A, B, bias, relu_aux, out, bgrad, act=None):
         """Check the operands and every tensor given against the plan, then plan (once)
         and allocate the outputs not given."""
         import torch
@@ -329,13 +331,17 @@ class Matmul:
             _require(bgrad, "bgrad", self.vec_dtype, self.m, dev)
         if self.epilog == "DRELU_BGRAD" and relu_aux is None:
             raise ValueError("DRELU_BGRAD needs the relu_aux mask of the forward pass")
+        if self.epilog == "DRELU_BGRAD_UNFUSED":
+            if act is None:
+                raise ValueError("DRELU_BGRAD_UNFUSED needs the forward activation as act")
+            _require(act, "act", self.dtype, self.m * self.n, dev)
         if self.handle is None:
             self.plan()
         if out is None:
             out = torch.empty((self.m, self.n), dtype=A.dtype, device=dev)
         if self.epilog == "RELU_AUX_BIAS" and relu_aux is None:
             relu_aux = torch.empty((aux_words, self.n), dtype=torch.int32, device=dev)
-        if self.epilog == "DRELU_BGRAD" and bgrad is None:
+        if self.epilog in ("DRELU_BGRAD", "DRELU_BGRAD_UNFUSED") and bgrad is None:
             vt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[self.vec_dtype]
             bgrad = torch.empty(self.m, dtype=vt, device=dev)
         return relu_aux, out, bgrad
@@ -343,21 +349,24 @@ class Matmul:
     def _result(self, out, relu_aux, bgrad):
         if self.epilog == "RELU_AUX_BIAS":
             return out, {"relu_aux": relu_aux}
-        if self.epilog == "DRELU_BGRAD":
+        if self.epilog in ("DRELU_BGRAD", "DRELU_BGRAD_UNFUSED"):
             return out, {"drelu_bgrad": bgrad}
         return out
 
-    def execute(self, A, B, bias=None, relu_aux=None, out=None, bgrad=None, stream=None):
-        relu_aux, out, bgrad = self._outputs(A, B, bias, relu_aux, out, bgrad)
-        gemm_epilog_execute(self.handle, A, B, bias, out, relu_aux, bgrad, stream)
+    def execute(self, A, B, bias=None, relu_aux=None, out=None, bgrad=None, stream=None, act=None):
+        relu_aux, out, bgrad = self._outputs(A, B, bias, relu_aux, out, bgrad, act)
+        aux = act if self.epilog == "DRELU_BGRAD_UNFUSED" else relu_aux
+        gemm_epilog_execute(self.handle, A, B, bias, out, aux, bgrad, stream)
         return self._result(out, relu_aux, bgrad)
 
-    def autotune(self, A, B, bias=None, relu_aux=None, out=None, bgrad=None, stream=None, repeats: int = 10):
+    def autotune(self, A, B, bias=None, relu_aux=None, out=None, bgrad=None, stream=None, repeats: int = 10,
+                 act=None):
         """Time the candidate configurations on these operands and keep the fastest in
         the plan (gemm_epilog_autotune). Returns (ms per execute, the result as
         execute returns it)."""
-        relu_aux, out, bgrad = self._outputs(A, B, bias, relu_aux, out, bgrad)
-        ms = gemm_epilog_autotune(self.handle, A, B, bias, out, relu_aux, bgrad, stream, repeats)
+        relu_aux, out, bgrad = self._outputs(A, B, bias, relu_aux, out, bgrad, act)
+        aux = act if self.epilog == "DRELU_BGRAD_UNFUSED" else relu_aux
+        ms = gemm_epilog_autotune(self.handle, A, B, bias, out, aux, bgrad, stream, repeats)
         return ms, self._result(out, relu_aux, bgrad)
 
     def free(self):

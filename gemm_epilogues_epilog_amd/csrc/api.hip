@@ -58,6 +58,11 @@ hipError_t clear_now(void* p, size_t bytes) {
   return e != hipSuccess ? e : d;
 }
 
+static_assert((int)gek::NONE == GE_EPILOG_NONE && (int)gek::RELU_BIAS == GE_EPILOG_RELU_BIAS &&
+                  (int)gek::GELU_BIAS == GE_EPILOG_GELU_BIAS && (int)gek::RELU_AUX_BIAS == GE_EPILOG_RELU_AUX_BIAS &&
+                  (int)gek::DRELU_BGRAD == GE_EPILOG_DRELU_BGRAD && (int)gek::BIAS == GE_EPILOG_BIAS,
+              "the kernels' epilogue codes are the public ones");
+
 gek::LaunchFn lookup(ge_dtype_t ab, int ep, int cfg, int lay) {
   if (lay != 0 && !gek::cfg_has_layouts(cfg)) return nullptr;
   switch (ab) {
@@ -89,8 +94,7 @@ ge_status_t build_plan(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt, ge_epilo
   geh::Layout L;
   if (ge_status_t st = geh::make_layout(m, n, k, dt, ep, lay, cus, cfg, allow_split, allow_persist, &L); st != GE_OK)
     return st;
-  const int kernel_ep = ep == GE_EPILOG_RELU_BIAS_UNFUSED ? (int)gek::NONE : (int)ep;
-  gek::LaunchFn fn = lookup(dt.ab, kernel_ep, cfg, lay);
+  gek::LaunchFn fn = lookup(dt.ab, geh::gemm_epilog_of(ep), cfg, lay);
   if (!fn) return GE_ERR_NOT_SUPPORTED;
   ge_plan* h = new (std::nothrow) ge_plan();
   if (!h) return GE_ERR_ALLOC;
@@ -143,7 +147,7 @@ ge_status_t enqueue(const ge_plan& h, char* ws, uint32_t epoch, const void* A, c
   void* t1 = ws + L.off_t1;
   void* t2 = ws + L.off_t2;
   float* partial = reinterpret_cast<float*>(ws + L.off_partial);
-  a.D = h.ep == GE_EPILOG_RELU_BIAS_UNFUSED ? t1 : D;
+  a.D = geh::is_unfused(h.ep) ? t1 : D;
   a.aux = static_cast<uint32_t*>(aux);
   a.partial = h.ep == GE_EPILOG_DRELU_BGRAD ? partial : nullptr;
   a.m = h.m;
@@ -168,6 +172,9 @@ ge_status_t enqueue(const ge_plan& h, char* ws, uint32_t epoch, const void* A, c
   } else if (h.ep == GE_EPILOG_RELU_BIAS_UNFUSED) {
     if (gek::launch_bias_add((int)h.dt.d, t1, bias, (int)h.dt.vec, t2, h.m, h.n, s) != hipSuccess) return GE_ERR_HIP;
     if (gek::launch_relu((int)h.dt.d, t2, D, h.m, h.n, s) != hipSuccess) return GE_ERR_HIP;
+  } else if (h.ep == GE_EPILOG_DRELU_BGRAD_UNFUSED) {
+    if (gek::launch_drelu((int)h.dt.d, t1, aux, D, h.m, h.n, s) != hipSuccess) return GE_ERR_HIP;
+    if (gek::launch_row_sum((int)h.dt.d, D, h.m, h.n, bgrad, (int)h.dt.vec, s) != hipSuccess) return GE_ERR_HIP;
   }
   return GE_OK;
 }
@@ -407,7 +414,7 @@ ge_status_t gemm_epilog_execute_noalloc(int64_t m, int64_t n, int64_t k, ge_dtyp
   h.device = dev;
   h.cus = cus;
   h.L = L;
-  h.gemm = lookup(dt.ab, ep == GE_EPILOG_RELU_BIAS_UNFUSED ? (int)gek::NONE : (int)ep, cfg, lay);
+  h.gemm = lookup(dt.ab, geh::gemm_epilog_of(ep), cfg, lay);
   if (!h.gemm) return GE_ERR_NOT_SUPPORTED;
   h.ws = ws;
   h.spin_limit = kSkSpinDefault;
@@ -500,6 +507,26 @@ hipError_t launch_relu(int dt, const void* in, void* out, int64_t m, int n, hipS
   const void* fn = dt == F32 ? reinterpret_cast<const void*>(&relu_kernel<F32>)
                  : dt == F16 ? reinterpret_cast<const void*>(&relu_kernel<F16>)
                              : reinterpret_cast<const void*>(&relu_kernel<BF16>);
+  return hipLaunchKernel(fn, grid, dim3(256), params, 0, s);
+}
+
+hipError_t launch_drelu(int dt, const void* in, const void* act, void* out, int64_t m, int n, hipStream_t s) {
+  const int E = dt == F32 ? 4 : 8;
+  const int64_t chunks = m * (int64_t)n / E;
+  const dim3 grid((unsigned)((chunks + 255) / 256));
+  void* params[] = {&in, &act, &out, const_cast<int64_t*>(&chunks)};
+  const void* fn = dt == F32 ? reinterpret_cast<const void*>(&drelu_kernel<F32>)
+                 : dt == F16 ? reinterpret_cast<const void*>(&drelu_kernel<F16>)
+                             : reinterpret_cast<const void*>(&drelu_kernel<BF16>);
+  return hipLaunchKernel(fn, grid, dim3(256), params, 0, s);
+}
+
+hipError_t launch_row_sum(int dt, const void* in, int64_t m, int n, void* bgrad, int vec_dt, hipStream_t s) {
+  const dim3 grid((unsigned)((m + 3) / 4));
+  void* params[] = {&in, &m, &n, &bgrad, &vec_dt};
+  const void* fn = dt == F32 ? reinterpret_cast<const void*>(&row_sum_kernel<F32>)
+                 : dt == F16 ? reinterpret_cast<const void*>(&row_sum_kernel<F16>)
+                             : reinterpret_cast<const void*>(&row_sum_kernel<BF16>);
   return hipLaunchKernel(fn, grid, dim3(256), params, 0, s);
 }
 

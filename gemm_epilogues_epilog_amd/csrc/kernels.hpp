@@ -442,4 +442,71 @@ __global__ __launch_bounds__(256) void relu_kernel(const void* __restrict__ in, 
   static_cast<i32x4*>(out)[c] = o;
 }
 
+// ---- unfused backward baseline, kernels 2 and 3 ---------------------------------
+// D = T1 where the forward activation is > 0, else +0 (the ReLU backward as its own
+// kernel, reading the activation the unfused forward stored), 16 bytes per thread.
+template <int DT>
+__global__ __launch_bounds__(256) void drelu_kernel(const void* __restrict__ in, const void* __restrict__ act,
+                                                    void* __restrict__ out, int64_t chunks) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= chunks) return;
+  const i32x4 v = static_cast<const i32x4*>(in)[c];
+  const i32x4 a = static_cast<const i32x4*>(act)[c];
+  i32x4 o;
+  if constexpr (DT == F32) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = __int_as_float(a[e]) > 0.0f ? v[e] : 0;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t u = (uint32_t)a[e];
+      const uint32_t keep_lo = Tr<DT>::widen((uint16_t)(u & 0xffffu)) > 0.0f ? 0x0000ffffu : 0u;
+      const uint32_t keep_hi = Tr<DT>::widen((uint16_t)(u >> 16)) > 0.0f ? 0xffff0000u : 0u;
+      o[e] = (int)((uint32_t)v[e] & (keep_lo | keep_hi));
+    }
+  }
+  static_cast<i32x4*>(out)[c] = o;
+}
+
+// bgrad[row] = the sum of the row's n stored values, one wave per row: lane l adds the
+// 16-byte chunks l, l + 64, l + 128, ... in ascending order (kRowSumBatch loads in
+// flight), then the lanes' sums are added by a fixed butterfly, so results repeat bit
+// for bit.
+constexpr int kRowSumBatch = 4;
+template <int DT>
+__global__ __launch_bounds__(256) void row_sum_kernel(const void* __restrict__ in, int64_t m, int n,
+                                                      void* __restrict__ bgrad, int vec_dt) {
+  constexpr int E = Tr<DT>::E;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= m) return;
+  const int chunks = n / E;
+  const i32x4* p = static_cast<const i32x4*>(in) + row * chunks;
+  float s = 0.0f;
+  for (int c0 = lane; c0 < chunks; c0 += 64 * kRowSumBatch) {
+    i32x4 v[kRowSumBatch];
+#pragma unroll
+    for (int u = 0; u < kRowSumBatch; ++u) {
+      const int c = c0 + 64 * u;
+      v[u] = c < chunks ? p[c] : i32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < kRowSumBatch; ++u) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (DT == F32) {
+          s += __int_as_float(v[u][e]);
+        } else {
+          const uint32_t w = (uint32_t)v[u][e];
+          s += Tr<DT>::widen((uint16_t)(w & 0xffffu));
+          s += Tr<DT>::widen((uint16_t)(w >> 16));
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) s += __shfl_xor(s, off);
+  if (lane == 0) store_vec(bgrad, vec_dt, row, s);
+}
+
 }  // namespace gek

@@ -136,10 +136,12 @@ LaunchFn get_launch_bf16_lay1(int ep, int cfg);
 LaunchFn get_launch_bf16_lay2(int ep, int cfg);
 LaunchFn get_launch_bf16_lay3(int ep, int cfg);
 
-// Elementwise kernels of the unfused chain and the bgrad second pass.
+// Elementwise kernels of the unfused chains and the bgrad second pass.
 hipError_t launch_bias_add(int dt, const void* in, const void* bias, int vec_dt, void* out, int64_t m, int n,
                            hipStream_t s);
 hipError_t launch_relu(int dt, const void* in, void* out, int64_t m, int n, hipStream_t s);
 hipError_t launch_bgrad_reduce(const float* partial, int t, int64_t m, void* bgrad, int vec_dt, hipStream_t s);
+hipError_t launch_drelu(int dt, const void* in, const void* act, void* out, int64_t m, int n, hipStream_t s);
+hipError_t launch_row_sum(int dt, const void* in, int64_t m, int n, void* bgrad, int vec_dt, hipStream_t s);
 
 }  // namespace gek

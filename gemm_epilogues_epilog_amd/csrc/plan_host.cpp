@@ -25,7 +25,7 @@ bool known_dtype(int d) { return d == GE_F32 || d == GE_F16 || d == GE_BF16; }
 bool known_epilog(int e) {
   return e == GE_EPILOG_NONE || e == GE_EPILOG_RELU_BIAS || e == GE_EPILOG_GELU_BIAS ||
          e == GE_EPILOG_RELU_AUX_BIAS || e == GE_EPILOG_DRELU_BGRAD || e == GE_EPILOG_BIAS ||
-         e == GE_EPILOG_RELU_BIAS_UNFUSED;
+         e == GE_EPILOG_RELU_BIAS_UNFUSED || e == GE_EPILOG_DRELU_BGRAD_UNFUSED;
 }
 
 const char* dt_name(ge_dtype_t d) { return d == GE_F32 ? "f32" : d == GE_F16 ? "f16" : "bf16"; }
@@ -39,6 +39,7 @@ const char* ep_name(ge_epilog_t e) {
     case GE_EPILOG_DRELU_BGRAD: return "DRELU_BGRAD";
     case GE_EPILOG_BIAS: return "BIAS";
     case GE_EPILOG_RELU_BIAS_UNFUSED: return "RELU_BIAS_UNFUSED";
+    case GE_EPILOG_DRELU_BGRAD_UNFUSED: return "DRELU_BGRAD_UNFUSED";
   }
   return "?";
 }
@@ -57,6 +58,10 @@ bool uses_bias(ge_epilog_t e) {
   return e == GE_EPILOG_RELU_BIAS || e == GE_EPILOG_GELU_BIAS || e == GE_EPILOG_RELU_AUX_BIAS ||
          e == GE_EPILOG_BIAS || e == GE_EPILOG_RELU_BIAS_UNFUSED;
 }
+
+bool is_unfused(ge_epilog_t e) { return e == GE_EPILOG_RELU_BIAS_UNFUSED || e == GE_EPILOG_DRELU_BGRAD_UNFUSED; }
+
+int gemm_epilog_of(ge_epilog_t e) { return is_unfused(e) ? (int)GE_EPILOG_NONE : (int)e; }
 
 bool env_off(const char* name) {
   const char* v = std::getenv(name);
@@ -193,7 +198,7 @@ ge_status_t make_layout(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt, ge_epil
     if (k % tc.bk == 0 && kt % tc.stages == 0 && kt >= 2 * tc.stages) L.persist_grid = (int)std::min<int64_t>(tiles, cus);
   }
 
-  // ---- workspace: [split flags][DRELU_BGRAD row sums | unfused T1, T2][split partials] ----
+  // ---- workspace: [split flags][DRELU_BGRAD row sums | unfused T1 (and T2)][split partials] ----
   // The flags (one word per split workgroup, and the count of owner waits that ran out
   // in the region's last word) come first, in a region of fixed size, so their place
   // does not move with the problem: a workspace reused across problems keeps them at 0
@@ -211,6 +216,9 @@ ge_status_t make_layout(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt, ge_epil
     main_bytes = 2 * (size_t)m * (size_t)n * es;
     L.off_t1 = main_off;
     L.off_t2 = main_off + (size_t)m * (size_t)n * es;
+  } else if (ep == GE_EPILOG_DRELU_BGRAD_UNFUSED) {
+    main_bytes = (size_t)m * (size_t)n * es;
+    L.off_t1 = main_off;
   }
   L.off_sk_partial = main_off + align256(main_bytes);
   L.ws_bytes = L.off_sk_partial + (size_t)L.sk_wgs * gek::sk_slot_bytes(tc);
@@ -245,11 +253,11 @@ ge_status_t check_execute_args(ge_epilog_t ep, ge_dtypes_t dt, const void* A, co
     if (!bias) return GE_ERR_NULL_POINTER;
     if (!aligned(bias, vs)) return GE_ERR_MISALIGNED;
   }
-  if (ep == GE_EPILOG_RELU_AUX_BIAS || ep == GE_EPILOG_DRELU_BGRAD) {
+  if (ep == GE_EPILOG_RELU_AUX_BIAS || ep == GE_EPILOG_DRELU_BGRAD || ep == GE_EPILOG_DRELU_BGRAD_UNFUSED) {
     if (!aux) return GE_ERR_NULL_POINTER;
     if (!aligned(aux, 16)) return GE_ERR_MISALIGNED;
   }
-  if (ep == GE_EPILOG_DRELU_BGRAD) {
+  if (ep == GE_EPILOG_DRELU_BGRAD || ep == GE_EPILOG_DRELU_BGRAD_UNFUSED) {
     if (!bgrad) return GE_ERR_NULL_POINTER;
     if (!aligned(bgrad, vs)) return GE_ERR_MISALIGNED;
   }

@@ -40,6 +40,12 @@ struct Layout {
 
 size_t elem_size(ge_dtype_t d);
 bool uses_bias(ge_epilog_t e);
+// The unfused baselines: a product kernel without epilogue into T1, then kernels of
+// their own for the remaining steps.
+bool is_unfused(ge_epilog_t e);
+// The epilogue the product kernel applies (the kernels' codes equal the public enum's):
+// NONE for the unfused baselines, the plan's own otherwise.
+int gemm_epilog_of(ge_epilog_t e);
 
 // The argument rules of gemm_epilog_plan_ex; on GE_OK *lay holds the storage bits.
 ge_status_t check_plan_args(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt, ge_epilog_t ep, ge_op_t op_a,

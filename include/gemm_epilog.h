@@ -90,7 +90,14 @@ typedef enum {
   /* Measurement baseline: three kernels GEMM -> T1, T1 + bias -> T2, max(T2, 0) -> D,
    * with T1 and T2 in D's type held in the plan's workspace ([P5] section 2.2 diagram
    * of the chain before fusion). */
-  GE_EPILOG_RELU_BIAS_UNFUSED = 100
+  GE_EPILOG_RELU_BIAS_UNFUSED = 100,
+  /* Measurement baseline of the backward: the three steps DRELU_BGRAD does in one call
+   * ([P3] section "The DRELU_BGRAD path in the backward pass"), each as its own kernel
+   * as in [P5] section 2.2: GEMM -> T1 in D's type (held in the plan's workspace);
+   * D = T1 where the forward activation in aux is > 0, else +0; bgrad[i] = the sum of
+   * row i of the stored D. The unfused forward writes no bit mask, so aux holds its ReLU
+   * output. No bias input. */
+  GE_EPILOG_DRELU_BGRAD_UNFUSED = 101
 } ge_epilog_t;
 
 typedef enum {
@@ -114,7 +121,8 @@ typedef enum {
  *   ep      : epilogue.
  *   out     : receives the handle; untouched on error.
  * Allocates the workspace on the current device: the per-tile bias-gradient
- * partial sums for DRELU_BGRAD, T1 and T2 for RELU_BIAS_UNFUSED, nothing otherwise.
+ * partial sums for DRELU_BGRAD, T1 and T2 for RELU_BIAS_UNFUSED, T1 for
+ * DRELU_BGRAD_UNFUSED, nothing otherwise.
  * Environment (tuning experiments): GE_TILE=S|M|L|LH|LM|LM4 forces a tile configuration;
  * GE_GROUP_M=g (1..1024) sets how many m-tiles share one group of the tile order;
  * GE_STREAMK=0 keeps a sparse last round of tiles whole instead of splitting its k loop;
@@ -160,8 +168,10 @@ ge_status_t gemm_epilog_plan_ex(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt,
  *   D      : device output (m,n), type dt.d, 16-byte aligned.
  *   aux    : device mask words, gemm_epilog_aux_bytes(m,n) bytes, 16-byte aligned.
  *            Written by RELU_AUX_BIAS, read by DRELU_BGRAD, ignored otherwise.
+ *            For DRELU_BGRAD_UNFUSED instead the forward activation, (m,n) of type
+ *            dt.d, 16-byte aligned, read.
  *   bgrad  : device output, m values of type dt.vec, aligned to its element size.
- *            Written by DRELU_BGRAD, ignored otherwise.
+ *            Written by DRELU_BGRAD and DRELU_BGRAD_UNFUSED, ignored otherwise.
  *   stream : a hipStream_t; NULL means the null stream.
  * Every output element in range is written; nothing outside the stated extents is.
  * Returns GE_ERR_HIP if a launch fails.
@@ -249,7 +259,7 @@ ge_status_t gemm_epilog_lost_waits(ge_handle_t h, void* stream, uint32_t* count)
  * under HIP graph capture, tight serving loops and harnesses that forbid hipMalloc.
  * The plan's decisions are made on the host (as gemm_epilog_plan_info reports them) and
  * the kernels of gemm_epilog_execute run with their workspace (bias-gradient partial
- * sums, the unfused chain's T1 and T2, the split tail's partials and flags) in a static
+ * sums, the unfused chains' T1 and T2, the split tail's partials and flags) in a static
  * device array of GEMM_EPILOG_NOALLOC_SCRATCH_BYTES (64 MiB) per device, which each GPU
  * the library runs on holds until the process ends. No hipMalloc, hipFree or other
  * allocating call is made; the first call on a device takes the array's address once
@@ -258,7 +268,8 @@ ge_status_t gemm_epilog_lost_waits(ge_handle_t h, void* stream, uint32_t* count)
  *   A .. stream : as for gemm_epilog_execute, same rules and errors.
  * Returns GE_ERR_SCRATCH when the workspace does not fit the scratch even without the
  * split tail (e.g. DRELU_BGRAD with ceil(n/64) * m * 4 bytes of partial sums above
- * 64 MiB, or the unfused chain with 2 m n element bytes above it); nothing is launched
+ * 64 MiB, the unfused chain with 2 m n element bytes above it, or the unfused backward
+ * with m n element bytes above it); nothing is launched
  * then. A split tail that does not fit is left out (the tiles run whole).
  * Every call on a device shares that device's array, and the array keeps the last
  * call's contents: calls that overlap on one device (two streams, two threads) race and

@@ -66,9 +66,10 @@ def check_guard(buf, fill, what):
 
 
 def run(ge, epilog, dt, A, B, bias=None, mask=None, vec=None, tile=None, stream=None, repeat=1,
-        trans_a=False, trans_b=False):
-    """A, B, bias, mask: CPU or device tensors; A is (k, m) with trans_a and B is (n, k)
-    with trans_b. Returns numpy outputs + plan description."""
+        trans_a=False, trans_b=False, act=None):
+    """A, B, bias, mask, act: CPU or device tensors; A is (k, m) with trans_a and B is
+    (n, k) with trans_b; act is the (m, n) forward activation DRELU_BGRAD_UNFUSED reads.
+    Returns numpy outputs + plan description."""
     vec = vec or dt
     m, k = A.shape[::-1] if trans_a else A.shape
     n = B.shape[0] if trans_b else B.shape[1]
@@ -90,8 +91,10 @@ def run(ge, epilog, dt, A, B, bias=None, mask=None, vec=None, tile=None, stream=
             aux = aux.view(groups, n)
         elif epilog == "DRELU_BGRAD":
             aux = mask.to("cuda").contiguous()
+        elif epilog == "DRELU_BGRAD_UNFUSED":
+            aux = act.to("cuda").contiguous()
         gbuf = bg = None
-        if epilog == "DRELU_BGRAD":
+        if epilog in ("DRELU_BGRAD", "DRELU_BGRAD_UNFUSED"):
             gbuf, bg = guarded(m, TORCH[vec], float("nan"))
         if stream is not None:
             stream.wait_stream(torch.cuda.current_stream())

@@ -57,6 +57,9 @@ void check_args() {
       {8, 8, 8, dts(GE_F32), GE_EPILOG_RELU_BIAS, 0, 1, GE_ERR_NOT_SUPPORTED},
       {12, 8, 8, f16, GE_EPILOG_RELU_BIAS, 0, 1, GE_OK},
       {33, 8, 8, ge_dtypes_t{GE_BF16, GE_BF16, GE_F32}, GE_EPILOG_DRELU_BGRAD, 0, 0, GE_OK},
+      {33, 8, 8, ge_dtypes_t{GE_BF16, GE_BF16, GE_F32}, GE_EPILOG_DRELU_BGRAD_UNFUSED, 1, 0, GE_ERR_NOT_SUPPORTED},
+      {40, 8, 8, f16, GE_EPILOG_DRELU_BGRAD_UNFUSED, 1, 0, GE_OK},
+      {8, 8, 8, f16, 102, 0, 0, GE_ERR_INVALID_VALUE},
   };
   for (const Case& c : cases) {
     const ge_status_t st =
@@ -78,6 +81,16 @@ void check_args() {
   check(geh::check_execute_args(GE_EPILOG_DRELU_BGRAD, dts(GE_F32), p, p, nullptr, p, p, buf + 2) ==
             GE_ERR_MISALIGNED,
         "exec bgrad misaligned", 0, 0, 0, -1);
+  check(geh::check_execute_args(GE_EPILOG_DRELU_BGRAD_UNFUSED, f16, p, p, nullptr, p, nullptr, p) ==
+            GE_ERR_NULL_POINTER,
+        "exec unfused backward activation null", 0, 0, 0, -1);
+  check(geh::check_execute_args(GE_EPILOG_DRELU_BGRAD_UNFUSED, f16, p, p, nullptr, p, buf + 8, p) == GE_ERR_MISALIGNED,
+        "exec unfused backward activation misaligned", 0, 0, 0, -1);
+  check(geh::check_execute_args(GE_EPILOG_DRELU_BGRAD_UNFUSED, f16, p, p, nullptr, p, p, nullptr) ==
+            GE_ERR_NULL_POINTER,
+        "exec unfused backward bgrad null", 0, 0, 0, -1);
+  check(geh::check_execute_args(GE_EPILOG_DRELU_BGRAD_UNFUSED, f16, p, p, nullptr, p, p, p) == GE_OK,
+        "exec unfused backward ok without a bias", 0, 0, 0, -1);
 }
 
 // The split tail of layout L for K k-tiles, through the kernel's own run arithmetic.
@@ -177,6 +190,7 @@ void check_layout(long long m, long long n, long long k, ge_dtype_t t, ge_epilog
         regions.push_back({L.off_t1, (size_t)m * (size_t)n * es});
         regions.push_back({L.off_t2, (size_t)m * (size_t)n * es});
       }
+      if (ep == GE_EPILOG_DRELU_BGRAD_UNFUSED) regions.push_back({L.off_t1, (size_t)m * (size_t)n * geh::elem_size(t)});
       if (L.sk_wgs) regions.push_back({L.off_sk_partial, (size_t)L.sk_wgs * gek::sk_slot_bytes(tc)});
       for (size_t i = 0; i < regions.size(); ++i) {
         check(regions[i].first % 16 == 0, "region aligned", m, n, k, cfg);
@@ -205,7 +219,8 @@ int main() {
   const long long ms[] = {1, 33, 200, 1024, 1032, 4096, 4352, 8192, 12000, 65536};
   const long long ns[] = {8, 136, 512, 1376, 4096, 11008};
   const long long ks[] = {8, 72, 256, 2048, 4096, 8192};
-  const ge_epilog_t eps[] = {GE_EPILOG_RELU_BIAS, GE_EPILOG_DRELU_BGRAD, GE_EPILOG_RELU_BIAS_UNFUSED};
+  const ge_epilog_t eps[] = {GE_EPILOG_RELU_BIAS, GE_EPILOG_DRELU_BGRAD, GE_EPILOG_RELU_BIAS_UNFUSED,
+                             GE_EPILOG_DRELU_BGRAD_UNFUSED};
   const int cuss[] = {256, 80, 1};
   int cases = 0;
   for (long long m : ms)
@@ -214,7 +229,7 @@ int main() {
         for (ge_epilog_t ep : eps)
           for (int cus : cuss)
             for (ge_dtype_t t : {GE_F16, GE_F32}) {
-              if (ep == GE_EPILOG_RELU_BIAS_UNFUSED && m * n > (1LL << 26)) continue;   // keep the run short
+              if (geh::is_unfused(ep) && m * n > (1LL << 26)) continue;   // keep the run short
               check_layout(m, n, k, t, ep, cus);
               ++cases;
             }

@@ -104,3 +104,20 @@ def test_outputs_operand_shapes_and_devices():
         mm()._outputs(FakeDev((32, 64), torch.float16), B, None, None, None, None)
     with pytest.raises(ValueError, match="same device"):
         mm()._outputs(A, FakeDev((32, 48), torch.float16, device="cuda:1"), None, None, None, None)
+
+
+def test_outputs_unfused_backward_checks():
+    # DRELU_BGRAD_UNFUSED reads the forward activation (m, n) in the plan's type
+    A, B = ops(torch.bfloat16)
+    m = mm("DRELU_BGRAD_UNFUSED", "bf16")
+    with pytest.raises(ValueError, match="act"):
+        m._outputs(A, B, None, None, None, None)                                   # no activation
+    with pytest.raises(ValueError, match="act"):
+        m._outputs(A, B, None, None, None, None, FakeDev((2, 48), torch.int32))    # a mask is not it
+    with pytest.raises(ValueError, match="act"):
+        m._outputs(A, B, None, None, None, None, FakeDev((64, 40), torch.bfloat16))
+    with pytest.raises(ValueError, match="act"):
+        m._outputs(A, B, None, None, None, None, FakeDev((64, 48), torch.float16))
+    with pytest.raises(ValueError, match="bgrad"):
+        m._outputs(A, B, None, None, None, FakeDev((48,), torch.bfloat16), FakeDev((64, 48), torch.bfloat16))
+    assert m.handle is None

@@ -2,8 +2,9 @@
 new operand values written into the captured buffers, with eager work in between, and
 must give the bits of an eager execute of the same plan on the same values. Covers the
 split tail (whose flags carry the frozen epoch of the capture), the persistent kernel,
-DRELU_BGRAD with its second pass, the three-kernel unfused chain, transposed operands
-(one workgroup per tile and persistent) and the four-wave 128 x 128 tile."""
+DRELU_BGRAD with its second pass, the three-kernel unfused chains (forward and
+backward), transposed operands (one workgroup per tile and persistent) and the four-wave
+128 x 128 tile."""
 import numpy as np
 import pytest
 import torch
@@ -19,6 +20,7 @@ CASES = [
     ("bgrad", 1024, 1032, 512, "bf16", "DRELU_BGRAD", False, False, ""),
     ("bgrad split tail", 1024, 512, 2048, "f16", "DRELU_BGRAD", False, False, "split"),
     ("unfused", 512, 520, 256, "f16", "RELU_BIAS_UNFUSED", False, False, ""),
+    ("unfused backward, A transposed", 512, 520, 264, "bf16", "DRELU_BGRAD_UNFUSED", True, False, "op_a T"),
     ("A transposed", 512, 520, 264, "bf16", "RELU_AUX_BIAS", True, False, "op_a T"),
     ("A transposed, persistent", 4096, 4096, 256, "bf16", "RELU_AUX_BIAS", True, False, "persistent"),
     ("B transposed, persistent", 4096, 4096, 256, "f16", "DRELU_BGRAD", False, True, "persistent"),
@@ -41,17 +43,25 @@ def test_graph_replays_match_eager(gpu, case):
     D = torch.empty(m, n, dtype=t, device="cuda")
     groups = (m + 31) // 32
     aux = torch.zeros(groups, n, dtype=torch.int32, device="cuda")
-    bg = torch.empty(m, dtype=t, device="cuda") if ep == "DRELU_BGRAD" else None
+    backward = ep in ("DRELU_BGRAD", "DRELU_BGRAD_UNFUSED")
+    bg = torch.empty(m, dtype=t, device="cuda") if backward else None
     if ep == "DRELU_BGRAD":
         # a mask from a forward of other operands, fixed for every replay
         hf = ge.gemm_epilog_plan(m, n, k, (dt, dt, dt), "RELU_AUX_BIAS")
         ge.gemm_epilog_execute(hf, A.cuda(), Bkn, bd, D, aux, None)
         torch.cuda.synchronize()
         ge.gemm_epilog_free(hf)
+    if ep == "DRELU_BGRAD_UNFUSED":
+        # the activation of an unfused forward of other operands, fixed for every replay
+        aux = torch.empty(m, n, dtype=t, device="cuda")
+        hf = ge.gemm_epilog_plan(m, n, k, (dt, dt, dt), "RELU_BIAS_UNFUSED")
+        ge.gemm_epilog_execute(hf, A.cuda(), Bkn, bd, aux, None, None)
+        torch.cuda.synchronize()
+        ge.gemm_epilog_free(hf)
     h = ge.gemm_epilog_plan_ex(m, n, k, (dt, dt, dt), ep, int(ta), int(tb))
     try:
         assert want in ge.gemm_epilog_describe(h), ge.gemm_epilog_describe(h)
-        use_bias = bd if ep != "DRELU_BGRAD" else None
+        use_bias = None if backward else bd
 
         def operands(i):
             # new values for replay i, written into the captured buffer

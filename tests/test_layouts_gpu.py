@@ -65,6 +65,10 @@ def test_integer_exact_layouts(gpu, dt, lay, tile, shape):
     ob = oracle.gemm_epilog(to_np(A2s), to_np(B2s), "DRELU_BGRAD", mask=o["mask"], ab=dt, **kw)
     assert np.array_equal(gb["D"].view(np.uint8), ob["D"].view(np.uint8)), gb["desc"]
     assert np.array_equal(gb["bgrad"].view(np.uint8), ob["bgrad"].view(np.uint8)), gb["desc"]
+    gu = R.run(gpu, "DRELU_BGRAD_UNFUSED", dt, A2s, B2s, act=g["D_dev"], tile=tile, **kw)
+    ou = oracle.gemm_epilog(to_np(A2s), to_np(B2s), "DRELU_BGRAD_UNFUSED", act=g["D"], ab=dt, **kw)
+    assert np.array_equal(gu["D"].view(np.uint8), ou["D"].view(np.uint8)), gu["desc"]
+    assert np.array_equal(gu["bgrad"].view(np.uint8), ou["bgrad"].view(np.uint8)), gu["desc"]
 
 
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
@@ -95,6 +99,10 @@ def test_random_parity_layouts(gpu, dt, lay, shape):
     ob = oracle.gemm_epilog(to_np(A2s), to_np(B2s), "DRELU_BGRAD", mask=g["mask"].view(np.uint32), ab=dt, **kw)
     assert_close(gb["D"], ob["D"], dt, gb["desc"])
     assert_bgrad(gb["bgrad"], ob["bgrad"], ob["absum"], dt)
+    gu = R.run(gpu, "DRELU_BGRAD_UNFUSED", dt, A2s, B2s, act=g["D_dev"], **kw)
+    ou = oracle.gemm_epilog(to_np(A2s), to_np(B2s), "DRELU_BGRAD_UNFUSED", act=g["D"], ab=dt, **kw)
+    assert_close(gu["D"], ou["D"], dt, gu["desc"])
+    assert_bgrad(gu["bgrad"], ou["bgrad"], ou["absum"], dt)
 
 
 @pytest.mark.parametrize("tile", ["L", "LH", "LM"])

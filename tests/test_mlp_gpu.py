@@ -40,6 +40,33 @@ def test_mlp_step_stage_parity(gpu, dt, dims):
     assert_close(dW1, oracle.gemm_epilog(dZ1, x, "NONE", ab=dt, trans_b=True)["D"], dt, "dW1")
 
 
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("dims", [(72, 136, 40, 264), (520, 264, 136, 1032)])
+def test_mlp_step_unfused_stage_parity(gpu, dt, dims):
+    # the baseline step: the forward's unfused chain keeps H and no mask, the backward's
+    # unfused chain reads H; every stage against the oracle on the inputs it received
+    from gemm_epilogues_epilog_amd.mlp import MLP2Step
+    d, h, o, b = dims
+    print(f"[case] unfused mlp step {dt} d={d} h={h} o={o} batch={b}", flush=True)
+    X, W1, b1, W2, dY = inputs.mlp_case(d, h, o, b, dt)
+    Xd, W1d, b1d, W2d, dYd = (t.cuda() for t in (X, W1, b1, W2, dY))
+    with MLP2Step(d, h, o, b, dt, fused=False) as st:
+        assert st.mask is None
+        assert "RELU_BIAS_UNFUSED" in st.fwd1.describe() and "DRELU_BGRAD_UNFUSED" in st.dz1.describe()
+        g = st.step(Xd, W1d, b1d, W2d, dYd)
+        torch.cuda.synchronize()
+        H, Y = to_np(st.H), to_np(st.Y)
+        dW2, dZ1, db1, dW1 = to_np(g["dW2"]), to_np(g["dZ1"]), to_np(g["db1"]), to_np(g["dW1"])
+    x, w1, bb1, w2, dy = (to_np(t) for t in (X, W1, b1, W2, dY))
+    assert_close(H, oracle.gemm_epilog(w1, x, "RELU_BIAS_UNFUSED", bias=bb1, ab=dt)["D"], dt, "H")
+    assert_close(Y, oracle.gemm_epilog(w2, H, "NONE", ab=dt)["D"], dt, "Y")
+    assert_close(dW2, oracle.gemm_epilog(dy, H, "NONE", ab=dt, trans_b=True)["D"], dt, "dW2")
+    ob = oracle.gemm_epilog(w2, dy, "DRELU_BGRAD_UNFUSED", act=H, ab=dt, trans_a=True)
+    assert_close(dZ1, ob["D"], dt, "dZ1")
+    assert_bgrad(db1, ob["bgrad"], ob["absum"], dt)
+    assert_close(dW1, oracle.gemm_epilog(dZ1, x, "NONE", ab=dt, trans_b=True)["D"], dt, "dW1")
+
+
 def test_mlp_step_rejects_bad_sizes(gpu):
     from gemm_epilogues_epilog_amd.mlp import MLP2Step
     with pytest.raises(ValueError):

@@ -54,6 +54,13 @@ def test_integer_exact_all_epilogues(gpu, dt, tile, shape):
     ob = oracle.gemm_epilog(to_np(A2), to_np(B2), "DRELU_BGRAD", mask=o["mask"], ab=dt)
     assert np.array_equal(gb["D"].view(np.uint8), ob["D"].view(np.uint8)), gb["desc"]
     assert np.array_equal(gb["bgrad"].view(np.uint8), ob["bgrad"].view(np.uint8)), gb["desc"]
+    # the unfused backward against the forward's activation (ReLU output: zeros and
+    # positive half-integers)
+    act = g["D_dev"]
+    gu = R.run(gpu, "DRELU_BGRAD_UNFUSED", dt, A2, B2, act=act, tile=tile)
+    ou = oracle.gemm_epilog(to_np(A2), to_np(B2), "DRELU_BGRAD_UNFUSED", act=g["D"], ab=dt)
+    assert np.array_equal(gu["D"].view(np.uint8), ou["D"].view(np.uint8)), gu["desc"]
+    assert np.array_equal(gu["bgrad"].view(np.uint8), ou["bgrad"].view(np.uint8)), gu["desc"]
 
 
 @pytest.mark.parametrize("dt", DTS)
@@ -70,6 +77,10 @@ def test_integer_exact_fp32_vectors(gpu, dt, shape):
     gb = R.run(gpu, "DRELU_BGRAD", dt, A2, B2, mask=mask, vec="f32")
     ob = oracle.gemm_epilog(to_np(A2), to_np(B2), "DRELU_BGRAD", mask=o["mask"], ab=dt, vec="f32")
     assert np.array_equal(gb["bgrad"], ob["bgrad"])
+    gu = R.run(gpu, "DRELU_BGRAD_UNFUSED", dt, A2, B2, act=g["D_dev"], vec="f32")
+    ou = oracle.gemm_epilog(to_np(A2), to_np(B2), "DRELU_BGRAD_UNFUSED", act=g["D"], ab=dt, vec="f32")
+    assert np.array_equal(gu["D"].view(np.uint8), ou["D"].view(np.uint8))
+    assert np.array_equal(gu["bgrad"], ou["bgrad"])
 
 
 RAND_SHAPES = [(64, 48, 32), (130, 200, 264), (257, 392, 520), (512, 256, 1024)]
@@ -100,6 +111,10 @@ def test_random_parity(gpu, dt, shape):
         ob = oracle.gemm_epilog(to_np(A2), to_np(B2), "DRELU_BGRAD", mask=g["mask"].view(np.uint32), ab=dt)
         assert_close(gb["D"], ob["D"], dt, gb["desc"])
         assert_bgrad(gb["bgrad"], ob["bgrad"], ob["absum"], dt)
+        gu = R.run(gpu, "DRELU_BGRAD_UNFUSED", dt, A2, B2, act=g["D_dev"], tile=tile)
+        ou = oracle.gemm_epilog(to_np(A2), to_np(B2), "DRELU_BGRAD_UNFUSED", act=g["D"], ab=dt)
+        assert_close(gu["D"], ou["D"], dt, gu["desc"])
+        assert_bgrad(gu["bgrad"], ou["bgrad"], ou["absum"], dt)
 
 
 def test_zero_A_closed_form(gpu):

@@ -3,7 +3,7 @@ library's static per-device scratch) against plan + execute, the entry point who
 kernels it shares: the same plan on the same operands must give the same bits. Two and
 more calls in a row share the scratch, the later ones on smaller problems, so what an
 earlier call left there must not leak into a later one: the split tail's flags, the
-bias-gradient partial sums and the unfused chain's intermediates. A problem whose
+bias-gradient partial sums and the unfused chains' intermediates. A problem whose
 workspace exceeds the scratch is refused on the host."""
 import numpy as np
 import pytest
@@ -22,17 +22,20 @@ def outputs(m, n, dt, ep):
     D = torch.full((m, n), float("nan"), dtype=T[dt], device="cuda")
     aux = torch.full(((m + 31) // 32, n), 0x5A5A5A5A, dtype=torch.int32, device="cuda") \
         if ep == "RELU_AUX_BIAS" else None
-    bg = torch.full((m,), float("nan"), dtype=T[dt], device="cuda") if ep == "DRELU_BGRAD" else None
+    bg = torch.full((m,), float("nan"), dtype=T[dt], device="cuda") \
+        if ep in ("DRELU_BGRAD", "DRELU_BGRAD_UNFUSED") else None
     return D, aux, bg
 
 
-def both(ge, m, n, k, dt, ep, A, B, bias=None, mask=None, ta=False, tb=False):
+def both(ge, m, n, k, dt, ep, A, B, bias=None, mask=None, ta=False, tb=False, act=None):
     """(noalloc outputs, plan + execute outputs), each a list of device tensors."""
     res = []
     for noalloc in (True, False):
         D, aux, bg = outputs(m, n, dt, ep)
         if ep == "DRELU_BGRAD":
             aux = mask
+        elif ep == "DRELU_BGRAD_UNFUSED":
+            aux = act
         if noalloc:
             ge.gemm_epilog_execute_noalloc(m, n, k, (dt, dt, dt), ep, A, B, bias, D, aux, bg, int(ta), int(tb))
         else:
@@ -80,6 +83,15 @@ def test_noalloc_matches_plan_and_execute(gpu):
     assert same_bits(na, pe)
     o = oracle.gemm_epilog(to_np(A), to_np(B), "RELU_BIAS_UNFUSED", bias=to_np(bias))
     assert np.array_equal(to_np(na[0]).view(np.uint16), o["D"].view(np.uint16))
+    #    the unfused backward (T1 in the scratch) on that forward's activation
+    _, _, _, A2, B2 = inputs.integer_case(m3, n3, k3, "f16")
+    act = na[0]
+    print(f"[case] noalloc unfused backward f16 {m3}x{n3}x{k3}", flush=True)
+    na, pe = both(ge, m3, n3, k3, "f16", "DRELU_BGRAD_UNFUSED", A2.cuda(), B2.cuda(), act=act)
+    assert same_bits(na, pe)
+    o = oracle.gemm_epilog(to_np(A2), to_np(B2), "DRELU_BGRAD_UNFUSED", act=to_np(act))
+    assert np.array_equal(to_np(na[0]).view(np.uint16), o["D"].view(np.uint16))
+    assert np.array_equal(to_np(na[1]).view(np.uint16), o["bgrad"].view(np.uint16))
     m4, n4, k4 = 128, 136, 72
     A, B, bias, _, _ = inputs.integer_case(m4, n4, k4, "bf16")
     print(f"[case] noalloc A transposed bf16 {m4}x{n4}x{k4}", flush=True)
