@@ -51,7 +51,7 @@ class ge_plan_info_t(ctypes.Structure):
     _fields_ = [("tile_m", ctypes.c_int), ("tile_n", ctypes.c_int), ("tile_k", ctypes.c_int), ("waves", ctypes.c_int),
                 ("tiles", ctypes.c_int64), ("persistent_workgroups", ctypes.c_int), ("whole_tiles", ctypes.c_int),
                 ("split_workgroups", ctypes.c_int), ("split_run_ktiles", ctypes.c_int), ("group_m", ctypes.c_int),
-                ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace_bytes", ctypes.c_size_t), ("stages", ctypes.c_int)]
 
 
 class GemmEpilogError(RuntimeError):

@@ -282,11 +282,12 @@ ge_status_t gemm_epilog_autotune(ge_handle_t h, const void* A, const void* B, co
     cands = {{gek::CFG_S, false, false}, {gek::CFG_M, false, false}};
   } else if (h->L.lay != 0) {
     cands = {{gek::CFG_L, false, true}, {gek::CFG_L, false, false}, {gek::CFG_LH, false, false},
-             {gek::CFG_LM, false, false}};
+             {gek::CFG_LM, false, false}, {gek::CFG_LMD, false, false}};
   } else {
     cands = {{gek::CFG_L, true, true},   {gek::CFG_L, false, true},   {gek::CFG_L, false, false},
              {gek::CFG_LH, true, false}, {gek::CFG_LH, false, false}, {gek::CFG_LM, true, false},
-             {gek::CFG_LM, false, false}, {gek::CFG_LM4, false, false}};
+             {gek::CFG_LM, false, false}, {gek::CFG_LM4, false, false}, {gek::CFG_LMD, true, false},
+             {gek::CFG_LMD, false, false}};
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipEvent_t e0 = nullptr, e1 = nullptr;

@@ -78,6 +78,7 @@ LaunchFn pick_cfg(int cfg) {
       case CFG_LH: return &launch_dtl<DT, EP, 256, 256, 128, 64, 64, 2, LOCKSTEP_HALF>;
       case CFG_LM: return &launch_dtl<DT, EP, 128, 128, 32, 64, 64, 2, LOCKSTEP>;
       case CFG_LM4: return &launch_dtl<DT, EP, 128, 128, 64, 64, 64, 2, LOCKSTEP>;
+      case CFG_LMD: return &launch_dtl<DT, EP, 128, 128, 32, 64, 64, 3, LOCKSTEP>;
       default: break;
     }
   }
@@ -107,6 +108,7 @@ LaunchFn pick_cfg_t(int cfg) {
     case CFG_L: return &launch_dtl<DT, EP, 256, 256, 128, 64, 64, 2, PERSIST, LAY>;
     case CFG_LH: return &launch_dtl<DT, EP, 256, 256, 128, 64, 64, 2, LOCKSTEP_HALF, LAY>;
     case CFG_LM: return &launch_dtl<DT, EP, 128, 128, 32, 64, 64, 2, LOCKSTEP, LAY>;
+    case CFG_LMD: return &launch_dtl<DT, EP, 128, 128, 32, 64, 64, 3, LOCKSTEP, LAY>;
     default: return nullptr;
   }
 }

@@ -59,6 +59,12 @@ bool uses_bias(ge_epilog_t e) {
          e == GE_EPILOG_BIAS || e == GE_EPILOG_RELU_BIAS_UNFUSED;
 }
 
+int64_t split_run_length(int64_t rem, int64_t kt, int cus) {
+  // one run per CU at most, and runs of at least a quarter tile: an owner then adds at
+  // most about four partials
+  return std::max(cdiv(rem * kt, cus), cdiv(kt, 4));
+}
+
 bool is_unfused(ge_epilog_t e) { return e == GE_EPILOG_RELU_BIAS_UNFUSED || e == GE_EPILOG_DRELU_BGRAD_UNFUSED; }
 
 int gemm_epilog_of(ge_epilog_t e) { return is_unfused(e) ? (int)GE_EPILOG_NONE : (int)e; }
@@ -88,16 +94,26 @@ ge_status_t check_plan_args(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt, ge_
   return GE_OK;
 }
 
-// 16-bit types, by the number T of 256 x 256 tiles and of 64-wide k-tiles KT
-// (measured at 4096x2752x4096, 4096x3200x4096, 8192x1024x8192, 2048x2048x8192,
-// 2048x1024x16384, 3072x2560x4096, 4096x1376x4096, 2048^3 and 1024x1024x4096):
+// 16-bit types, by the number T of 256 x 256 tiles, the number TM of 128 x 128 tiles
+// and of 64-wide k-tiles KT (measured at 4096x2752x4096, 4096x3200x4096,
+// 8192x1024x8192, 2048x2048x8192, 2048x1024x16384, 3072x2560x4096, 4096x1376x4096,
+// 2048^3 and 1024x1024x4096, and for LMD at 26 shapes from 1024x512x2048 to
+// 2048x2048x16384, fp16 and bf16, forward and backward, A or B transposed):
 //   T >= CUs:      the 256 x 256 tile;
 //   T > CUs / 2:   still the 256 x 256 tile, one partly filled round (15-18% faster
 //                  than 128 x 128 tiles, which would need more than one round of two
 //                  workgroups per CU);
+//   TM <= CUs:     the 128 x 128 tile with a 3-stage ring (LMD, 96 KB: one workgroup
+//                  per CU, which such a grid has anyway) when each workgroup's k loop is
+//                  long enough for the ring to hide the copies' latency: split runs of
+//                  12 to 64 k-tiles (5-16% faster than the 2-stage ring; 3-51% faster
+//                  than the 256 x 256 split at KT >= 128, which stays 4% ahead with runs
+//                  of 128), or whole tiles of 24 to 127 k-tiles (3-20% faster; at 16-20
+//                  k-tiles it is 1-2% slower, and from 128 on the 256 x 256 split stays
+//                  7% ahead);
 //   KT >= 128:     the 256 x 256 tile with its k loop split across the idle CUs (3-9%
-//                  faster: long runs amortise the partial sums); not for transposed
-//                  operands, whose plans do not split;
+//                  faster than the 2-stage 128 x 128 tile: long runs amortise the partial
+//                  sums); not for transposed operands, whose plans do not split;
 //   otherwise:     the 128 x 128 tile (two workgroups per compute unit), with four
 //                  waves of 64 x 64 (LM4) when its grid fills the CUs without a
 //                  split and KT >= 64 or two workgroups per CU, else eight waves of
@@ -117,13 +133,23 @@ int choose_cfg(int64_t m, int64_t n, int64_t k, ge_dtype_t ab, int cus, int lay)
   if (ab != GE_F32) {
     const int64_t t = tiles(gek::CFG_L);
     const int64_t kt = cdiv(k, gek::kTiles[gek::CFG_L].bk);
-    if (t >= cus || 2 * t > cus || (kt >= 128 && lay == 0)) return gek::CFG_L;
+    if (t >= cus || 2 * t > cus) return gek::CFG_L;
+    const int64_t tm = tiles(gek::CFG_LM);
+    if (tm <= cus) {
+      if (lay == 0 && 2 * tm <= cus && kt >= 2) {   // LMD splits this grid's k loops
+        const int64_t run = split_run_length(tm, kt, cus);
+        if (run >= 12 && run <= 64) return gek::CFG_LMD;
+      } else if (kt >= 24 && (kt < 128 || lay != 0)) {
+        return gek::CFG_LMD;
+      }
+    }
+    if (kt >= 128 && lay == 0) return gek::CFG_L;
     // 128 x 128 tiles: four waves of 64 x 64 (LM4) beat eight of 32 x 64 (LM) by 1-2.4%
     // once the grid fills the CUs and either k spans 64 or more k-tiles or the grid
     // fills two workgroups per CU; LM4 cannot split a sparse grid's k loop (measured at
     // 4096x1376x4096, 3072x2560x4096, 2048x2048x4096, 4096x2048x2048, 2048x4096x6144;
     // LM stays ahead at 2048^3 and 1536x2048x4096)
-    const int64_t tm = tiles(gek::CFG_LM), rem = tm % (2 * (int64_t)cus);
+    const int64_t rem = tm % (2 * (int64_t)cus);
     const bool lm_splits = rem != 0 && 2 * rem <= cus && kt >= 2;
     if (lay == 0 && !lm_splits && tm >= cus && (kt >= 64 || tm >= 2 * (int64_t)cus)) return gek::CFG_LM4;
     return gek::CFG_LM;
@@ -158,14 +184,13 @@ ge_status_t make_layout(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt, ge_epil
   L.dp_tiles = (int)tiles;
   if (gek::cfg_can_split(cfg) && lay == 0 && allow_split) {
     const int64_t kt = cdiv(k, tc.bk);
-    // a round holds one workgroup per CU, two for the 128 x 128 tile (64 KB of LDS): a
+    // a round holds one workgroup per CU, two for the 2-stage 128 x 128 tile (64 KB of LDS): a
     // grid of up to 2 CUs tiles of that size runs in one round and has no sparse tail
     const int64_t slots = cfg == gek::CFG_LM ? 2 * (int64_t)cus : cus;
     const int64_t rem = tiles % slots;
     if (rem != 0 && rem * 2 <= (int64_t)cus && kt >= 2) {
       const int64_t units = rem * kt;
-      // runs of at least a quarter tile: an owner then adds at most about four partials
-      int64_t per = std::max(cdiv(units, cus), cdiv(kt, 4));
+      int64_t per = split_run_length(rem, kt, cus);
       // (experiments: GE_SK_RUN sets the run length, never below one run per compute
       // unit, so every split workgroup is resident at once and every wait ends)
       if (const char* e = std::getenv("GE_SK_RUN")) {
@@ -292,6 +317,7 @@ extern "C" ge_status_t gemm_epilog_plan_info(int64_t m, int64_t n, int64_t k, ge
   r.split_run_ktiles = L.sk_units;
   r.group_m = L.group_m;
   r.workspace_bytes = L.ws_bytes;
+  r.stages = gek::cfg_is_dtl(cfg) ? tc.stages : 0;
   *info = r;
   return GE_OK;
 }

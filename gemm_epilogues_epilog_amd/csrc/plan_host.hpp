@@ -40,6 +40,9 @@ struct Layout {
 
 size_t elem_size(ge_dtype_t d);
 bool uses_bias(ge_epilog_t e);
+// k-tiles per run when `rem` sparse tiles of `kt` k-tiles share `cus` compute units
+// (before the GE_SK_RUN override).
+int64_t split_run_length(int64_t rem, int64_t kt, int cus);
 // The unfused baselines: a product kernel without epilogue into T1, then kernels of
 // their own for the remaining steps.
 bool is_unfused(ge_epilog_t e);

@@ -123,7 +123,7 @@ typedef enum {
  * Allocates the workspace on the current device: the per-tile bias-gradient
  * partial sums for DRELU_BGRAD, T1 and T2 for RELU_BIAS_UNFUSED, T1 for
  * DRELU_BGRAD_UNFUSED, nothing otherwise.
- * Environment (tuning experiments): GE_TILE=S|M|L|LH|LM|LM4 forces a tile configuration;
+ * Environment (tuning experiments): GE_TILE=S|M|L|LH|LM|LM4|LMD forces a tile configuration;
  * GE_GROUP_M=g (1..1024) sets how many m-tiles share one group of the tile order;
  * GE_STREAMK=0 keeps a sparse last round of tiles whole instead of splitting its k loop;
  * GE_SK_RUN=r sets the k-tiles per split run (at least one run per compute unit);
@@ -220,6 +220,7 @@ typedef struct {
   int split_run_ktiles;        /* k-tiles per split workgroup */
   int group_m;                 /* m-tiles per group of the tile order */
   size_t workspace_bytes;      /* device workspace the plan allocates */
+  int stages;                  /* LDS stages of the operand ring (0: register-staged kernel) */
 } ge_plan_info_t;
 
 /*

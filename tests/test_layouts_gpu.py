@@ -4,9 +4,9 @@ dX = W^T . dY with W as stored), B as its (n, k) transpose (the weight gradient
 dW = dZ . X^T with X as stored), or both.
 
 * integer-valued inputs: D, the mask and bgrad equal the oracle bit for bit, for every
-  epilogue but GELU, both 16-bit types, both tiles with layouts (256 x 256 "LH" and
-  128 x 128 "LM"), ragged n, several k-tiles and a ragged k tail (and a ragged m where
-  A is not transposed);
+  epilogue but GELU, both 16-bit types, the tiles with layouts (256 x 256 "LH", 128 x 128
+  "LM" and "LMD", the same tile with a 3-stage ring), ragged n, several k-tiles and a
+  ragged k tail (and a ragged m where A is not transposed);
 * random normal inputs: the fused-epilogue tolerances and the rounding-model ratio;
 * the same tile on the same data gives the same bits whatever the operands' order.
 """
@@ -22,7 +22,7 @@ from tests.helpers import assert_bgrad, assert_close, assert_mask, tight_ratio, 
 pytestmark = pytest.mark.gpu
 
 LAYOUTS = {"TN": (True, False), "NT": (False, True), "TT": (True, True)}
-TILES = [None, "L", "LH", "LM"]
+TILES = [None, "L", "LH", "LM", "LMD"]
 # the last two run the persistent kernel under "L" (k a multiple of 64 over an even number
 # of at least 4 k-tiles); the others fall back to one workgroup per tile
 INT_SHAPES = [(8, 8, 8), (40, 136, 72), (200, 264, 200), (304, 520, 136), (512, 520, 256), (264, 392, 512)]
@@ -105,7 +105,7 @@ def test_random_parity_layouts(gpu, dt, lay, shape):
     assert_bgrad(gu["bgrad"], ou["bgrad"], ou["absum"], dt)
 
 
-@pytest.mark.parametrize("tile", ["L", "LH", "LM"])
+@pytest.mark.parametrize("tile", ["L", "LH", "LM", "LMD"])
 def test_layout_does_not_change_bits(gpu, tile):
     # one tile configuration, one k order: the storage order of the operands only changes
     # how they reach LDS, so the random-input results agree bit for bit (the reference
