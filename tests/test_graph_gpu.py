@@ -3,8 +3,8 @@ new operand values written into the captured buffers, with eager work in between
 must give the bits of an eager execute of the same plan on the same values. Covers the
 split tail (whose flags carry the frozen epoch of the capture), the persistent kernel,
 DRELU_BGRAD with its second pass, the three-kernel unfused chains (forward and
-backward), transposed operands (one workgroup per tile and persistent) and the four-wave
-128 x 128 tile."""
+backward), transposed operands (one workgroup per tile and persistent), the four-wave
+128 x 128 tile and the 3-stage ring of the eight-wave one."""
 import numpy as np
 import pytest
 import torch
@@ -25,6 +25,7 @@ CASES = [
     ("A transposed, persistent", 4096, 4096, 256, "bf16", "RELU_AUX_BIAS", True, False, "persistent"),
     ("B transposed, persistent", 4096, 4096, 256, "f16", "DRELU_BGRAD", False, True, "persistent"),
     ("four-wave 128x128", 4096, 1376, 4096, "f16", "RELU_BIAS", False, False, "waves 2x2"),
+    ("three-stage 128x128, split tail", 1024, 1024, 4096, "f16", "RELU_AUX_BIAS", False, False, "stages 3"),
 ]
 
 

@@ -97,7 +97,15 @@ def test_noalloc_matches_plan_and_execute(gpu):
     print(f"[case] noalloc A transposed bf16 {m4}x{n4}x{k4}", flush=True)
     na, pe = both(ge, m4, n4, k4, "bf16", "RELU_BIAS", A.t().contiguous().cuda(), B.cuda(), bias.cuda(), ta=True)
     assert same_bits(na, pe)
-    # 4. the first shape again (flags left by the earlier calls must be idle)
+    # 4. the 3-stage 128 x 128 ring with its split tail (runs of 16 k-tiles)
+    m5, n5, k5 = 1024, 1024, 4096
+    print(f"[case] noalloc 3-stage split RELU_AUX_BIAS f16 {m5}x{n5}x{k5}", flush=True)
+    info = ge.gemm_epilog_plan_info(m5, n5, k5, ("f16",) * 3, "RELU_AUX_BIAS")
+    assert info["stages"] == 3 and info["split_workgroups"] > 0, info
+    A, B, bias, _, _ = inputs.small_case(m5, n5, k5, "f16", std=k5 ** -0.5, std_bias=0.5, seed=5)
+    na, pe = both(ge, m5, n5, k5, "f16", "RELU_AUX_BIAS", A.cuda(), B.cuda(), bias.cuda())
+    assert same_bits(na, pe)
+    # 5. the first shape again (flags left by the earlier calls must be idle)
     A, B, bias, _, _ = inputs.small_case(m, n, k, "f16", std=k ** -0.5, std_bias=0.5, seed=3)
     na, pe = both(ge, m, n, k, "f16", "RELU_AUX_BIAS", A.cuda(), B.cuda(), bias.cuda())
     assert same_bits(na, pe)
