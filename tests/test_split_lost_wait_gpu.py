@@ -41,7 +41,8 @@ def tile_states(D, ref, bm, bn):
 # (shape, wave sub-tile, forced run length, whether the runs cover whole tiles)
 CASES = [((1024, 512, 2048), (32, 64), None, True),      # 128 x 128 tiles, 4 parts per tile
          ((4352, 4096, 1024), (128, 64), None, True),    # 256 x 256 tiles, 4 parts per tile
-         ((1024, 512, 2048), (32, 64), "12", False)]     # runs of 12 of a tile's 32 k-tiles
+         ((1024, 512, 2048), (32, 64), "12", False),     # runs of 12 of a tile's 32 k-tiles
+         ((1024, 1024, 4096), (32, 64), None, True)]     # the 3-stage 128 x 128 ring, 4 parts per tile
 
 
 @pytest.mark.parametrize("shape,sub,run_len,parts", CASES)
