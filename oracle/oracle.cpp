@@ -52,7 +52,10 @@
 // row-major (k, m) matrix At and a[i,kk] = At[kk,i]; with trans_b the B argument holds
 // the row-major (n, k) matrix Bt and b[kk,j] = Bt[j,kk]. The product is the same sum.
 //
-// Parity unpinned: NaN / Inf propagation and the sign of zero; inputs never hold them.
+// Special values: infinities and NaN in the operands propagate through the products and
+// sums as IEEE arithmetic gives them, ReLU of NaN is +0 with mask bit 0, and D's rounding
+// overflows to +-inf (fp16: from the tie at 65520 on); pinned against float64 elementwise
+// products in the tests. The sign of zero at the ReLU tie is pinned as well.
 //
 // Build: g++ -O3 -march=x86-64-v3 -ffp-contract=off -fno-fast-math -shared -fPIC -pthread
 // -ffp-contract=off keeps every product and every sum individually rounded.

@@ -459,3 +459,82 @@ def test_unfused_within_one_extra_rounding():
 def test_oracle_rejects_bad_arguments():
     with pytest.raises(ValueError):
         oracle.gemm_epilog(np.zeros((2, 2), np.float16), np.zeros((2, 2), np.float16), "RELU_BIAS", bias=None)
+
+
+# ---- special values: infinities, NaN, 16-bit overflow --------------------------------
+
+def special_case(dt):
+    """m = 8 rows, k = 8, n = 8: row 0 holds +inf (every product with a positive B
+    entry is +inf), row 1 -inf, row 2 +inf and -inf (their sum is NaN), row 3 NaN,
+    row 4 +inf against a B row with a zero (inf x 0 = NaN in that column), rows 5-7
+    small integers; B is small positive integers but for one zero. Values exact in
+    every type."""
+    A = np.tile(np.arange(1, 9, dtype=np.float64) % 3 - 1, (8, 1))   # -1, 0, 1 pattern
+    A[0, 2] = np.inf
+    A[1, 5] = -np.inf
+    A[2, 1], A[2, 6] = np.inf, -np.inf
+    A[3, 4] = np.nan
+    A[4, 7] = np.inf
+    B = (np.arange(64, dtype=np.float64).reshape(8, 8) % 4) + 1
+    B[7, 3] = 0.0
+    return A, B
+
+
+def to_dt(x, dt):
+    cast = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dt]
+    return np_of(torch.from_numpy(np.ascontiguousarray(x)).to(cast), dt)
+
+
+def special_reference(A, B):
+    """IEEE float64 elementwise products and their sum per element: for these inputs the
+    class of each result (NaN, +inf, -inf, finite) does not depend on the summation
+    order, and the finite results are small integers."""
+    with np.errstate(invalid="ignore"):
+        return (A[:, :, None] * B[None, :, :]).sum(axis=1)
+
+
+def same_values(got32, ref64):
+    g, r = np.asarray(got32, np.float64), np.asarray(ref64, np.float64)
+    return bool(np.array_equal(np.isnan(g), np.isnan(r)) and np.array_equal(g[~np.isnan(g)], r[~np.isnan(r)]))
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+def test_special_values_propagate(dt):
+    A, B = special_case(dt)
+    bias = np.array([1, -1, 0.5, 2, 0, -3, 4, -0.5])
+    acc = special_reference(A, B)
+    pre = acc + bias[:, None]
+    a, b, c = to_dt(A, dt), to_dt(B, dt), to_dt(bias, dt)
+    w = lambda x: oracle.to_f32(x, dt)
+    assert same_values(w(oracle.gemm_epilog(a, b, "NONE", ab=dt)["D"]), acc)
+    assert same_values(w(oracle.gemm_epilog(a, b, "BIAS", bias=c, ab=dt)["D"]), pre)
+    relu = np.where(pre > 0, pre, 0.0)                       # NaN is not > 0: +0
+    o = oracle.gemm_epilog(a, b, "RELU_AUX_BIAS", bias=c, ab=dt)
+    assert same_values(w(o["D"]), relu) and not np.signbit(w(o["D"])).any()
+    assert np.array_equal(o["mask"], pack_mask_np(pre > 0))
+    # the backward on the same product: dz = bit ? acc : +0, bgrad = its row sums
+    bits = np.zeros((8, 8), bool)
+    bits[:, ::2] = True
+    ob = oracle.gemm_epilog(a, b, "DRELU_BGRAD", mask=pack_mask_np(bits), ab=dt, vec="f32")
+    dz = np.where(bits, acc, 0.0)
+    assert same_values(w(ob["D"]), dz)
+    assert same_values(ob["bgrad"], dz.sum(axis=1))
+    assert [bool(np.isnan(v)) for v in ob["bgrad"]] == [bool(np.isnan(v)) for v in dz.sum(axis=1)]
+
+
+def test_f16_output_overflow():
+    """Finite fp16 operands whose fp32 sums leave fp16's range: RNE gives 65504 up to
+    65519 and +inf from the tie at 65520 on (the largest finite fp16 is 65504, the next
+    step would be 65536); ReLU keeps +inf, and turns -inf into +0."""
+    A = np.array([[32768, 32736, 0], [32768, 32736, 15], [32768, 32752, 0], [32768, 32768, 0],
+                  [-32768, -32768, 0], [32768, 32752, -16], [1, 2, 3], [0, 0, 0]], np.float64)
+    B = np.ones((3, 8))
+    bias = np.array([0, 0, 0, 0, 0, 0, 0, 0], np.float64)
+    want = np.array([65504, 65504, np.inf, np.inf, -np.inf, 65504, 6, 0])
+    a, b, c = A.astype(np.float16), B.astype(np.float16), bias.astype(np.float16)
+    d = oracle.gemm_epilog(a, b, "BIAS", bias=c)["D"].astype(np.float64)
+    assert np.array_equal(d, np.repeat(want[:, None], 8, 1))
+    r = oracle.gemm_epilog(a, b, "RELU_BIAS", bias=c)["D"].astype(np.float64)
+    assert np.array_equal(r, np.repeat(np.maximum(want, 0)[:, None], 8, 1))
+    with np.errstate(over="ignore"):
+        assert np.array_equal(np.float16(65520.0).astype(np.float64), np.inf)   # numpy agrees on the tie
