@@ -538,3 +538,10 @@ def test_f16_output_overflow():
     assert np.array_equal(r, np.repeat(np.maximum(want, 0)[:, None], 8, 1))
     with np.errstate(over="ignore"):
         assert np.array_equal(np.float16(65520.0).astype(np.float64), np.inf)   # numpy agrees on the tie
+
+
+def test_gelu_special_values():
+    # the tanh form as written: 0.5 x (1 + tanh(u)) is +inf at +inf, -inf * 0 = NaN at -inf
+    assert oracle.gelu_tanh(float("inf")) == float("inf")
+    assert math.isnan(oracle.gelu_tanh(float("-inf")))
+    assert math.isnan(oracle.gelu_tanh(float("nan")))

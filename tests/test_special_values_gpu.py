@@ -3,7 +3,8 @@ operands (their products and sums follow IEEE arithmetic: +inf rows, -inf rows, 
 with -inf in one row giving NaN, NaN rows, inf x 0 giving NaN in one column) and fp16
 outputs that overflow (RNE: 65519 -> 65504, the tie 65520 -> +inf). Every epilogue but
 GELU, every tile configuration; NaN positions must agree and every other element, mask
-word and bias gradient must agree bit for bit. The finite values are small integers, so
+word and bias gradient must agree bit for bit. GELU: the same NaN and infinity positions,
+its finite elements within the path's tolerance. The finite values are small integers, so
 no summation order changes them."""
 import numpy as np
 import pytest
@@ -76,6 +77,24 @@ def test_special_values_match_oracle(gpu, dt, tile, shape):
     ob = oracle.gemm_epilog(a, b, "DRELU_BGRAD", mask=o["mask"], ab=dt, vec="f32")
     same(gb["D"], ob["D"], dt)
     same(gb["bgrad"], ob["bgrad"], "f32")
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+def test_gelu_special_values(gpu, dt):
+    # GELU's pre-activations at +inf, -inf and NaN give +inf, NaN and NaN on both sides;
+    # the finite elements keep the path's tolerance
+    from tests.helpers import assert_close
+    m, n, k = 40, 136, 72
+    A, B = special_operands(m, n, k, dt)
+    bias = torch.zeros(m, dtype=TORCH[dt])
+    g = R.run(gpu, "GELU_BIAS", dt, A, B, bias)
+    o = oracle.gemm_epilog(to_np(A), to_np(B), "GELU_BIAS", bias=to_np(bias), ab=dt)
+    gf, of = oracle.to_f32(g["D"], dt), oracle.to_f32(o["D"], dt)
+    assert np.array_equal(np.isnan(gf), np.isnan(of))
+    assert np.array_equal(np.isposinf(gf), np.isposinf(of)) and np.array_equal(np.isneginf(gf), np.isneginf(of))
+    assert np.isposinf(of).any() and np.isnan(of).any()
+    fin = np.isfinite(of)
+    assert_close(np.where(fin, g["D"], 0), np.where(fin, o["D"], 0), dt, "GELU finite elements")
 
 
 @pytest.mark.parametrize("tile", [None, "L", "LH", "LM", "LMD"])
