@@ -54,3 +54,34 @@ def test_relu_tie_bit_exact(gpu, dt, tile, shape):
     assert np.array_equal(bits(gb["D"]), bits(ob["D"])), gb["desc"]
     assert not bits(gb["D"])[ties].any(), "a tie's masked gradient is not +0"
     assert np.array_equal(bits(gb["bgrad"]), bits(ob["bgrad"])), gb["desc"]
+
+
+LAYOUT_CASES = [(dt, lay, tile) for dt in ("f16", "bf16") for lay in ("TN", "NT", "TT")
+                for tile in (None, "L", "LH", "LM", "LMD")]
+
+
+@pytest.mark.parametrize("dt,lay,tile", LAYOUT_CASES)
+def test_relu_tie_bit_exact_transposed(gpu, dt, lay, tile):
+    # the same reading with A given as its (k, m) transpose and/or B as its (n, k) one
+    ta, tb = lay[0] == "T", lay[1] == "T"
+    m, n, k = 304, 392, 256
+    print(f"[case] tie {dt} {lay} tile {tile} m={m} n={n} k={k}", flush=True)
+    A, B, bias, A2, B2 = inputs.integer_tie_case(m, n, k, dt)
+    pre = A.double().numpy() @ B.double().numpy() + bias.double().numpy()[:, None]
+    ties = pre == 0
+    assert ties.sum() > 50, "the case must hold ties"
+    st = lambda t, tr: t.t().contiguous() if tr else t
+    As, Bs, A2s, B2s = st(A, ta), st(B, tb), st(A2, ta), st(B2, tb)
+    kw = dict(trans_a=ta, trans_b=tb)
+    g = R.run(gpu, "RELU_AUX_BIAS", dt, As, Bs, bias, tile=tile, **kw)
+    o = oracle.gemm_epilog(to_np(As), to_np(Bs), "RELU_AUX_BIAS", bias=to_np(bias), ab=dt, **kw)
+    assert np.array_equal(bits(g["D"]), bits(o["D"])), g["desc"]
+    assert not bits(g["D"])[ties].any(), f"a tie gave a nonzero bit pattern (-0?) {g['desc']}"
+    assert np.array_equal(g["mask"].view(np.uint32), o["mask"]), g["desc"]
+    assert not unpack_mask(g["mask"], m)[ties].any(), "a tie has its mask bit set"
+    mask = torch.from_numpy(g["mask"].view(np.int32).copy())
+    gb = R.run(gpu, "DRELU_BGRAD", dt, A2s, B2s, mask=mask, tile=tile, **kw)
+    ob = oracle.gemm_epilog(to_np(A2s), to_np(B2s), "DRELU_BGRAD", mask=g["mask"].view(np.uint32), ab=dt, **kw)
+    assert np.array_equal(bits(gb["D"]), bits(ob["D"])), gb["desc"]
+    assert not bits(gb["D"])[ties].any(), "a tie's masked gradient is not +0"
+    assert np.array_equal(bits(gb["bgrad"]), bits(ob["bgrad"])), gb["desc"]
