@@ -197,11 +197,11 @@ ge_status_t gemm_epilog_execute(ge_handle_t h, const void* A, const void* B, con
  *   best_ms : optional (may be NULL): receives the chosen configuration's mean time per
  *            execute in milliseconds, from HIP events on `stream`.
  * Candidates: for fp32 the 64x64 and 128x128 tiles; for fp16/bf16 with transposed
- * operands the 256x256 and 128x128 lockstep tiles; otherwise the 256x256 tile
- * (persistent, one workgroup per tile, with copies on all or half of the waves) and
- * the 128x128 tile with eight or four waves, each with and without the split tail
- * where it applies. A candidate
- * whose workspace cannot be allocated is skipped. The call synchronises `stream`, must
+ * operands the 256x256 and 128x128 lockstep tiles (the latter with a 2- and a 3-stage
+ * ring); otherwise the 256x256 tile (persistent, one workgroup per tile, with copies on
+ * all or half of the waves) and the 128x128 tile with eight waves (2- or 3-stage ring)
+ * or four, each with and without the split tail where it applies. A candidate whose
+ * workspace cannot be allocated is skipped. The call synchronises `stream`, must
  * not overlap another execute of this plan, and runs on the device current at plan
  * time. On an error the plan keeps its configuration (GE_ERR_HIP if a launch or an
  * event call failed).
