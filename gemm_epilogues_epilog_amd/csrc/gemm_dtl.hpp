@@ -653,7 +653,9 @@ __device__ __forceinline__ void lockstep_tile(const Args& p, char* smem, int64_t
   static_assert(C::KSTEPS % 2 == 0, "every tile starts on fragment buffer 0");
   constexpr int MB = C::MB, NB = C::NB, KS = C::KSTEPS;
   constexpr int NMMA = MB * NB;                          // MFMAs per k-step
-  static_assert(!ILV || F::PIECES <= NMMA, "one fragment read per MFMA");
+  // interleaved reads: `PER` fragment reads after each MFMA (one unless a wave holds
+  // more fragments than it issues MFMAs per k-step, as with three row blocks)
+  constexpr int PER = (F::PIECES + NMMA - 1) / NMMA;
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -728,7 +730,11 @@ __device__ __forceinline__ void lockstep_tile(const Args& p, char* smem, int64_t
         acc[a][b] = Tr<DT>::mma(fr[buf].bfrag(a), fr[buf].a[b], acc[a][b]);
         if constexpr (ILV) {
           if constexpr (LAY == 0) {
-            if (i < F::PIECES && reads) read_piece(op, rbase, rs, i, fr[buf ^ 1]);
+#pragma unroll
+            for (int e = 0; e < PER; ++e) {
+              const int q = i * PER + e;
+              if (q < F::PIECES && reads) read_piece(op, rbase, rs, q, fr[buf ^ 1]);
+            }
           }
         }
         if constexpr (ILV) __builtin_amdgcn_sched_barrier(0);
@@ -975,7 +981,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_persist_ke
   static_assert(DT == F16 || DT == BF16, "16-bit types only");
   static_assert(C::LDS + C::NW * EPI_BYTES <= 160 * 1024, "LDS");
   static_assert(KS % 2 == 0, "every k-tile starts on fragment buffer 0");
-  static_assert(PRE >= 0 && PRE < NMMA && (LAY != 0 || F::PIECES <= NMMA), "MFMA slots");
+  static_assert(PRE >= 0 && PRE < NMMA, "MFMA slots");
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS + C::NW * EPI_BYTES];
 
   const int T = p.tiles_m * p.tiles_n;
@@ -1305,7 +1311,7 @@ __device__ __forceinline__ void sk_reduce_scatter(const Args& p, char* smem, int
     if (!lost) {
       // the other runs' partials of this sub-tile, read at device scope: LOADS loads in
       // flight at a time, QB 4-float groups of each of PB runs
-      constexpr int LOADS = MB * NB <= 2 ? 24 : 16;
+      constexpr int LOADS = MB * NB <= 2 ? 24 : PL::QUADS % 16 == 0 ? 16 : 12;
       constexpr int QB = PL::QUADS < LOADS ? PL::QUADS : LOADS;
       constexpr int PB = LOADS / QB;
       static_assert(PL::QUADS % QB == 0, "load batches");
@@ -1452,7 +1458,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_sk_kernel(
     if (!lost) {
       // LOADS loads in flight at a time: QB 4-float groups of each of PB partials, then
       // the adds, partials in run order (the order of the sums does not depend on PB)
-      constexpr int LOADS = MB * NB <= 2 ? 24 : 16;
+      constexpr int LOADS = MB * NB <= 2 ? 24 : PL::QUADS % 16 == 0 ? 16 : 12;
       constexpr int QB = PL::QUADS < LOADS ? PL::QUADS : LOADS;
       constexpr int PB = LOADS / QB;
       static_assert(PL::QUADS % QB == 0, "load batches");

@@ -79,6 +79,7 @@ LaunchFn pick_cfg(int cfg) {
       case CFG_LM: return &launch_dtl<DT, EP, 128, 128, 32, 64, 64, 2, LOCKSTEP>;
       case CFG_LM4: return &launch_dtl<DT, EP, 128, 128, 64, 64, 64, 2, LOCKSTEP>;
       case CFG_LMD: return &launch_dtl<DT, EP, 128, 128, 32, 64, 64, 3, LOCKSTEP>;
+      case CFG_L3: return &launch_dtl<DT, EP, 192, 256, 96, 64, 64, 2, PERSIST>;
       default: break;
     }
   }

@@ -103,6 +103,15 @@ ge_status_t check_plan_args(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt, ge_
 //   T > CUs / 2:   still the 256 x 256 tile, one partly filled round (15-18% faster
 //                  than 128 x 128 tiles, which would need more than one round of two
 //                  workgroups per CU);
+//                  in both cases the 192 x 256 tile (L3) instead when its T3 tiles take
+//                  no more rounds than T, are more (a fuller last round) and leave no
+//                  last round to split: 0.3-8.8% faster at 4096x2752x4096,
+//                  3072x4096x4096, 6144x4096x4096, 8448x4096x4096 and seven more shapes.
+//                  It loses where it needs more rounds (8192^3 11%, 4096^3 27%), where
+//                  both fill whole rounds (2-3% per flop), and where its last round is
+//                  split into runs that do not divide the k loop (4352x4096x4096: 9-13%).
+//                  The power limit keeps the gain below the CUs' share: a round that
+//                  leaves CUs idle runs at a higher clock;
 //   TM <= CUs:     the 128 x 128 tile with a 3-stage ring (LMD, 96 KB: one workgroup
 //                  per CU, which such a grid has anyway) when each workgroup's k loop is
 //                  long enough for the ring to hide the copies' latency: split runs of
@@ -133,7 +142,13 @@ int choose_cfg(int64_t m, int64_t n, int64_t k, ge_dtype_t ab, int cus, int lay)
   if (ab != GE_F32) {
     const int64_t t = tiles(gek::CFG_L);
     const int64_t kt = cdiv(k, gek::kTiles[gek::CFG_L].bk);
-    if (t >= cus || 2 * t > cus) return gek::CFG_L;
+    if (t >= cus || 2 * t > cus) {
+      const int64_t t3 = tiles(gek::CFG_L3);
+      const int64_t rem3 = t3 % cus;
+      if (lay == 0 && t3 > t && cdiv(t3, cus) <= cdiv(t, cus) && (rem3 == 0 || 2 * rem3 > cus))
+        return gek::CFG_L3;
+      return gek::CFG_L;
+    }
     const int64_t tm = tiles(gek::CFG_LM);
     if (tm <= cus) {
       if (lay == 0 && 2 * tm <= cus && kt >= 2) {   // LMD splits this grid's k loops

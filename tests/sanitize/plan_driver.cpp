@@ -176,7 +176,7 @@ void check_layout(long long m, long long n, long long k, ge_dtype_t t, ge_epilog
       check(L.dp_tiles <= tiles && (L.sk_wgs == 0) == (L.dp_tiles == tiles), "split bookkeeping", m, n, k, cfg);
       if (!split) check(L.sk_wgs == 0, "no split when not allowed", m, n, k, cfg);
       if (L.persist_grid) {
-        check(cfg == gek::CFG_L && L.sk_wgs == 0 && L.persist_grid == (tiles < cus ? tiles : cus), "persistent grid", m,
+        check(gek::cfg_can_persist(cfg) && L.sk_wgs == 0 && L.persist_grid == (tiles < cus ? tiles : cus), "persistent grid", m,
               n, k, cfg);
         check(k % tc.bk == 0 && (k / tc.bk) % tc.stages == 0 && k / tc.bk >= 2 * tc.stages, "persistent k loop", m,
               n, k, cfg);

@@ -14,8 +14,15 @@ def info(m, n, k, lay="NN", ep="RELU_BIAS", dts=F16, cus=256):
 
 @pytest.mark.parametrize("shape,lay,tile,waves,stages,split", [
     ((4096, 11008, 4096), "NN", 256, 8, 2, False),   # the 7B FFN layer: 688 tiles, last round 69% full, not split
-    ((4096, 2752, 4096), "NN", 256, 8, 2, False),    # 176 tiles of 256 x 256: one partly filled round
-    ((4096, 3200, 4096), "NN", 256, 8, 2, False),
+    ((4096, 2752, 4096), "NN", 192, 8, 2, False),    # 176 tiles of 256 x 256 in one round; 242 of 192 x 256
+    ((3072, 4096, 4096), "NN", 192, 8, 2, False),    # 192 tiles of 256 x 256; 256 of 192 x 256: a full round
+    ((6144, 4096, 4096), "NN", 192, 8, 2, False),    # 384 (1.5 rounds) against 512 (2)
+    ((8448, 4096, 4096), "NN", 192, 8, 2, False),    # 528 (2 rounds and a split tail) against 704 (2.75)
+    ((4352, 4096, 4096), "NN", 256, 8, 2, True),     # 368 of 192 x 256 would split a 112-tile last round
+    ((4096, 2752, 4096), "TN", 256, 8, 2, False),    # no 192 x 256 tile for transposed operands
+    ((4096, 3200, 4096), "NN", 256, 8, 2, False),    # 208 tiles; 286 of 192 x 256 would take 2 rounds
+    ((4096, 4096, 4096), "NN", 256, 8, 2, False),
+    ((4096, 2048, 8192), "NN", 256, 8, 2, True),     # half a round: the 256 x 256 split already fills the CUs
     ((8192, 1024, 8192), "NN", 256, 8, 2, True),     # 128 tiles, 128 k-tiles: split k loop
     ((2048, 2048, 8192), "NN", 256, 8, 2, True),     # 256 tiles of 128 x 128 would fill the CUs unsplit
     ((2048, 1024, 16384), "NN", 256, 8, 2, True),    # its 128 x 128 split would run 128 k-tiles per run
@@ -37,7 +44,8 @@ def info(m, n, k, lay="NN", ep="RELU_BIAS", dts=F16, cus=256):
 ])
 def test_tile_rule(shape, lay, tile, waves, stages, split):
     r = info(*shape, lay=lay)
-    assert (r["tile_m"], r["tile_n"], r["waves"], r["stages"]) == (tile, tile, waves, stages), r
+    tile_n = 256 if tile == 192 else tile
+    assert (r["tile_m"], r["tile_n"], r["waves"], r["stages"]) == (tile, tile_n, waves, stages), r
     assert (r["split_workgroups"] > 0) == split, r
 
 
