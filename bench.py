@@ -60,6 +60,7 @@ VARIANTS = {
     # one GPU's share of an 8-way split along n (no exchange in the forward; the backward
     # leaves a partial bgrad of m values for one all-reduce)
     "ffn_shard8_relu_bias_f16": ("ffn_shard8_f16_4096x1376x4096", "RELU_BIAS", "f16", False),
+    "ffn_shard4_relu_bias_f16": ("ffn_shard4_f16_4096x2752x4096", "RELU_BIAS", "f16", False),
     "mlp8192_shard8_bwd_drelu_bgrad_bf16": ("mlp_shard8_bf16_8192x1024x8192", "DRELU_BGRAD", "bf16", True),
     # the square size the epilog-configuration page recommends for comparing fused and
     # unfused latency

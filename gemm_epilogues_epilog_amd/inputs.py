@@ -123,8 +123,11 @@ WORKLOADS: Dict[str, Workload] = {w.name: w for w in [
     _w(name="mlp_bf16_8192", m=8192, n=8192, k=8192, dtype="bf16", epilog="RELU_AUX_BIAS",
        std_a=8192 ** -0.5, std_b=1.0, std_bias=0.02, std_a2=8192 ** -0.5, std_b2=1.0),
     # one GPU's share of an 8-way split along n (the batch columns of B and D): the FFN
-    # layer with n = 11008 / 8, and the 8192 MLP pair with n = 8192 / 8
+    # layer with n = 11008 / 8, and the 8192 MLP pair with n = 8192 / 8; and of a 4-way
+    # split of the FFN layer, n = 11008 / 4
     _w(name="ffn_shard8_f16_4096x1376x4096", m=4096, n=1376, k=4096, dtype="f16", epilog="RELU_BIAS",
+       std_a=1.0 / 64, std_b=1.0 / 64, std_bias=0.02),
+    _w(name="ffn_shard4_f16_4096x2752x4096", m=4096, n=2752, k=4096, dtype="f16", epilog="RELU_BIAS",
        std_a=1.0 / 64, std_b=1.0 / 64, std_bias=0.02),
     _w(name="mlp_shard8_bf16_8192x1024x8192", m=8192, n=1024, k=8192, dtype="bf16", epilog="RELU_AUX_BIAS",
        std_a=8192 ** -0.5, std_b=1.0, std_bias=0.02, std_a2=8192 ** -0.5, std_b2=1.0),

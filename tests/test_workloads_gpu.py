@@ -229,6 +229,18 @@ def test_square_f16_4096_fused_and_unfused(gpu):
     assert_close(gu["D"], gf["D"], "f16", "unfused vs fused")
 
 
+def test_shard4_ffn_on_the_192x256_tile(gpu):
+    # one GPU's share of a 4-way split of the FFN layer, which the plan gives the
+    # 192 x 256 tile (242 tiles in one round instead of 176 of 256 x 256)
+    W = inputs.WORKLOADS["ffn_shard4_f16_4096x2752x4096"]
+    A, B, bias = W.a(), W.b(), W.bias()
+    print(f"[case] {W.name} RELU_BIAS", flush=True)
+    g = R.run(gpu, "RELU_BIAS", "f16", A, B, bias)
+    assert "tile 192x256" in g["desc"] and "persistent" in g["desc"], g["desc"]
+    assert_all_finite(g["D_dev"], "4-way shard D")
+    check_rows(g["D_dev"], W, A, B, bias, sample_groups(W.m, count=4), "RELU_BIAS", "f16")   # the last group lies in the ragged last tile
+
+
 def test_shard8_shapes(gpu):
     # one GPU's share of an 8-way split along n, as the benchmark times it
     W = inputs.WORKLOADS["ffn_shard8_f16_4096x1376x4096"]
