@@ -285,7 +285,8 @@ ge_status_t gemm_epilog_autotune(ge_handle_t h, const void* A, const void* B, co
              {gek::CFG_LM, false, false}, {gek::CFG_LMD, false, false}};
   } else {
     cands = {{gek::CFG_L, true, true},   {gek::CFG_L, false, true},   {gek::CFG_L, false, false},
-             {gek::CFG_L3, true, true},  {gek::CFG_L3, false, true},
+             {gek::CFG_L3, true, true},  {gek::CFG_L3, false, true},  {gek::CFG_LW, true, true},
+             {gek::CFG_LW, false, true},
              {gek::CFG_LH, true, false}, {gek::CFG_LH, false, false}, {gek::CFG_LM, true, false},
              {gek::CFG_LM, false, false}, {gek::CFG_LM4, false, false}, {gek::CFG_LMD, true, false},
              {gek::CFG_LMD, false, false}};

@@ -26,8 +26,10 @@ hipError_t launch_generic(const Args& a, int grid, hipStream_t s) {
 // apply).
 enum Loop { LOCKSTEP = 0, LOCKSTEP_HALF = 1, PERSIST = 2 };
 
-// MFMAs of a k-tile's last step that the persistent loop issues before its barrier.
+// MFMAs of a k-tile's last step that the persistent loop issues before its barrier
+// (half of a k-step's MFMAs for waves with fewer than eight).
 constexpr int kPersistPre = 4;
+constexpr int persist_pre(int nmma) { return kPersistPre < nmma ? kPersistPre : nmma / 2; }
 
 // LAY != 0 (an operand stored transposed): one workgroup per tile, plain lockstep loop.
 template <int DT, int EP, int BM, int BN, int WM, int WN, int BK, int ST, int LOOP, int LAY = 0>
@@ -43,7 +45,8 @@ hipError_t launch_dtl(const Args& a, int grid, hipStream_t s) {
     fn = reinterpret_cast<const void*>(&gemm_dtl_kernel<DT, EP, BM, BN, WM, WN, BK, ST, false, CW, LAY>);
     if constexpr (LOOP == PERSIST) {
       if (a.persist_grid > 0) {
-        fn = reinterpret_cast<const void*>(&gemm_persist_kernel<DT, EP, BM, BN, WM, WN, BK, ST, CW, kPersistPre, LAY>);
+        fn = reinterpret_cast<const void*>(
+            &gemm_persist_kernel<DT, EP, BM, BN, WM, WN, BK, ST, CW, persist_pre((WM / 32) * (WN / 32)), LAY>);
         grid = a.persist_grid;
       }
     }
@@ -57,7 +60,8 @@ hipError_t launch_dtl(const Args& a, int grid, hipStream_t s) {
     }
     if constexpr (LOOP == PERSIST) {
       if (a.dp_tiles == grid && a.persist_grid > 0) {
-        fn = reinterpret_cast<const void*>(&gemm_persist_kernel<DT, EP, BM, BN, WM, WN, BK, ST, CW, kPersistPre>);
+        fn = reinterpret_cast<const void*>(
+            &gemm_persist_kernel<DT, EP, BM, BN, WM, WN, BK, ST, CW, persist_pre((WM / 32) * (WN / 32))>);
         grid = a.persist_grid;
       }
     }
@@ -80,6 +84,7 @@ LaunchFn pick_cfg(int cfg) {
       case CFG_LM4: return &launch_dtl<DT, EP, 128, 128, 64, 64, 64, 2, LOCKSTEP>;
       case CFG_LMD: return &launch_dtl<DT, EP, 128, 128, 32, 64, 64, 3, LOCKSTEP>;
       case CFG_L3: return &launch_dtl<DT, EP, 192, 256, 96, 64, 64, 2, PERSIST>;
+      case CFG_LW: return &launch_dtl<DT, EP, 128, 256, 64, 64, 64, 2, PERSIST>;
       default: break;
     }
   }

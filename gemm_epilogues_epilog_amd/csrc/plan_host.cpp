@@ -122,7 +122,16 @@ ge_status_t check_plan_args(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt, ge_
 //                  7% ahead);
 //   KT >= 128:     the 256 x 256 tile with its k loop split across the idle CUs (3-9%
 //                  faster than the 2-stage 128 x 128 tile: long runs amortise the partial
-//                  sums); not for transposed operands, whose plans do not split;
+//                  sums; 1-7% faster than the 128 x 256 tile at 2048x4096x8192,
+//                  4096x2048x8192 and 2048x4096x16384); not for transposed operands,
+//                  whose plans do not split;
+//   TW in (CUs / 2, CUs], TW the 128 x 256 tiles, n padded by at most 5%: the
+//                  persistent 128 x 256 tile (LW; eight waves of 64 x 64, one
+//                  workgroup per CU) where two 128 x 128 workgroups per CU would run:
+//                  1.3-7.5% faster at 4096x2048x2048, 4096x2048x4096, 2048x4096x4096,
+//                  2048x4096x6144, 2048x3072x4096, 1536x4096x4096 and 3072x2560x4096 (it
+//                  copies 25% fewer bytes per flop); 3-6% slower at 4096x1376x4096,
+//                  whose n pads to 1536;
 //   otherwise:     the 128 x 128 tile (two workgroups per compute unit), with four
 //                  waves of 64 x 64 (LM4) when its grid fills the CUs without a
 //                  split and KT >= 64 or two workgroups per CU, else eight waves of
@@ -159,6 +168,10 @@ int choose_cfg(int64_t m, int64_t n, int64_t k, ge_dtype_t ab, int cus, int lay)
       }
     }
     if (kt >= 128 && lay == 0) return gek::CFG_L;
+    if (lay == 0) {
+      const int64_t tw = tiles(gek::CFG_LW), npad = cdiv(n, 256) * 256;
+      if (2 * tw > cus && tw <= cus && 20 * (npad - n) <= npad) return gek::CFG_LW;
+    }
     // 128 x 128 tiles: four waves of 64 x 64 (LM4) beat eight of 32 x 64 (LM) by 1-2.4%
     // once the grid fills the CUs and either k spans 64 or more k-tiles or the grid
     // fills two workgroups per CU; LM4 cannot split a sparse grid's k loop (measured at

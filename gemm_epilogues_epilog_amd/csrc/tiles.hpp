@@ -18,7 +18,7 @@ struct TileCfg {
   const char* loop;   // main loop of the direct-to-LDS kernels
 };
 
-enum CfgId { CFG_S = 0, CFG_M, CFG_L, CFG_LH, CFG_LM, CFG_LM4, CFG_LMD, CFG_L3, CFG_COUNT };
+enum CfgId { CFG_S = 0, CFG_M, CFG_L, CFG_LH, CFG_LM, CFG_LM4, CFG_LMD, CFG_L3, CFG_LW, CFG_COUNT };
 
 constexpr TileCfg kTiles[CFG_COUNT] = {
     {64, 64, 32, 32, 0, 2, "S", ""},
@@ -29,15 +29,18 @@ constexpr TileCfg kTiles[CFG_COUNT] = {
     {128, 128, 64, 64, 64, 2, "LM4", "lockstep"},                       // 4 waves of 64 x 64, two per CU
     {128, 128, 32, 64, 64, 3, "LMD", "lockstep"},                       // LM with a 3-stage ring, one per CU
     {192, 256, 96, 64, 64, 2, "L3", "persistent lockstep interleaved, copies on waves 0-3"},   // 8 waves of 96 x 64
+    {128, 256, 64, 64, 64, 2, "LW", "persistent lockstep interleaved, copies on waves 0-3"},   // 8 waves of 64 x 64
 };
 
 constexpr bool cfg_is_dtl(int c) { return c >= CFG_L; }
 // Configurations whose kernel can split the last round's K loop (8-wave lockstep
 // loops; the 4-wave tile has no registers left for the partial sums).
-constexpr bool cfg_can_split(int c) { return (c >= CFG_L && c <= CFG_LM) || c == CFG_LMD || c == CFG_L3; }
+constexpr bool cfg_can_split(int c) {
+  return (c >= CFG_L && c <= CFG_LM) || c == CFG_LMD || c == CFG_L3 || c == CFG_LW;
+}
 // Configurations with a persistent kernel, used when the tile grid is not split and
 // k spans a whole number of stage rings, at least two.
-constexpr bool cfg_can_persist(int c) { return c == CFG_L || c == CFG_L3; }
+constexpr bool cfg_can_persist(int c) { return c == CFG_L || c == CFG_L3 || c == CFG_LW; }
 // Configurations with kernels for operands stored transposed (16-bit types): the
 // 256 x 256 tile persistent (L) or with copies on waves 0-3 (LH), and the 128 x 128
 // tile (LM).

@@ -123,7 +123,7 @@ typedef enum {
  * Allocates the workspace on the current device: the per-tile bias-gradient
  * partial sums for DRELU_BGRAD, T1 and T2 for RELU_BIAS_UNFUSED, T1 for
  * DRELU_BGRAD_UNFUSED, nothing otherwise.
- * Environment (tuning experiments): GE_TILE=S|M|L|LH|LM|LM4|LMD|L3 forces a tile configuration;
+ * Environment (tuning experiments): GE_TILE=S|M|L|LH|LM|LM4|LMD|L3|LW forces a tile configuration;
  * GE_GROUP_M=g (1..1024) sets how many m-tiles share one group of the tile order;
  * GE_STREAMK=0 keeps a sparse last round of tiles whole instead of splitting its k loop;
  * GE_SK_RUN=r sets the k-tiles per split run (at least one run per compute unit);
@@ -199,7 +199,7 @@ ge_status_t gemm_epilog_execute(ge_handle_t h, const void* A, const void* B, con
  * Candidates: for fp32 the 64x64 and 128x128 tiles; for fp16/bf16 with transposed
  * operands the 256x256 and 128x128 lockstep tiles (the latter with a 2- and a 3-stage
  * ring); otherwise the 256x256 tile (persistent, one workgroup per tile, with copies on
- * all or half of the waves), the 192x256 tile (persistent) and the 128x128 tile with
+ * all or half of the waves), the 192x256 and 128x256 tiles (persistent) and the 128x128 tile with
  * eight waves (2- or 3-stage ring) or four, each with and without the split tail where it
  * applies. A candidate whose
  * workspace cannot be allocated is skipped. The call synchronises `stream`, must

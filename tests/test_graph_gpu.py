@@ -4,7 +4,7 @@ must give the bits of an eager execute of the same plan on the same values. Cove
 split tail (whose flags carry the frozen epoch of the capture), the persistent kernel,
 DRELU_BGRAD with its second pass, the three-kernel unfused chains (forward and
 backward), transposed operands (one workgroup per tile and persistent), the four-wave
-128 x 128 tile, the 3-stage ring of the eight-wave one and the persistent 192 x 256 tile."""
+128 x 128 tile, the 3-stage ring of the eight-wave one and the persistent 192 x 256 and 128 x 256 tiles."""
 import numpy as np
 import pytest
 import torch
@@ -27,6 +27,7 @@ CASES = [
     ("four-wave 128x128", 4096, 1376, 4096, "f16", "RELU_BIAS", False, False, "waves 2x2"),
     ("three-stage 128x128, split tail", 1024, 1024, 4096, "f16", "RELU_AUX_BIAS", False, False, "stages 3"),
     ("192x256 persistent", 4096, 2752, 256, "bf16", "DRELU_BGRAD", False, False, "tile 192x256"),
+    ("128x256 persistent", 2048, 4096, 256, "f16", "RELU_AUX_BIAS", False, False, "tile 128x256"),
 ]
 
 

@@ -23,7 +23,7 @@ DTS = ["f32", "f16", "bf16"]
 # finishes a part of the tile); "-run3" forces runs of 3 k-tiles, which do not divide the
 # 4 k-tiles of k = 200 or 256 (an owner run adds its partners' partials)
 TILES16 = ["S", "M", "L", "L-nosk", "L-run3", "LH", "LM", "LM-nosk", "LM-run3", "LM4", "LMD", "LMD-nosk", "LMD-run3",
-           "L3", "L3-nosk", "L3-run3"]
+           "L3", "L3-nosk", "L3-run3", "LW", "LW-nosk", "LW-run3"]
 TILES = {"f32": ["S", "M"], "f16": TILES16, "bf16": TILES16}
 # the last shape (k a multiple of 64 over 4 k-tiles) runs the persistent kernel in "L"
 INT_SHAPES = [(1, 8, 8), (33, 136, 72), (200, 264, 200), (300, 520, 136), (300, 520, 256)]

@@ -12,40 +12,41 @@ def info(m, n, k, lay="NN", ep="RELU_BIAS", dts=F16, cus=256):
     return ge.gemm_epilog_plan_info(m, n, k, dts, ep, int(lay[0] == "T"), int(lay[1] == "T"), compute_units=cus)
 
 
-@pytest.mark.parametrize("shape,lay,tile,waves,stages,split", [
-    ((4096, 11008, 4096), "NN", 256, 8, 2, False),   # the 7B FFN layer: 688 tiles, last round 69% full, not split
-    ((4096, 2752, 4096), "NN", 192, 8, 2, False),    # 176 tiles of 256 x 256 in one round; 242 of 192 x 256
-    ((3072, 4096, 4096), "NN", 192, 8, 2, False),    # 192 tiles of 256 x 256; 256 of 192 x 256: a full round
-    ((6144, 4096, 4096), "NN", 192, 8, 2, False),    # 384 (1.5 rounds) against 512 (2)
-    ((8448, 4096, 4096), "NN", 192, 8, 2, False),    # 528 (2 rounds and a split tail) against 704 (2.75)
-    ((4352, 4096, 4096), "NN", 256, 8, 2, True),     # 368 of 192 x 256 would split a 112-tile last round
-    ((4096, 2752, 4096), "TN", 256, 8, 2, False),    # no 192 x 256 tile for transposed operands
-    ((4096, 3200, 4096), "NN", 256, 8, 2, False),    # 208 tiles; 286 of 192 x 256 would take 2 rounds
-    ((4096, 4096, 4096), "NN", 256, 8, 2, False),
-    ((4096, 2048, 8192), "NN", 256, 8, 2, True),     # half a round: the 256 x 256 split already fills the CUs
-    ((8192, 1024, 8192), "NN", 256, 8, 2, True),     # 128 tiles, 128 k-tiles: split k loop
-    ((2048, 2048, 8192), "NN", 256, 8, 2, True),     # 256 tiles of 128 x 128 would fill the CUs unsplit
-    ((2048, 1024, 16384), "NN", 256, 8, 2, True),    # its 128 x 128 split would run 128 k-tiles per run
-    ((2048, 1024, 8192), "NN", 128, 8, 3, True),     # 128 tiles of 128 x 128, runs of 64 k-tiles
-    ((1024, 1024, 8192), "NN", 128, 8, 3, True),
-    ((512, 512, 8192), "NN", 128, 8, 3, True),
-    ((4096, 1376, 4096), "NN", 128, 4, 2, False),    # 352 tiles of 128 x 128: one round at two per CU
-    ((3072, 2560, 4096), "NN", 128, 4, 2, False),
-    ((1024, 512, 2048), "NN", 128, 8, 2, True),      # split runs of 8 k-tiles: the 2-stage ring
-    ((1024, 1024, 4096), "NN", 128, 8, 3, True),     # split runs of 16 k-tiles: the 3-stage ring
-    ((2048, 2048, 1024), "NN", 128, 8, 2, False),    # 16 k-tiles: the 2-stage ring
-    ((2048, 2048, 2048), "NN", 128, 8, 3, False),    # 32 k-tiles, one workgroup per CU: the 3-stage ring
-    ((2048, 2048, 4096), "NN", 128, 8, 3, False),
-    ((4096, 2048, 2048), "NN", 128, 4, 2, False),    # 32 k-tiles but two workgroups per CU
-    ((1536, 2048, 4096), "NN", 128, 8, 3, False),    # 192 tiles, fewer than the CUs
-    ((8192, 1024, 8192), "TN", 128, 8, 2, False),    # transposed operands never split
-    ((2048, 2048, 2048), "TN", 128, 8, 3, False),
-    ((4096, 2752, 4096), "TN", 256, 8, 2, False),
+@pytest.mark.parametrize("shape,lay,tile,waves,stages,split", [  # tile: (tile_m, tile_n)
+    ((4096, 11008, 4096), "NN", (256, 256), 8, 2, False),   # the 7B FFN layer: 688 tiles, last round 69% full, not split
+    ((4096, 2752, 4096), "NN", (192, 256), 8, 2, False),    # 176 tiles of 256 x 256 in one round; 242 of 192 x 256
+    ((3072, 4096, 4096), "NN", (192, 256), 8, 2, False),    # 192 tiles of 256 x 256; 256 of 192 x 256: a full round
+    ((6144, 4096, 4096), "NN", (192, 256), 8, 2, False),    # 384 (1.5 rounds) against 512 (2)
+    ((8448, 4096, 4096), "NN", (192, 256), 8, 2, False),    # 528 (2 rounds and a split tail) against 704 (2.75)
+    ((4352, 4096, 4096), "NN", (256, 256), 8, 2, True),     # 368 of 192 x 256 would split a 112-tile last round
+    ((4096, 2752, 4096), "TN", (256, 256), 8, 2, False),    # no 192 x 256 tile for transposed operands
+    ((4096, 3200, 4096), "NN", (256, 256), 8, 2, False),    # 208 tiles; 286 of 192 x 256 would take 2 rounds
+    ((4096, 4096, 4096), "NN", (256, 256), 8, 2, False),
+    ((4096, 2048, 8192), "NN", (256, 256), 8, 2, True),     # half a round: the 256 x 256 split already fills the CUs
+    ((8192, 1024, 8192), "NN", (256, 256), 8, 2, True),     # 128 tiles, 128 k-tiles: split k loop
+    ((2048, 2048, 8192), "NN", (256, 256), 8, 2, True),     # 256 tiles of 128 x 128 would fill the CUs unsplit
+    ((2048, 1024, 16384), "NN", (256, 256), 8, 2, True),    # its 128 x 128 split would run 128 k-tiles per run
+    ((2048, 1024, 8192), "NN", (128, 128), 8, 3, True),     # 128 tiles of 128 x 128, runs of 64 k-tiles
+    ((1024, 1024, 8192), "NN", (128, 128), 8, 3, True),
+    ((512, 512, 8192), "NN", (128, 128), 8, 3, True),
+    ((4096, 1376, 4096), "NN", (128, 128), 4, 2, False),    # 352 tiles of 128 x 128: one round at two per CU (n pads to 1536)
+    ((3072, 2560, 4096), "NN", (128, 256), 8, 2, False),    # 240 tiles of 128 x 256 in one round
+    ((2048, 4096, 4096), "NN", (128, 256), 8, 2, False),
+    ((2048, 4096, 8192), "NN", (256, 256), 8, 2, True),     # 128 k-tiles: the 256 x 256 split
+    ((1024, 512, 2048), "NN", (128, 128), 8, 2, True),      # split runs of 8 k-tiles: the 2-stage ring
+    ((1024, 1024, 4096), "NN", (128, 128), 8, 3, True),     # split runs of 16 k-tiles: the 3-stage ring
+    ((2048, 2048, 1024), "NN", (128, 128), 8, 2, False),    # 16 k-tiles: the 2-stage ring
+    ((2048, 2048, 2048), "NN", (128, 128), 8, 3, False),    # 32 k-tiles, one workgroup per CU: the 3-stage ring
+    ((2048, 2048, 4096), "NN", (128, 128), 8, 3, False),
+    ((4096, 2048, 2048), "NN", (128, 256), 8, 2, False),    # 256 tiles of 128 x 256 in one round
+    ((1536, 2048, 4096), "NN", (128, 128), 8, 3, False),    # 192 tiles, fewer than the CUs
+    ((8192, 1024, 8192), "TN", (128, 128), 8, 2, False),    # transposed operands never split
+    ((2048, 2048, 2048), "TN", (128, 128), 8, 3, False),
+    ((4096, 2752, 4096), "TN", (256, 256), 8, 2, False),
 ])
 def test_tile_rule(shape, lay, tile, waves, stages, split):
     r = info(*shape, lay=lay)
-    tile_n = 256 if tile == 192 else tile
-    assert (r["tile_m"], r["tile_n"], r["waves"], r["stages"]) == (tile, tile_n, waves, stages), r
+    assert ((r["tile_m"], r["tile_n"]), r["waves"], r["stages"]) == (tile, waves, stages), r
     assert (r["split_workgroups"] > 0) == split, r
 
 

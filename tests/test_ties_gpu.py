@@ -19,8 +19,8 @@ pytestmark = pytest.mark.gpu
 
 # (300, 520, 256): k over 4 k-tiles of 64, so the 256 x 256 tile runs the persistent
 # kernel; (257, 392, 72): ragged m and a ragged k tail
-CASES = [(dt, tile, shape) for dt, tiles in (("f32", [None, "S", "M"]), ("f16", [None, "L", "LH", "LM", "LM4", "LMD", "L3"]),
-                                             ("bf16", [None, "L", "LH", "LM", "LM4", "LMD", "L3"]))
+CASES = [(dt, tile, shape) for dt, tiles in (("f32", [None, "S", "M"]), ("f16", [None, "L", "LH", "LM", "LM4", "LMD", "L3", "LW"]),
+                                             ("bf16", [None, "L", "LH", "LM", "LM4", "LMD", "L3", "LW"]))
          for tile in tiles for shape in ((300, 520, 256), (257, 392, 72))]
 
 
