@@ -1208,14 +1208,14 @@ __device__ __forceinline__ uint32_t sk_wait_flags(uint32_t* flags, int np, uint3
 // Split runs that cover whole tiles (KT a multiple of the run length): the S runs of
 // tail tile t are t S .. t S + S - 1, run s computing k-tiles [s units, (s + 1) units).
 // Workgroup q (each XCD takes a contiguous range of q) runs:
-//   256 x 256 tiles, part-major: q = s T + t over the T tail tiles, so the runs that
+//   tiles of 256 rows, part-major: q = s T + t over the T tail tiles, so the runs that
 //   share an XCD read A and B over the same k range, and tiles of one m-tile (n-tile)
 //   share their A rows (B columns) in that XCD's L2 (2048 x 2048 x 8192: 3-5% faster
 //   than tile-major);
-//   128 x 128 tiles, tile-major: q = t S + s, so the S runs of a tile share an XCD. The
-//   XCDs start a launch's workgroups up to about 2.5 us apart, and a tile whose runs
-//   sit on several XCDs waits for the latest (1024 x 512 x 2048: 11.6 us tile-major,
-//   14.3 part-major).
+//   smaller tiles (128 or 192 rows), tile-major: q = t S + s, so the S runs of a tile
+//   share an XCD. The XCDs start a launch's workgroups up to about 2.5 us apart, and a
+//   tile whose runs sit on several XCDs waits for the latest (1024 x 512 x 2048:
+//   11.6 us tile-major, 14.3 part-major).
 // The tile is finished in S parts, one per run: wave w's sub-tile belongs to run
 // w % S. Every run stores the sub-tiles of its waves that other runs finish, publishes
 // them, waits until all S runs have published, and its own waves add the other runs'
