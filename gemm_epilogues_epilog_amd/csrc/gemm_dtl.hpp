@@ -1031,15 +1031,9 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_persist_ke
       }
     }
   };
+  // Each tile's first k-step gives its MFMAs a zero accumulator operand, so no
+  // instruction clears the accumulators between tiles.
   f32x16 acc[NB][MB];
-  auto zero_acc = [&]() {
-#pragma unroll
-    for (int a = 0; a < NB; ++a)
-#pragma unroll
-      for (int b = 0; b < MB; ++b)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
-  };
   F fr[2];
   auto read_all = [&](const char* base, int s, F& f) {
 #pragma unroll
@@ -1049,8 +1043,10 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_persist_ke
   // One k-tile in stage u. NEXT = false: copies of this tile's k-tile kt + STAGES;
   // NEXT = true (the last STAGES k-tiles): copies of the next tile's k-tile
   // kt + STAGES - KT when there is a next tile, and no reads past the last k-tile.
-  auto ktile = [&](auto next_tag, int kt, int u, bool more) {
+  // FIRST = true: the tile's k-tile 0, whose first k-step starts from zero.
+  auto ktile = [&](auto next_tag, auto first_tag, int kt, int u, bool more) {
     constexpr bool NEXT = decltype(next_tag)::value;
+    constexpr bool FIRST = decltype(first_tag)::value;
     const char* cur = smem + u * C::STAGE;
     const char* nxt = smem + ((u + 1) % STAGES) * C::STAGE;
 #pragma unroll
@@ -1085,7 +1081,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_persist_ke
 #pragma unroll
       for (int i = i0; i < NMMA; ++i) {
         const int a = i / MB, b = i % MB;
-        acc[a][b] = Tr<DT>::mma(fr[buf].bfrag(a), fr[buf].a[b], acc[a][b]);
+        acc[a][b] = Tr<DT>::mma(fr[buf].bfrag(a), fr[buf].a[b], FIRST && s == 0 ? f32x16{} : acc[a][b]);
 #pragma unroll
         for (int e = 0; e < per; ++e) {
           const int q = (i - i0) * per + e;
@@ -1099,7 +1095,6 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_persist_ke
 
   // prologue: the first tile's first STAGES k-tiles
   load_bias();
-  zero_acc();
   if (copier) {
 #pragma unroll
     for (int t = 0; t < STAGES; ++t) cp.issue_tile(t, t);
@@ -1113,15 +1108,17 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_persist_ke
     const bool more = vn < T;
     int tmn = 0, tnn = 0;
     if (more) raster(p, xcd_remap(vn, T), tmn, tnn);
-    int kt = 0;
-    do {
+    // k-tiles 0 .. STAGES - 1 (KT >= 2 STAGES), then the rest up to the last STAGES
+    ktile(std::false_type{}, std::true_type{}, 0, 0, more);
 #pragma unroll
-      for (int u = 0; u < STAGES; ++u) ktile(std::false_type{}, kt + u, u, more);
-      kt += STAGES;
-    } while (kt < KT - STAGES);
+    for (int u = 1; u < STAGES; ++u) ktile(std::false_type{}, std::false_type{}, u, u, more);
+    for (int kt = STAGES; kt < KT - STAGES; kt += STAGES) {
+#pragma unroll
+      for (int u = 0; u < STAGES; ++u) ktile(std::false_type{}, std::false_type{}, kt + u, u, more);
+    }
     if (more) cp.retarget(p, (int64_t)tmn * BM, tnn * BN, opaque(lane));
 #pragma unroll
-    for (int u = 0; u < STAGES; ++u) ktile(std::true_type{}, KT - STAGES + u, u, more);
+    for (int u = 0; u < STAGES; ++u) ktile(std::true_type{}, std::false_type{}, KT - STAGES + u, u, more);
 
     const int elane = opaque(lane);   // the epilogue's lane arithmetic stays out of the k loop
 #pragma unroll
@@ -1133,7 +1130,6 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) void gemm_persist_ke
     m0 = (int64_t)tmn * BM;
     n0 = tnn * BN;
     load_bias();
-    zero_acc();
     read_all(smem, 0, fr[0]);   // k-tile 0 of the new tile, published by the last barrier
   }
 }
