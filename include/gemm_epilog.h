@@ -151,9 +151,11 @@ typedef enum { GE_OP_N = 0, GE_OP_T = 1 } ge_op_t;
  * GE_OP_T, m follows the rules of n: a multiple of 8 and at most 2^20, else
  * GE_ERR_NOT_SUPPORTED. Every other argument, rule and error is that of
  * gemm_epilog_plan, which equals gemm_epilog_plan_ex(..., GE_OP_N, GE_OP_N, out).
- * Plans with a transposed operand run the same tiles as untransposed ones, the
- * persistent 256 x 256 kernel included, but never split their k loop (a small grid
- * with a deep k loop keeps the 128 x 128 tile); GE_TILE may pick L, LH or LM.
+ * Plans with a transposed operand run the 256 x 256 tile (the persistent kernel
+ * included) and the 128 x 128 tiles with eight waves (LM, and LMD for a small grid
+ * with 24 or more k-tiles), but never split their k loop; the 192 x 256, 128 x 256
+ * and four-wave 128 x 128 tiles take untransposed operands only. GE_TILE may pick
+ * L, LH, LM or LMD.
  */
 ge_status_t gemm_epilog_plan_ex(int64_t m, int64_t n, int64_t k, ge_dtypes_t dt, ge_epilog_t ep, ge_op_t op_a,
                                 ge_op_t op_b, ge_handle_t* out);
@@ -198,10 +200,10 @@ ge_status_t gemm_epilog_execute(ge_handle_t h, const void* A, const void* B, con
  *            execute in milliseconds, from HIP events on `stream`.
  * Candidates: for fp32 the 64x64 and 128x128 tiles; for fp16/bf16 with transposed
  * operands the 256x256 and 128x128 lockstep tiles (the latter with a 2- and a 3-stage
- * ring); otherwise the 256x256 tile (persistent, one workgroup per tile, with copies on
- * all or half of the waves), the 192x256 and 128x256 tiles (persistent) and the 128x128 tile with
- * eight waves (2- or 3-stage ring) or four, each with and without the split tail where it
- * applies. A candidate whose
+ * ring); otherwise the 256x256 tile (persistent, and one workgroup per tile with the
+ * fragment reads interleaved into the MFMAs or issued in blocks), the 192x256 and 128x256
+ * tiles (persistent) and the 128x128 tile with eight waves (2- or 3-stage ring) or four,
+ * each with and without the split tail where it applies. A candidate whose
  * workspace cannot be allocated is skipped. The call synchronises `stream`, must
  * not overlap another execute of this plan, and runs on the device current at plan
  * time. On an error the plan keeps its configuration (GE_ERR_HIP if a launch or an
