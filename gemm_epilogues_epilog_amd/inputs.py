@@ -161,17 +161,24 @@ def mlp_case(d: int, h: int, o: int, batch: int, dtype: str, seed: int = 0) -> T
             normal(o, batch, 1.0, dtype, seed, TAG_DY))
 
 
-def integer_case(m: int, n: int, k: int, dtype: str, seed: int = 0, vec: Optional[str] = None):
+def integer_case(m: int, n: int, k: int, dtype: str, seed: int = 0, vec: Optional[str] = None,
+                 second: bool = True):
     """Integer-valued A, B in [-2, 2] and half-integer bias in [-7.5, 7.5].
 
     With k <= 16 every product, sum and biased value is exact in fp32, fp16 and bf16,
     and no pre-activation is zero, so any correct implementation gives the same bits.
+    (For any k below 2^21 the fp32 sums and biased values stay exact, so the same holds up to
+    the one rounding of the output, which both sides take alike.) second = False
+    leaves out the second pair of operands (A2, B2 are then None); the first draws
+    are the same either way.
     """
     v = vec or dtype
     g = torch.Generator().manual_seed(_mix(seed, 99, m * 131 + n * 17 + k))
     A = torch.randint(-2, 3, (m, k), generator=g).to(TORCH_DT[dtype])
     B = torch.randint(-2, 3, (k, n), generator=g).to(TORCH_DT[dtype])
     bias = (torch.randint(-8, 8, (m,), generator=g).to(torch.float32) + 0.5).to(TORCH_DT[v])
+    if not second:
+        return A, B, bias, None, None
     A2 = torch.randint(-2, 3, (m, k), generator=g).to(TORCH_DT[dtype])
     B2 = torch.randint(-2, 3, (k, n), generator=g).to(TORCH_DT[dtype])
     return A, B, bias, A2, B2
