@@ -245,7 +245,12 @@ ge_status_t gemm_epilog_plan_info(int64_t m, int64_t n, int64_t k, ge_dtypes_t d
  * A plan whose last round of tiles is split hands parts of a tile's k loop to other
  * workgroups; the workgroup that finishes the tile waits, bounded (about a second),
  * for their partial sums. A wait that runs out gives that tile NaN in D instead of
- * hanging the device, and leaves the plan's flags clean for later executes. This call
+ * hanging the device, and leaves the plan's flags clean for later executes. The waits
+ * end once the workgroups they wait for are scheduled, which a split plan's grid alone
+ * always allows (its split workgroups fit the device at once); kernels of other streams
+ * that keep compute units busy for longer than the bound (a second split plan's waiting
+ * workgroups among them) can make a wait run out, so callers that run split plans
+ * concurrently should check this count. This call
  * synchronises `stream` (hipStream_t, NULL = null stream), reads the count from the
  * plan's workspace and clears it; a plan without a split tail reports 0 at once.
  *   h     : the plan (GE_ERR_NULL_POINTER if NULL).
