@@ -281,12 +281,15 @@ __device__ __forceinline__ void store_vec(void* p, int vec_dt, int64_t i, float 
 }
 
 // GELU, tanh form: 0.5 x (1 + tanh(u)) with u = sqrt(2/pi) (x + 0.044715 x^3).
-// 0.5 (1 + tanh(u)) = 1 / (1 + e^{-2u}), evaluated with the hardware exp2 and
-// reciprocal. e^{-2u} overflowing to +inf gives x * 0 = 0, the correct limit.
+// 0.5 (1 + tanh(u)) = 1 / (1 + 2^t) with t = -2 log2(e) u = x (c1 + c2 x^2), where
+// c1 = -2 log2(e) sqrt(2/pi) and c2 = 0.044715 c1: one multiply, one fma and one
+// multiply for t, then the hardware exp2 and reciprocal. 2^t overflowing to +inf
+// gives x * 0 = 0, the correct limit.
 __device__ __forceinline__ float gelu_tanh(float x) {
-  const float u = 0.7978845608028654f * (x + 0.044715f * x * x * x);
-  const float e = __builtin_amdgcn_exp2f(-2.8853900817779268f * u);   // -2 log2(e) u
-  return x * __builtin_amdgcn_rcpf(1.0f + e);
+  constexpr float c1 = -2.302208198144325f;    // -2 log2(e) sqrt(2/pi)
+  constexpr float c2 = -0.1029432395800235f;   // 0.044715 c1
+  const float t = x * __builtin_fmaf(c2, x * x, c1);
+  return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
 }
 
 template <int EP>

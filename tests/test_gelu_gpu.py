@@ -56,10 +56,13 @@ def test_device_gelu_error_bound_fp32(gpu, tile):
         jj = np.unravel_index(int(j), units.shape)
         print(f"[gelu]   x = {x[jj]!r}: y = {out['D'][jj]!r}, y_ref = {ref['D'][jj]!r}, {units[jj]:.3f} units",
               flush=True)
+    # plain relative error in units of 2^-24 where the output is at least 1e-3 in size (below that the
+    # tail's tiny outputs make relative units meaningless; the bound above covers them)
+    big = np.abs(ref["D"]) >= 1e-3
+    rel = float((np.abs(out["D"] - ref["D"])[big] / (np.abs(ref["D"])[big] * 2.0 ** -24)).max())
     print(f"[gelu] tile {tile}: max error {worst:.3f} units of the bound's scale at x = {x[i]!r}, "
-          f"y = {out['D'][i]!r}, y_ref = {ref['D'][i]!r}; plain ulps of y_ref: "
-          f"{float((np.abs(out['D'] - ref['D']) / np.maximum(np.abs(ref['D']) * 2.0 ** -24, 2.0 ** -149)).max()):.1f}",
-          flush=True)
+          f"y = {out['D'][i]!r}, y_ref = {ref['D'][i]!r}; relative error where |y_ref| >= 1e-3: "
+          f"{rel:.1f} units of 2^-24", flush=True)
     assert np.isfinite(out["D"]).all()
     assert worst <= C_BOUND, f"device GELU error {worst} > {C_BOUND} units at x = {x[i]}"
     # the fused path's fp32 tolerance, for scale
