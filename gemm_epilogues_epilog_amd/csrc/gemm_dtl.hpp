@@ -141,7 +141,6 @@ __device__ __forceinline__ void epilogue_lds(const Args& p, f32x16 (&acc)[NB][MB
 
   // ---- phase 1: finish every accumulator and stage it in scratch ----
   if constexpr (EP == DRELU_BGRAD) {
-    const uint32_t mybit = 1u << lrow;
 #pragma unroll
     for (int b = 0; b < MB; ++b) {
       const int row = 32 * b + lrow;
@@ -158,8 +157,7 @@ __device__ __forceinline__ void epilogue_lds(const Args& p, f32x16 (&acc)[NB][MB
         float dz[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const uint32_t wr = mask_word_of_reg(word, r, lane);
-          dz[r] = (wr & mybit) ? acc[a][b][r] : 0.0f;
+          dz[r] = mask_bit_of_reg(word, r) ? acc[a][b][r] : 0.0f;
           rowsum += dz[r];
         }
 #pragma unroll
@@ -258,7 +256,6 @@ __device__ __forceinline__ void epilogue_block(const Args& p, const f32x16 (&acc
   const int s = L::swz(lrow);
 
   if constexpr (EP == DRELU_BGRAD) {
-    const uint32_t mybit = 1u << lrow;
     float rowsum = 0.0f;
 #pragma unroll
     for (int a = 0; a < NB; ++a) {
@@ -266,8 +263,7 @@ __device__ __forceinline__ void epilogue_block(const Args& p, const f32x16 (&acc
       float dz[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const uint32_t wr = mask_word_of_reg(word, r, lane);
-        dz[r] = (wr & mybit) ? acc[a][b][r] : 0.0f;
+        dz[r] = mask_bit_of_reg(word, r) ? acc[a][b][r] : 0.0f;
         rowsum += dz[r];
       }
 #pragma unroll

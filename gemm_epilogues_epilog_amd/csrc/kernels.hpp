@@ -230,13 +230,16 @@ __device__ __forceinline__ float vec_value(uint32_t bits, int vec_dt) {
 // lane l holds row l % 32 and column 8 (r / 4) + 4 (l / 32) + r % 4, so the ballot of
 // register r holds column 8 (r / 4) + r % 4 in its low half and that column + 4 in
 // its high half; each half is written straight into its column's lane.
-// The mask word that register r of this lane needs: `word` holds in lane c (and
-// c + 32) the mask word of block column c, and register r of lane l is row l % 32,
-// column 8 (r / 4) + 4 (l / 32) + r % 4 of the block. Bit l % 32 of the result is the
-// register's mask bit.
-__device__ __forceinline__ uint32_t mask_word_of_reg(uint32_t word, int r, int lane) {
-  const int col = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-  return (uint32_t)__builtin_amdgcn_ds_bpermute(col << 2, (int)word);
+// This lane's mask bit for register r: `word` holds in lane c (and c + 32) the mask
+// word of block column c, and register r of lane l is row l % 32, column
+// 8 (r / 4) + 4 (l / 32) + r % 4 of the block. Lanes 0-31 take their bits from the
+// word of column c0 = 8 (r / 4) + r % 4 and lanes 32-63 from that of column c0 + 4, so
+// the two words, read with readlane, form one 64-bit lane mask whose bit l is lane l's.
+__device__ __forceinline__ bool mask_bit_of_reg(uint32_t word, int r) {
+  const int c0 = 8 * (r >> 2) + (r & 3);
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readlane((int)word, c0);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readlane((int)word, c0 + 4);
+  return __builtin_amdgcn_inverse_ballot_w64(hi << 32 | lo);
 }
 
 // Lane L of v = s (v_writelane_b32, immediate lane select). The compiler does not
@@ -314,7 +317,6 @@ __device__ __forceinline__ void epilogue(const Args& p, f32x16 (&acc)[NB][MB], i
   const __amdgpu_buffer_rsrc_t rd = rsrc(Dw);
 
   if constexpr (EP == DRELU_BGRAD) {
-    const uint32_t mybit = 1u << lrow;
 #pragma unroll
     for (int b = 0; b < MB; ++b) {
       const int64_t mrow = m0w + 32 * b + lrow;
@@ -330,8 +332,7 @@ __device__ __forceinline__ void epilogue(const Args& p, f32x16 (&acc)[NB][MB], i
         float dz[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const uint32_t wr = mask_word_of_reg(word, r, lane);
-          dz[r] = (wr & mybit) ? acc[a][b][r] : 0.0f;
+          dz[r] = mask_bit_of_reg(word, r) ? acc[a][b][r] : 0.0f;
           rowsum += dz[r];
         }
 #pragma unroll
